@@ -1,0 +1,429 @@
+/*
+ * moe_oracle.c -- CPU oracle for the W4A8 (MXFP4 weights, FP8 activations) sparse-MoE decode
+ * layer, its 42-layer stack steps, and the FP8 LM head with argmax.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg load this file's library.  The GPU library never links, calls or includes it, and it shares
+ * no code, header, table or helper with the GPU path.  It is plain, slow and single-threaded:
+ * every sum runs in natural index order in fp64, and every quantisation step is written out as
+ * its definition.  The block-scaled sums are exact in fp64 for the generated value ranges (each
+ * term is an integer multiple of 2^-16 below 2^26, a 2560-term sum stays below 2^38).
+ *
+ * Pages cited (titles as printed; sections named on each page):
+ *   [tanhow]  tanhow.com, "NVIDIA 在单台 DGX Spark 上叠加三项优化，Ling-3.0-flash 的 MoE 推理吞吐提升 42.5%"
+ *   [devotd]  devotd.net, "dgx-spark-moe-inference-optimizations"
+ *   [aivibe]  aivibenews.ru, "Три приёма ускорить MoE-инференс на DGX Spark без потери GSM8K"
+ *
+ * What the pages fix: each MoE layer sends a token to 8 of 512 routed experts plus one shared
+ * expert ([tanhow] "Ling 3.0 是什么" section, sparse-MoE bullet; [aivibe] intro); the expert
+ * layers are 768 wide ([tanhow] "三项优化是什么" item 1); the LM head is 157,184 x 2,560, so the
+ * hidden size is 2,560 ([tanhow] "三项优化是什么" item 2); expert weights are MXFP4, a blocked
+ * 4-bit float format ([devotd] section 2); the recipe is 4-bit weights with 8-bit activations
+ * ([tanhow] "为什么 DGX Spark 上的 MoE 解码是内存受限的"; [devotd] section 2); a verify pass
+ * checks 4 positions at once and touches up to 32 experts ([tanhow] item 3; [devotd] section 3);
+ * the LM head is quantised to FP8 at load time to halve its reads ([tanhow] item 2; [devotd]
+ * section 2).
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   - routing: top-k on raw router logits (ties -> lower expert index), then a softmax over the
+ *     k selected logits; router weights and input are bf16, products summed in fp64 here;
+ *   - shared expert: always on, weight 1, same format and width, stored at expert index E;
+ *   - SwiGLU: h = SiLU(gate) * up, gate rows first in the fused gate/up matrix;
+ *   - MXFP4 = OCP MX: E2M1 elements, one E8M0 scale per 32 consecutive k starting at k = 0, low
+ *     nibble = even k;
+ *   - FP8 = OCP E4M3 ("fn": bias 7, max 448, no inf); per-token activation scale
+ *     s = fl32(amax / 448) (s = 1 when amax = 0), codes = RNE-satfinite(fl32(x / s));
+ *   - the down projection's input h is requantised to E4M3 per (token, expert) the same way;
+ *   - combine: y = sum_r w_r d_(ids[r]) (rank order) + d_shared, rounded once to fp32;
+ *   - stack: unweighted RMSNorm (eps 1e-6) on each layer's MoE input, residual carried in bf16;
+ *   - LM head: weight-only E4M3 with a per-row fp32 scale, bf16 x, argmax = lowest index among
+ *     the maxima.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------------ */
+/* Codecs                                                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* OCP MX E2M1: bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa, no inf/NaN.
+ * Exponent field 0 is subnormal (0.m x 2^0). */
+double oracle_e2m1_decode(uint32_t code) {
+    code &= 0xFu;
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP MX E8M0: 2^(b - 127); b = 255 is NaN. */
+double oracle_e8m0_decode(uint32_t b) {
+    b &= 0xFFu;
+    if (b == 255) return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* OCP FP8 E4M3 ("fn"): bias 7; exponent field 0 is subnormal 0.mmm x 2^-6; S.1111.111 is NaN. */
+double oracle_e4m3_decode(uint32_t code) {
+    code &= 0xFFu;
+    int s = code >> 7, e = (code >> 3) & 0xF, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* fp32 -> E4M3, round to nearest with ties to even, saturating to +-448 (no inf in E4M3).
+ * NaN maps to the NaN code with the input's sign. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    if (a == 0.0) return sign;
+    /* Spacing of E4M3 values around a: 2^(floor(log2 a) - 3) for normals, 2^-9 below 2^-6. */
+    int e2;
+    frexp(a, &e2);               /* a = f * 2^e2 with f in [0.5, 1) */
+    int ex = e2 - 1;             /* floor(log2 a) */
+    if (ex < -6) ex = -6;
+    double quantum = ldexp(1.0, ex - 3);
+    double n = nearbyint(a / quantum); /* a / quantum is exact; default mode rounds half to even */
+    double r = n * quantum;            /* rounded magnitude, at most 448 since a < 448 */
+    if (r == 0.0) return sign;
+    int er;
+    frexp(r, &er);
+    int E = er - 1;
+    if (E < -6) return sign | (uint8_t)(r / ldexp(1.0, -9)); /* subnormal: mantissa = r / 2^-9 */
+    int mant = (int)((r / ldexp(1.0, E) - 1.0) * 8.0);
+    return sign | (uint8_t)(((E + 7) << 3) | mant);
+}
+
+/* bf16 -> fp32 is exact (the bf16 bits are the high half of the fp32 bits). */
+float oracle_bf16_decode(uint16_t b) {
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)b << 16;
+    return v.f;
+}
+
+/* fp32 -> bf16, round to nearest with ties to even.  Adding 0x7FFF plus the lowest kept bit
+ * to the fp32 bits and truncating rounds the dropped 16 bits exactly that way (a carry into
+ * the exponent is the correct round-up to the next binade).  NaN stays a quiet NaN. */
+uint16_t oracle_bf16_encode(float f) {
+    union { float f; uint32_t u; } v;
+    v.f = f;
+    if (isnan(f)) return (uint16_t)((v.u >> 16) | 0x0040u);
+    uint32_t u = v.u + 0x7FFFu + ((v.u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_e4m3_encode_array(const float* in, uint8_t* out, uint64_t n) {
+    for (uint64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(in[i]);
+}
+
+void oracle_bf16_encode_array(const float* in, uint16_t* out, uint64_t n) {
+    for (uint64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(in[i]);
+}
+
+/* Decode tables, filled from the decoders above on first use. */
+static double g_e2m1[16], g_e8m0[256], g_e4m3[256];
+static int g_tables_ready = 0;
+
+static void tables(void) {
+    if (g_tables_ready) return;
+    for (int i = 0; i < 16; ++i) g_e2m1[i] = oracle_e2m1_decode((uint32_t)i);
+    for (int i = 0; i < 256; ++i) g_e8m0[i] = oracle_e8m0_decode((uint32_t)i);
+    for (int i = 0; i < 256; ++i) g_e4m3[i] = oracle_e4m3_decode((uint32_t)i);
+    g_tables_ready = 1;
+}
+
+/* Dequantised MXFP4 element (row, k) of a [rows][K] matrix stored as E2M1 codes [rows][K/2]
+ * (low nibble = even k) and E8M0 scales [rows][K/32]. */
+static double mx_elem(const uint8_t* codes, const uint8_t* scl, int K, int row, int k) {
+    uint8_t byte = codes[(size_t)row * (size_t)(K / 2) + (size_t)(k / 2)];
+    uint32_t code = (k & 1) ? (uint32_t)(byte >> 4) : (uint32_t)(byte & 0xF);
+    return g_e2m1[code] * g_e8m0[scl[(size_t)row * (size_t)(K / 32) + (size_t)(k / 32)]];
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* One MoE layer                                                                              */
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t hidden;      /* H */
+    int32_t num_experts; /* E routed experts */
+    int32_t top_k;       /* k */
+    int32_t num_shared;  /* S, 0 or 1; the shared expert is stored at index E */
+    int32_t inter;       /* I, SwiGLU width */
+} oracle_shape;
+
+/* Weights.  Expert tables hold E + S pointers; entries of experts that are never selected may
+ * be NULL (only the selected experts and the shared expert are read). */
+typedef struct {
+    const uint16_t* router;        /* bf16 [E][H] */
+    const uint8_t* const* w13;     /* [E+S] -> E2M1 [2I][H/2] (rows 0..I-1 gate, I..2I-1 up) */
+    const uint8_t* const* w13_s;   /* [E+S] -> E8M0 [2I][H/32] */
+    const uint8_t* const* w2;      /* [E+S] -> E2M1 [H][I/2] */
+    const uint8_t* const* w2_s;    /* [E+S] -> E8M0 [H][I/32] */
+} oracle_weights;
+
+/* Optional intermediate values, all per token t (slot j < k is routed rank j, slot k the shared
+ * expert).  Any pointer may be NULL. */
+typedef struct {
+    double* logits;  /* [T][E] */
+    double* bounds;  /* [T][E] bound on any-order fp32 summation error of each logit */
+    int32_t* ids;    /* [T][k] */
+    double* w;       /* [T][k] */
+    float* sx;       /* [T] */
+    uint8_t* qx;     /* [T][H] */
+    double* g;       /* [T][k+S][I] gate pre-activation */
+    double* u;       /* [T][k+S][I] up pre-activation */
+    float* h;        /* [T][k+S][I] */
+    float* sh;       /* [T][k+S] */
+    uint8_t* qh;     /* [T][k+S][I] */
+    double* d;       /* [T][k+S][H] expert outputs */
+} oracle_trace;
+
+static int shape_ok(const oracle_shape* s) {
+    return s && s->hidden > 0 && s->hidden % 32 == 0 && s->inter > 0 && s->inter % 32 == 0 &&
+           s->num_experts > 0 && s->top_k >= 1 && s->top_k <= s->num_experts &&
+           (s->num_shared == 0 || s->num_shared == 1);
+}
+
+/* Router logits and error bounds of one token.  Products of two bf16 values are exact; the sum
+ * is in fp64.  bound = gamma_(H-1) * sum |w x| with gamma_n = n u / (1 - n u), u = 2^-24: the
+ * largest error of an fp32 accumulation of these H products in any order. */
+static void router_logits(const oracle_shape* s, const uint16_t* router, const float* xf, double* logits,
+                          double* bounds) {
+    const int H = s->hidden;
+    const double nu = (double)(H - 1) * 0x1p-24;
+    const double gamma = nu / (1.0 - nu);
+    for (int e = 0; e < s->num_experts; ++e) {
+        double acc = 0.0, mag = 0.0;
+        for (int c = 0; c < H; ++c) {
+            double p = (double)oracle_bf16_decode(router[(size_t)e * H + c]) * (double)xf[c];
+            acc += p;
+            mag += fabs(p);
+        }
+        logits[e] = acc;
+        if (bounds) bounds[e] = gamma * mag;
+    }
+}
+
+/* Top-k: repeatedly take the not-yet-taken expert with the largest logit, the lower index
+ * winning ties; ids come out in that order. */
+static void select_top_k(int E, int k, const double* logits, int32_t* ids) {
+    char* taken = (char*)calloc((size_t)E, 1);
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || logits[e] > logits[best]) best = e;
+        }
+        ids[r] = best;
+        taken[best] = 1;
+    }
+    free(taken);
+}
+
+/* Softmax over the k selected logits. */
+static void route_weights(int k, const double* logits, const int32_t* ids, double* w) {
+    double m = logits[ids[0]], z = 0.0;
+    for (int r = 0; r < k; ++r) {
+        w[r] = exp(logits[ids[r]] - m);
+        z += w[r];
+    }
+    for (int r = 0; r < k; ++r) w[r] /= z;
+}
+
+/* Per-vector E4M3 quantisation: s = fl32(amax / 448) (1 if amax = 0), q = E4M3(fl32(v / s)). */
+static float quantize_e4m3(const float* v, int n, uint8_t* q) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int i = 0; i < n; ++i) q[i] = oracle_e4m3_encode(v[i] / s);
+    return s;
+}
+
+/* Routing only: logits, bounds, ids and weights of T tokens (bf16 inputs [T][H]). */
+int oracle_route(const oracle_shape* s, const uint16_t* router, const uint16_t* x, int32_t T, double* logits,
+                 double* bounds, int32_t* ids, double* w) {
+    if (!shape_ok(s) || !router || !x || T < 1) return -1;
+    const int H = s->hidden, E = s->num_experts, k = s->top_k;
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    double* l = (double*)malloc(sizeof(double) * (size_t)E);
+    double* b = (double*)malloc(sizeof(double) * (size_t)E);
+    int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* wr = (double*)malloc(sizeof(double) * (size_t)k);
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < H; ++c) xf[c] = oracle_bf16_decode(x[(size_t)t * H + c]);
+        router_logits(s, router, xf, l, b);
+        select_top_k(E, k, l, id);
+        route_weights(k, l, id, wr);
+        if (logits) memcpy(logits + (size_t)t * E, l, sizeof(double) * (size_t)E);
+        if (bounds) memcpy(bounds + (size_t)t * E, b, sizeof(double) * (size_t)E);
+        if (ids) memcpy(ids + (size_t)t * k, id, sizeof(int32_t) * (size_t)k);
+        if (w) memcpy(w + (size_t)t * k, wr, sizeof(double) * (size_t)k);
+    }
+    free(xf); free(l); free(b); free(id); free(wr);
+    return 0;
+}
+
+/* One MoE layer on T tokens x (bf16 [T][H]); y is fp32 [T][H].  Tokens are independent. */
+int oracle_moe_layer(const oracle_shape* s, const oracle_weights* W, const uint16_t* x, int32_t T, float* y,
+                     oracle_trace* tr) {
+    if (!shape_ok(s) || !W || !W->router || !W->w13 || !W->w13_s || !W->w2 || !W->w2_s || !x || T < 1 || !y)
+        return -1;
+    tables();
+    const int H = s->hidden, E = s->num_experts, k = s->top_k, S = s->num_shared, I = s->inter;
+    const int slots = k + S;
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    double* l = (double*)malloc(sizeof(double) * (size_t)E);
+    double* bnd = (double*)malloc(sizeof(double) * (size_t)E);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* w = (double*)malloc(sizeof(double) * (size_t)k);
+    uint8_t* qx = (uint8_t*)malloc((size_t)H);
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double* G = (double*)malloc(sizeof(double) * (size_t)I);
+    double* U = (double*)malloc(sizeof(double) * (size_t)I);
+    float* h = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* qh = (uint8_t*)malloc((size_t)I);
+    double* hh = (double*)malloc(sizeof(double) * (size_t)I);
+    double* d = (double*)malloc(sizeof(double) * (size_t)slots * (size_t)H);
+    int rc = 0;
+
+    for (int t = 0; t < T; ++t) {
+        /* 1. bf16 -> fp32 (exact) */
+        for (int c = 0; c < H; ++c) xf[c] = oracle_bf16_decode(x[(size_t)t * H + c]);
+        /* 2-4. router logits, top-k, softmax over the selected k */
+        router_logits(s, W->router, xf, l, bnd);
+        select_top_k(E, k, l, ids);
+        route_weights(k, l, ids, w);
+        /* 5. per-token FP8 quantisation of the activation */
+        float sx = quantize_e4m3(xf, H, qx);
+        for (int c = 0; c < H; ++c) xh[c] = g_e4m3[qx[c]];
+        /* 6-8. experts: routed ranks 0..k-1, then the shared expert */
+        for (int j = 0; j < slots; ++j) {
+            int e = (j < k) ? ids[j] : E;
+            const uint8_t* w13 = W->w13[e];
+            const uint8_t* w13s = W->w13_s[e];
+            const uint8_t* w2 = W->w2[e];
+            const uint8_t* w2s = W->w2_s[e];
+            if (!w13 || !w13s || !w2 || !w2s) { rc = -2; goto done; }
+            for (int i = 0; i < I; ++i) {
+                double ag = 0.0, au = 0.0;
+                for (int c = 0; c < H; ++c) {
+                    ag += mx_elem(w13, w13s, H, i, c) * xh[c];
+                    au += mx_elem(w13, w13s, H, I + i, c) * xh[c];
+                }
+                G[i] = (double)sx * ag;
+                U[i] = (double)sx * au;
+                h[i] = (float)(G[i] / (1.0 + exp(-G[i])) * U[i]);
+            }
+            float sh = quantize_e4m3(h, I, qh);
+            for (int i = 0; i < I; ++i) hh[i] = g_e4m3[qh[i]];
+            for (int r = 0; r < H; ++r) {
+                double acc = 0.0;
+                for (int i = 0; i < I; ++i) acc += mx_elem(w2, w2s, I, r, i) * hh[i];
+                d[(size_t)j * H + r] = (double)sh * acc;
+            }
+            if (tr) {
+                size_t o = ((size_t)t * slots + j) * (size_t)I;
+                if (tr->g) memcpy(tr->g + o, G, sizeof(double) * (size_t)I);
+                if (tr->u) memcpy(tr->u + o, U, sizeof(double) * (size_t)I);
+                if (tr->h) memcpy(tr->h + o, h, sizeof(float) * (size_t)I);
+                if (tr->qh) memcpy(tr->qh + o, qh, (size_t)I);
+                if (tr->sh) tr->sh[(size_t)t * slots + j] = sh;
+                if (tr->d) memcpy(tr->d + ((size_t)t * slots + j) * (size_t)H, d + (size_t)j * H, sizeof(double) * (size_t)H);
+            }
+        }
+        /* 9. combine: routed terms in rank order, then the shared expert with weight 1 */
+        for (int r = 0; r < H; ++r) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) acc += w[j] * d[(size_t)j * H + r];
+            if (S) acc += d[(size_t)k * H + r];
+            y[(size_t)t * H + r] = (float)acc;
+        }
+        if (tr) {
+            if (tr->logits) memcpy(tr->logits + (size_t)t * E, l, sizeof(double) * (size_t)E);
+            if (tr->bounds) memcpy(tr->bounds + (size_t)t * E, bnd, sizeof(double) * (size_t)E);
+            if (tr->ids) memcpy(tr->ids + (size_t)t * k, ids, sizeof(int32_t) * (size_t)k);
+            if (tr->w) memcpy(tr->w + (size_t)t * k, w, sizeof(double) * (size_t)k);
+            if (tr->sx) tr->sx[t] = sx;
+            if (tr->qx) memcpy(tr->qx + (size_t)t * H, qx, (size_t)H);
+        }
+    }
+done:
+    free(xf); free(l); free(bnd); free(ids); free(w); free(qx); free(xh);
+    free(G); free(U); free(h); free(qh); free(hh); free(d);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Stack steps (reading: pre-MoE unweighted RMSNorm, bf16 residual)                            */
+/* ------------------------------------------------------------------------------------------ */
+
+/* x_in = bf16(fl32(x * r)), r = 1 / sqrt(mean(x^2) + 1e-6), with mean and r in fp64. */
+void oracle_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, uint16_t* out) {
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int c = 0; c < H; ++c) {
+            double v = (double)oracle_bf16_decode(x[(size_t)t * H + c]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + 1e-6);
+        for (int c = 0; c < H; ++c) {
+            double v = (double)oracle_bf16_decode(x[(size_t)t * H + c]);
+            out[(size_t)t * H + c] = oracle_bf16_encode((float)(v * r));
+        }
+    }
+}
+
+/* x_next = bf16(fl32(x + y)) with x bf16 and y fp32. */
+void oracle_residual_bf16(const uint16_t* x, const float* y, int32_t T, int32_t H, uint16_t* out) {
+    for (size_t i = 0; i < (size_t)T * (size_t)H; ++i) out[i] = oracle_bf16_encode(oracle_bf16_decode(x[i]) + y[i]);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* FP8 LM head                                                                                 */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Load-time per-row quantisation: s_r = fl32(amax_r / 448) (1 if the row is zero),
+ * Wq[r][c] = E4M3(fl32(W[r][c] / s_r)). */
+void oracle_head_quantize(const float* W, int32_t V, int32_t H, uint8_t* Wq, float* scale) {
+    for (int r = 0; r < V; ++r) scale[r] = quantize_e4m3(W + (size_t)r * H, H, Wq + (size_t)r * H);
+}
+
+/* logits[t][r] = s_r * sum_c E4M3(Wq[r][c]) * x[t][c] in fp64; argmax = lowest index among the
+ * maxima.  bounds (optional) = s_r * gamma_(H-1) * sum |Wq x| + 2^-24 |logit|: the largest error
+ * of an fp32 dot product in any order followed by one fp32 multiply by s_r. */
+void oracle_head_logits(const uint8_t* Wq, const float* scale, int32_t V, int32_t H, const uint16_t* x, int32_t T,
+                        double* logits, double* bounds, int32_t* argmax) {
+    tables();
+    const double nu = (double)(H - 1) * 0x1p-24;
+    const double gamma = nu / (1.0 - nu);
+    double* xf = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < H; ++c) xf[c] = (double)oracle_bf16_decode(x[(size_t)t * H + c]);
+        int best = 0;
+        double bestv = -INFINITY;
+        for (int r = 0; r < V; ++r) {
+            const uint8_t* row = Wq + (size_t)r * H;
+            double acc = 0.0, mag = 0.0;
+            for (int c = 0; c < H; ++c) {
+                double p = g_e4m3[row[c]] * xf[c];
+                acc += p;
+                mag += fabs(p);
+            }
+            double lg = (double)scale[r] * acc;
+            if (logits) logits[(size_t)t * V + r] = lg;
+            if (bounds) bounds[(size_t)t * V + r] = (double)scale[r] * gamma * mag + 0x1p-24 * fabs(lg);
+            if (lg > bestv) { bestv = lg; best = r; }
+        }
+        if (argmax) argmax[t] = best;
+    }
+    free(xf);
+}
