@@ -1,0 +1,168 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) W4A8 sparse-MoE decode library.
+ *
+ * One call of moe_decode_run computes, for T <= 4 tokens, the decode step of a stack of sparse
+ * Mixture-of-Experts layers with MXFP4 expert weights and FP8 (E4M3) activations:
+ *   router GEMV (bf16) -> top-k over the routed experts -> softmax over the k selected logits ->
+ *   per-token FP8 quantisation of the input -> dequant-on-the-fly gate/up GEMVs, h = SiLU(gate)*up ->
+ *   per-(token, expert) FP8 requantisation of h -> dequant-on-the-fly down GEMV ->
+ *   weighted combine y = sum_r w_r d_(id_r) + d_shared.
+ * With several layers each layer's input is an unweighted RMSNorm of the bf16 residual and the
+ * residual is updated as x <- bf16(x + y).  fp8_head_* is the companion FP8 LM-head GEMV with a
+ * per-token argmax.
+ *
+ * Passages that define the operation (titles as printed on the pages):
+ *   - 8 of 512 routed experts plus one shared expert per MoE layer: tanhow.com, "NVIDIA 在单台 DGX
+ *     Spark 上叠加三项优化，Ling-3.0-flash 的 MoE 推理吞吐提升 42.5%", section "Ling 3.0 是什么",
+ *     sparse-MoE bullet; aivibenews.ru, "Три приёма ускорить MoE-инференс на DGX Spark без потери
+ *     GSM8K", introduction.
+ *   - expert layers of width 768, MXFP4 expert kernel: tanhow.com, section "三项优化是什么", item 1;
+ *     devotd.net, "dgx-spark-moe-inference-optimizations", section 2 (MXFP4 is a blocked 4-bit float).
+ *   - 4-bit weights with 8-bit activations (W4A8): tanhow.com, section "为什么 DGX Spark 上的 MoE
+ *     解码是内存受限的"; devotd.net, section 2, last paragraph.
+ *   - 4-position verify touching up to 32 experts: tanhow.com, section "三项优化是什么", item 3;
+ *     devotd.net, section 3.
+ *   - FP8 LM head of 157,184 x 2,560 (hence hidden size 2,560), read in full per token:
+ *     tanhow.com, section "三项优化是什么", item 2; devotd.net, section 2.
+ *   - the silent FP8-read-as-BF16 fallback and the advice to check at start-up that every
+ *     optimisation is active: tanhow.com, section "三项优化是什么", paragraph on the integration
+ *     trap; devotd.net, section 3.  Hence every tensor carries a dtype tag that is checked, an
+ *     unsupported request is an error (never a slower fallback), and moe_decode_query reports the
+ *     kernel variant in use.
+ *
+ * Formats (OCP MX v1.0 and OCP FP8):
+ *   E2M1X2  two E2M1 codes per byte, the even element in the low nibble.
+ *   E8M0    one byte per 32 consecutive elements along the reduction (K) dimension, 2^(b-127).
+ *   E4M3    OCP "fn" FP8, bias 7, max 448, no infinities.
+ *   BF16    bfloat16 bits.
+ *
+ * Conventions for every function:
+ *   - Pointers inside moe_tensor / moe_outputs and the x argument are DEVICE pointers on the
+ *     device that was current at create time.  Config and descriptor structs are host memory.
+ *   - All arguments are validated before any HIP call; a failure returns an error status and
+ *     leaves the handle unchanged.  moe_last_error() gives a message for the last failure of the
+ *     calling thread.
+ *   - run / set_layer only enqueue work on the given stream (hipStream_t, 0 = default stream) and
+ *     return; asynchronous device faults surface at the caller's next synchronisation.
+ *   - A handle is used from one stream at a time.  Calls that overlap on one handle race on its
+ *     workspace.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* NULL/unaligned pointer, bad size, bad struct_size */
+    MOE_ERR_UNSUPPORTED = -2, /* valid shape this build has no kernel for (never a fallback) */
+    MOE_ERR_DTYPE = -3,       /* a tensor's dtype tag is not the one the slot requires */
+    MOE_ERR_OOM = -4,         /* device allocation failed */
+    MOE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_NO_DEVICE = -6,   /* no HIP device visible */
+    MOE_ERR_STATE = -7        /* e.g. run before every layer was set */
+} moe_status;
+
+typedef enum {
+    MOE_DT_BF16 = 1,
+    MOE_DT_FP32 = 2,
+    MOE_DT_E4M3 = 3,
+    MOE_DT_E2M1X2 = 4,
+    MOE_DT_E8M0 = 5
+} moe_dtype;
+
+/* flags of moe_decode_config */
+#define MOE_F_RMSNORM_INPUT 0x1u /* each layer's MoE input is RMSNorm(x), eps 1e-6, unweighted */
+
+typedef struct moe_decode_handle moe_decode_handle;
+typedef struct fp8_head_handle fp8_head_handle;
+
+typedef struct {
+    uint32_t struct_size; /* sizeof(moe_decode_config) */
+    int32_t hidden;       /* H: multiple of 256, 256..2560 */
+    int32_t num_experts;  /* E routed experts: 1..512 */
+    int32_t top_k;        /* k: 1..8, <= E */
+    int32_t num_shared;   /* S: 0 or 1; the shared expert is stored at expert index E */
+    int32_t inter;        /* I: SwiGLU width: 64, 128, 256, 512 or 768 */
+    int32_t max_tokens;   /* 1..4 tokens per run */
+    int32_t num_layers;   /* L >= 1 */
+    uint32_t flags;       /* MOE_F_* */
+} moe_decode_config;
+
+typedef struct {
+    const void* ptr; /* device pointer */
+    int32_t dtype;   /* moe_dtype tag; checked against the slot it is passed in */
+} moe_tensor;
+
+/* One layer's weights in canonical (row-major) layout.  set_layer copies and repacks them into
+ * handle-owned device memory; the caller may free them once the stream has passed set_layer. */
+typedef struct {
+    moe_tensor router; /* BF16   [E][H] */
+    moe_tensor w13;    /* E2M1X2 [E+S][2I][H/2]   rows 0..I-1 gate, rows I..2I-1 up */
+    moe_tensor w13_s;  /* E8M0   [E+S][2I][H/32] */
+    moe_tensor w2;     /* E2M1X2 [E+S][H][I/2]    down projection */
+    moe_tensor w2_s;   /* E8M0   [E+S][H][I/32] */
+} moe_layer_desc;
+
+/* Outputs of one run; every pointer is a device pointer and may be NULL (not written). */
+typedef struct {
+    uint32_t struct_size;  /* sizeof(moe_outputs) */
+    void* x_out;           /* BF16 [T][H]: residual after the last layer, x_L */
+    float* y;              /* FP32 [T][H]: MoE output y of the last layer */
+    int32_t* topk_ids;     /* [L][T][k]: expert ids, logit descending, lower index first on ties */
+    float* topk_w;         /* [L][T][k]: softmax weights of the selected experts */
+    void* x_trace;         /* BF16 [L][T][H]: each layer's input residual x_l */
+    float* x_scale;        /* FP32 [L][T]: per-token activation scale s_x of each layer */
+    uint8_t* x_codes;      /* E4M3 [L][T][H]: the quantised activation of each layer */
+} moe_outputs;
+
+typedef struct {
+    uint32_t struct_size;         /* sizeof(moe_decode_info) */
+    char variant[64];             /* name of the kernel set in use */
+    uint64_t weight_bytes;        /* handle-owned repacked weight memory, all layers */
+    uint64_t workspace_bytes;     /* handle-owned scratch memory */
+    uint64_t bytes_per_layer_t1;  /* algorithmic HBM bytes of one layer, 1 token */
+    int32_t layers_set;           /* number of layers set so far */
+} moe_decode_info;
+
+/* Creates a handle bound to the current device: allocates repacked weight storage for all layers
+ * and the workspace.  Returns MOE_ERR_NO_DEVICE when no HIP device is visible.  *out is written
+ * only on success. */
+moe_status moe_decode_create(const moe_decode_config* cfg, void* stream, moe_decode_handle** out);
+
+/* Copies and repacks the weights of layer `layer` (0-based) into the handle, on `stream`. */
+moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_layer_desc* desc, void* stream);
+
+/* Runs all L layers on x (BF16 [T][H], device, 16-byte aligned), 1 <= T <= max_tokens.
+ * Every layer must have been set.  Only enqueues work on `stream`. */
+moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t num_tokens, const moe_outputs* out,
+                          void* stream);
+
+moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_info* info);
+
+/* Frees the handle's device memory (synchronises the device first).  NULL is a no-op. */
+moe_status moe_decode_destroy(moe_decode_handle* h);
+
+/* FP8 LM head (tanhow.com, section "三项优化是什么", item 2): logits[t][v] = s_v * sum_c W[v][c] x[t][c]
+ * with W E4M3 [V][H] (row-major), s FP32 [V] per-row scales, x BF16 [T][H]; argmax[t] is the
+ * lowest index among the maxima.  create copies W and s into handle-owned memory. */
+moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, void* stream,
+                           fp8_head_handle** out);
+/* logits (FP32 [T][V], device) may be NULL; argmax (INT32 [T], device) is required. */
+moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, float* logits, int32_t* argmax,
+                        void* stream);
+moe_status fp8_head_destroy(fp8_head_handle* h);
+
+const char* moe_status_string(moe_status s);
+/* Message of the last failed call made by this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

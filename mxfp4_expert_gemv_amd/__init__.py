@@ -1,0 +1,171 @@
+"""Python binding of the MI355X W4A8 sparse-MoE decode library (``libmoe_decode.so``).
+
+Argument marshalling only: every step of the decode path runs in the library's HIP kernels.  The
+functions keep the C names (``include/moe_decode.h`` documents each one).  Tensors are torch
+tensors on the GPU; only their ``data_ptr()`` crosses the boundary, together with the hipStream_t
+of a torch stream (the current stream by default).  A missing library is an error, never a
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "libmoe_decode.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_DTYPE",
+          -4: "MOE_ERR_OOM", -5: "MOE_ERR_HIP", -6: "MOE_ERR_NO_DEVICE", -7: "MOE_ERR_STATE"}
+DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
+F_RMSNORM_INPUT = 0x1
+
+# every symbol the header declares
+EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
+           "moe_decode_destroy", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
+           "moe_status_string", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("num_shared", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("num_layers", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("router", Tensor), ("w13", Tensor), ("w13_s", Tensor), ("w2", Tensor), ("w2_s", Tensor)]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("x_out", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("x_trace", ctypes.c_void_p),
+                ("x_scale", ctypes.c_void_p), ("x_codes", ctypes.c_void_p)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("variant", ctypes.c_char * 64),
+                ("weight_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+                ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built (run __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        sig = {
+            "moe_decode_create": [ctypes.POINTER(Config), vp, ctypes.POINTER(vp)],
+            "moe_decode_set_layer": [vp, i32, ctypes.POINTER(LayerDesc), vp],
+            "moe_decode_run": [vp, vp, i32, ctypes.POINTER(Outputs), vp],
+            "moe_decode_query": [vp, ctypes.POINTER(Info)],
+            "moe_decode_destroy": [vp],
+            "fp8_head_create": [i32, i32, Tensor, Tensor, vp, ctypes.POINTER(vp)],
+            "fp8_head_run": [vp, vp, i32, vp, vp, vp],
+            "fp8_head_destroy": [vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _tensor(t, default_tag: int) -> Tensor:
+    """A torch tensor (tag from its slot) or a (tensor, tag) pair (explicit tag)."""
+    if isinstance(t, tuple):
+        t, tag = t
+    else:
+        tag = default_tag
+    return Tensor(None if t is None else t.data_ptr(), tag)
+
+
+def moe_decode_create(hidden: int, num_experts: int, top_k: int, num_shared: int, inter: int, max_tokens: int,
+                      num_layers: int = 1, flags: int = 0, stream=None) -> ctypes.c_void_p:
+    cfg = Config(ctypes.sizeof(Config), hidden, num_experts, top_k, num_shared, inter, max_tokens, num_layers, flags)
+    h = ctypes.c_void_p()
+    _check(lib().moe_decode_create(ctypes.byref(cfg), _stream(stream) if stream != 0 else None, ctypes.byref(h)))
+    return h
+
+
+def moe_decode_set_layer(handle, layer: int, router, w13, w13_s, w2, w2_s, stream=None) -> None:
+    d = LayerDesc(_tensor(router, DT_BF16), _tensor(w13, DT_E2M1X2), _tensor(w13_s, DT_E8M0),
+                  _tensor(w2, DT_E2M1X2), _tensor(w2_s, DT_E8M0))
+    _check(lib().moe_decode_set_layer(handle, layer, ctypes.byref(d), _stream(stream)))
+
+
+def moe_decode_run(handle, x, num_tokens: int | None = None, x_out=None, y=None, topk_ids=None, topk_w=None,
+                   x_trace=None, x_scale=None, x_codes=None, stream=None) -> None:
+    T = x.shape[0] if num_tokens is None else num_tokens
+    o = Outputs(ctypes.sizeof(Outputs), _ptr(x_out), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(x_trace),
+                _ptr(x_scale), _ptr(x_codes))
+    _check(lib().moe_decode_run(handle, _ptr(x), T, ctypes.byref(o), _stream(stream)))
+
+
+def moe_decode_query(handle) -> dict:
+    info = Info()
+    info.struct_size = ctypes.sizeof(Info)
+    _check(lib().moe_decode_query(handle, ctypes.byref(info)))
+    return {"variant": info.variant.decode(), "weight_bytes": info.weight_bytes,
+            "workspace_bytes": info.workspace_bytes, "bytes_per_layer_t1": info.bytes_per_layer_t1,
+            "layers_set": info.layers_set}
+
+
+def moe_decode_destroy(handle) -> None:
+    _check(lib().moe_decode_destroy(handle))
+
+
+def fp8_head_create(w, row_scale, stream=None) -> ctypes.c_void_p:
+    wt = w[0] if isinstance(w, tuple) else w
+    vocab, hidden = wt.shape
+    h = ctypes.c_void_p()
+    _check(lib().fp8_head_create(vocab, hidden, _tensor(w, DT_E4M3), _tensor(row_scale, DT_FP32), _stream(stream),
+                                 ctypes.byref(h)))
+    return h
+
+
+def fp8_head_run(handle, x, argmax, logits=None, num_tokens: int | None = None, stream=None) -> None:
+    T = x.shape[0] if num_tokens is None else num_tokens
+    _check(lib().fp8_head_run(handle, _ptr(x), T, _ptr(logits), _ptr(argmax), _stream(stream)))
+
+
+def fp8_head_destroy(handle) -> None:
+    _check(lib().fp8_head_destroy(handle))

@@ -1,0 +1,93 @@
+// head_api.cpp -- C ABI of the FP8 LM head (declarations and contracts in include/moe_decode.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "moe_launch.h"
+
+namespace head {
+hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream);
+hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
+                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, hipStream_t stream);
+}
+
+struct fp8_head_handle {
+    int V, H, VT, device;
+    uint8_t* mem;      // repacked weights | scales | per-tile partials | ticket
+    void* w;
+    float* scale;
+    float* pval;
+    int32_t* pidx;
+    unsigned* ticket;
+};
+
+static uint64_t a256(uint64_t v) { return (v + 255) & ~(uint64_t)255; }
+
+extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, void* stream,
+                                      fp8_head_handle** out) {
+    if (!out) return moe_fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (vocab <= 0 || hidden <= 0) return moe_fail(MOE_ERR_INVALID_ARG, "vocab and hidden must be positive");
+    if (hidden % 256 || hidden > 2560)
+        return moe_fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", hidden);
+    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
+    if (!row_scale.ptr || (uintptr_t)row_scale.ptr % 4)
+        return moe_fail(MOE_ERR_INVALID_ARG, "row_scale is NULL or not 4-byte aligned");
+    if (w.dtype != MOE_DT_E4M3) return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected E4M3 (%d)", w.dtype, MOE_DT_E4M3);
+    if (row_scale.dtype != MOE_DT_FP32)
+        return moe_fail(MOE_ERR_DTYPE, "row_scale: dtype tag %d, expected FP32 (%d)", row_scale.dtype, MOE_DT_FP32);
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    fp8_head_handle* h = new (std::nothrow) fp8_head_handle();
+    if (!h) return moe_fail(MOE_ERR_OOM, "host allocation failed");
+    h->V = vocab;
+    h->H = hidden;
+    h->VT = (vocab + 63) / 64;
+    (void)hipGetDevice(&h->device);
+    const uint64_t wb = a256((uint64_t)h->VT * 64 * hidden), sb = a256((uint64_t)h->VT * 64 * 4);
+    const uint64_t pb = a256((uint64_t)h->VT * 4 * 4);
+    if (hipMalloc(&h->mem, wb + sb + 2 * pb + 256) != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return moe_fail(MOE_ERR_OOM, "hipMalloc for the LM head failed");
+    }
+    h->w = h->mem;
+    h->scale = (float*)(h->mem + wb);
+    h->pval = (float*)(h->mem + wb + sb);
+    h->pidx = (int32_t*)(h->mem + wb + sb + pb);
+    h->ticket = (unsigned*)(h->mem + wb + sb + 2 * pb);
+    hipError_t e = hipMemsetAsync(h->ticket, 0, 256, (hipStream_t)stream);
+    if (e == hipSuccess) e = head::launch_repack_head(w.ptr, row_scale.ptr, h->w, h->scale, vocab, hidden, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        (void)hipFree(h->mem);
+        delete h;
+        return moe_fail(MOE_ERR_HIP, "LM-head repack failed: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t T, float* logits, int32_t* argmax,
+                                   void* stream) {
+    if (!h) return moe_fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!x || (uintptr_t)x % 16) return moe_fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+    if (!argmax) return moe_fail(MOE_ERR_INVALID_ARG, "argmax is NULL");
+    if (T < 1 || T > 4) return moe_fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [1, 4]", T);
+    if (hipSetDevice(h->device) != hipSuccess) return moe_fail(MOE_ERR_HIP, "hipSetDevice failed");
+    hipError_t e = head::launch_head(h->w, h->scale, (const uint16_t*)x, T, logits, argmax, h->pval, h->pidx, h->ticket,
+                                     h->V, h->H, (hipStream_t)stream);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_destroy(fp8_head_handle* h) {
+    if (!h) return MOE_OK;
+    (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->mem);
+    delete h;
+    return MOE_OK;
+}

@@ -1,0 +1,182 @@
+// head_kernels.hip -- FP8 LM-head GEMV with a fused per-token argmax (gfx950).
+//
+// The head is the 157,184 x 2,560 vocabulary projection that is read in full for every generated
+// token and is quantised to FP8 at load time to halve those reads (tanhow.com, "NVIDIA 在单台 DGX
+// Spark 上叠加三项优化...", section "三项优化是什么", item 2; devotd.net,
+// "dgx-spark-moe-inference-optimizations", section 2).  Weights are OCP E4M3 with one fp32 scale
+// per row; x stays bf16; logits are fp32; argmax takes the lowest index among equal maxima.
+//
+// Layout (repacked by fp8_head_create): [ceil(V/64) tiles][H/16 units][64 lanes][16 B], lane = row
+// within the 64-row tile, so each wave-wide 16-byte load reads 1 KiB of contiguous HBM.  Each
+// workgroup owns one 64-row tile; its waves split the K range, E4M3 pairs are converted exactly to
+// bf16 pairs in VGPRs and multiplied with bf16 x pairs from LDS by v_dot2_f32_bf16 (exact products,
+// fp32 accumulation).  The last workgroup to finish reduces the per-tile (max, index) pairs.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace head {
+
+constexpr int kWave = 64;
+constexpr int kUnit = 16;           // E4M3 codes per 16-byte unit
+constexpr int kUnitsPerWave = 16;   // 256 K elements per wave
+constexpr int kSlice = kUnit * kUnitsPerWave;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__global__ void repack_head(const uint4* __restrict__ src, const float* __restrict__ ssrc, uint4* __restrict__ dst,
+                            float* __restrict__ sdst, int V, int H, int VT) {
+    const int NU = H / kUnit;
+    const uint64_t total = (uint64_t)VT * NU * kWave;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+         u += (uint64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(u % kWave);
+        const uint64_t r1 = u / kWave;
+        const int unit = (int)(r1 % NU);
+        const uint64_t vt = r1 / NU;
+        const uint64_t row = vt * kWave + lane;
+        dst[u] = row < (uint64_t)V ? src[row * NU + unit] : make_uint4(0, 0, 0, 0);
+        if (unit == 0) sdst[row] = row < (uint64_t)V ? ssrc[row] : 0.0f;
+    }
+}
+
+struct HeadArgs {
+    const uint4* w;       // repacked E4M3
+    const float* scale;   // [VT*64], zero past V
+    const uint16_t* x;    // [T][H] bf16
+    float* logits;        // [T][V] or null
+    int32_t* argmax;      // [T]
+    float* pval;          // [VT][T] per-tile maxima
+    int32_t* pidx;        // [VT][T]
+    unsigned* ticket;
+    int V, H;
+};
+
+__device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
+    if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+template <int T>
+__global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
+    extern __shared__ uint32_t xs[];  // [T][H/2] bf16 pairs
+    __shared__ float red[10][T][kWave];
+    __shared__ int is_last;
+    const int vt = blockIdx.x, VT = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    const int H = a.H, NU = H / kUnit, Hh = H / 2;
+
+    uint4 wr[kUnitsPerWave];
+    {
+        const uint4* p = a.w + ((size_t)vt * NU + (size_t)wv * kUnitsPerWave) * kWave + lane;
+#pragma unroll
+        for (int i = 0; i < kUnitsPerWave; ++i) wr[i] = ld_nt(p + i * kWave);
+    }
+    for (int i = tid; i < T * Hh; i += blockDim.x) xs[i] = ((const uint32_t*)a.x)[i];
+    __syncthreads();
+
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kUnitsPerWave; ++i) {
+        const int pbase = (wv * kUnitsPerWave + i) * (kUnit / 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint4 xv[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase + 4 * h);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t wd = comp(wr[i], 2 * h + q);
+                const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, false);
+                const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, true);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q)),
+                                                            acc[t], false);
+                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q + 1)),
+                                                            acc[t], false);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[wv][t][lane] = acc[t];
+    __syncthreads();
+
+    if (wv < T) {
+        const int t = wv;
+        float s = 0.0f;
+        for (int w = 0; w < NW; ++w) s += red[w][t][lane];
+        const int row = vt * kWave + lane;
+        float v = -INFINITY;
+        int idx = 0x7fffffff;
+        if (row < a.V) {
+            v = s * a.scale[row];
+            idx = row;
+            if (a.logits) a.logits[(size_t)t * a.V + row] = v;
+        }
+        for (int off = 32; off > 0; off >>= 1) better(v, idx, __shfl_xor(v, off, 64), __shfl_xor(idx, off, 64));
+        if (lane == 0) {
+            a.pval[(size_t)vt * T + t] = v;
+            a.pidx[(size_t)vt * T + t] = idx;
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) is_last = atomicAdd(a.ticket, 1u) == (unsigned)(VT - 1);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    if (wv < T) {
+        const int t = wv;
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int i = lane; i < VT; i += kWave)
+            better(bv, bi, __builtin_nontemporal_load(a.pval + (size_t)i * T + t),
+                   __builtin_nontemporal_load(a.pidx + (size_t)i * T + t));
+        for (int off = 32; off > 0; off >>= 1) better(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
+        if (lane == 0) a.argmax[t] = bi;
+    }
+    if (tid == 0) *a.ticket = 0u;
+}
+
+hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream) {
+    const int VT = (V + kWave - 1) / kWave;
+    uint64_t total = (uint64_t)VT * (H / kUnit) * kWave;
+    uint64_t g = (total + 255) / 256;
+    if (g > 65536) g = 65536;
+    repack_head<<<(unsigned)g, 256, 0, stream>>>((const uint4*)w, (const float*)s, (uint4*)dw, (float*)ds, V, H, VT);
+    return hipGetLastError();
+}
+
+hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
+                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, hipStream_t stream) {
+    const int VT = (V + kWave - 1) / kWave;
+    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, V, H};
+    const unsigned block = kWave * (H / kSlice);
+    const size_t lds = (size_t)T * H * 2;
+    switch (T) {
+        case 1: head_kernel<1><<<VT, block, lds, stream>>>(a); break;
+        case 2: head_kernel<2><<<VT, block, lds, stream>>>(a); break;
+        case 3: head_kernel<3><<<VT, block, lds, stream>>>(a); break;
+        case 4: head_kernel<4><<<VT, block, lds, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace head

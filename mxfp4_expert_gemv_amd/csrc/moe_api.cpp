@@ -1,0 +1,268 @@
+// moe_api.cpp -- C ABI of the MI355X MoE decode library (declarations and contracts in
+// include/moe_decode.h).  Validation runs before any HIP call; every unsupported request is an
+// error, never a fallback to a slower path.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/moe_decode.h"
+#include "moe_launch.h"
+
+
+using moe::Shape;
+
+static thread_local char g_err[512];
+
+moe_status moe_fail(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+#define fail moe_fail
+
+static uint64_t align256(uint64_t v) { return (v + 255) & ~(uint64_t)255; }
+
+struct moe_decode_handle {
+    moe_decode_config cfg;
+    Shape sh;
+    int device;
+    // per layer: one allocation holding router, w13, w13_s, w2, w2_s (256-byte aligned pieces)
+    std::vector<uint8_t*> layer_mem;
+    std::vector<char> layer_set;
+    uint64_t off_w13, off_w13s, off_w2, off_w2s, layer_bytes;
+    // workspace
+    uint8_t* ws;
+    uint64_t ws_bytes;
+    uint16_t* xin;
+    uint16_t* xbuf[2];
+    float* partial;
+    unsigned* ticket;
+    moe::SlotTable* slots;
+    float* h;
+    float* hamax;
+};
+
+extern "C" const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_DTYPE: return "dtype tag mismatch";
+        case MOE_ERR_OOM: return "out of device memory";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_NO_DEVICE: return "no HIP device";
+        case MOE_ERR_STATE: return "invalid state";
+    }
+    return "unknown status";
+}
+
+extern "C" const char* moe_last_error(void) { return g_err; }
+
+static moe_status check_config(const moe_decode_config* c) {
+    if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+    if (c->struct_size != sizeof(moe_decode_config))
+        return fail(MOE_ERR_INVALID_ARG, "config struct_size %u != %zu", c->struct_size, sizeof(moe_decode_config));
+    if (c->hidden <= 0 || c->num_experts <= 0 || c->top_k <= 0 || c->inter <= 0 || c->max_tokens <= 0 ||
+        c->num_layers <= 0 || c->num_shared < 0)
+        return fail(MOE_ERR_INVALID_ARG, "sizes must be positive");
+    if (c->top_k > c->num_experts) return fail(MOE_ERR_INVALID_ARG, "top_k %d > num_experts %d", c->top_k, c->num_experts);
+    if (c->num_shared > 1) return fail(MOE_ERR_UNSUPPORTED, "num_shared %d (0 or 1 supported)", c->num_shared);
+    if (c->hidden % moe::kGuSlice || c->hidden > 2560)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", c->hidden);
+    if (c->num_experts > 512) return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > 512", c->num_experts);
+    if (c->top_k > moe::kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k %d > 8", c->top_k);
+    if (c->max_tokens > moe::kMaxTokens) return fail(MOE_ERR_UNSUPPORTED, "max_tokens %d > 4", c->max_tokens);
+    if (c->inter % moe::kGuHalf || !moe::down_supported(c->inter) || c->inter > 768)
+        return fail(MOE_ERR_UNSUPPORTED, "inter %d (64, 128, 256, 512 or 768 supported)", c->inter);
+    if (c->flags & ~(uint32_t)MOE_F_RMSNORM_INPUT) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+    return MOE_OK;
+}
+
+static moe_status device_present() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    return MOE_OK;
+}
+
+static void free_handle(moe_decode_handle* h) {
+    for (uint8_t* p : h->layer_mem)
+        if (p) (void)hipFree(p);
+    if (h->ws) (void)hipFree(h->ws);
+    delete h;
+}
+
+extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stream, moe_decode_handle** out) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if ((s = device_present()) != MOE_OK) return s;
+    (void)stream;
+    moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
+    if (!h) return fail(MOE_ERR_OOM, "host allocation failed");
+    h->cfg = *cfg;
+    h->sh = Shape{cfg->hidden, cfg->num_experts, cfg->top_k, cfg->num_shared, cfg->inter};
+    const Shape& sh = h->sh;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    }
+    const uint64_t nexp = (uint64_t)sh.E + sh.S;
+    h->off_w13 = align256(sh.router_bytes());
+    h->off_w13s = h->off_w13 + align256(nexp * sh.w13_bytes_per_expert());
+    h->off_w2 = h->off_w13s + align256(nexp * sh.w13s_bytes_per_expert());
+    h->off_w2s = h->off_w2 + align256(nexp * sh.w2_bytes_per_expert());
+    h->layer_bytes = h->off_w2s + align256(nexp * sh.w2s_bytes_per_expert());
+    h->layer_mem.assign(cfg->num_layers, nullptr);
+    h->layer_set.assign(cfg->num_layers, 0);
+    for (int l = 0; l < cfg->num_layers; ++l) {
+        if (hipMalloc(&h->layer_mem[l], h->layer_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            free_handle(h);
+            return fail(MOE_ERR_OOM, "hipMalloc of %llu bytes for layer %d failed", (unsigned long long)h->layer_bytes, l);
+        }
+    }
+    // workspace
+    const int T = moe::kMaxTokens, G = sh.H / moe::kRouterSlice;
+    uint64_t o = 0;
+    const uint64_t o_xin = o; o += align256((uint64_t)T * sh.H * 2);
+    const uint64_t o_xb0 = o; o += align256((uint64_t)T * sh.H * 2);
+    const uint64_t o_xb1 = o; o += align256((uint64_t)T * sh.H * 2);
+    const uint64_t o_part = o; o += align256((uint64_t)G * T * sh.RT() * moe::kRouterRows * 4);
+    const uint64_t o_tick = o; o += 256;
+    const uint64_t o_slot = o; o += align256(sizeof(moe::SlotTable));
+    const uint64_t o_h = o; o += align256((uint64_t)moe::kMaxSlots * T * sh.I * 4);
+    const uint64_t o_ham = o; o += align256((uint64_t)moe::kMaxSlots * T * (sh.I / moe::kGuHalf) * 4);
+    h->ws_bytes = o;
+    if (hipMalloc(&h->ws, o) != hipSuccess) {
+        (void)hipGetLastError();
+        free_handle(h);
+        return fail(MOE_ERR_OOM, "workspace hipMalloc failed");
+    }
+    if (hipMemset(h->ws, 0, o) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        free_handle(h);
+        return fail(MOE_ERR_HIP, "workspace clear failed");
+    }
+    h->xin = (uint16_t*)(h->ws + o_xin);
+    h->xbuf[0] = (uint16_t*)(h->ws + o_xb0);
+    h->xbuf[1] = (uint16_t*)(h->ws + o_xb1);
+    h->partial = (float*)(h->ws + o_part);
+    h->ticket = (unsigned*)(h->ws + o_tick);
+    h->slots = (moe::SlotTable*)(h->ws + o_slot);
+    h->h = (float*)(h->ws + o_h);
+    h->hamax = (float*)(h->ws + o_ham);
+    *out = h;
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+static moe_status check_tensor(const moe_tensor& t, moe_dtype want, const char* name) {
+    if (!t.ptr) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", name);
+    if ((uintptr_t)t.ptr % 16) return fail(MOE_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);
+    if (t.dtype != want) return fail(MOE_ERR_DTYPE, "%s: dtype tag %d, expected %d", name, t.dtype, (int)want);
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_layer_desc* d,
+                                           void* stream) {
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "descriptor is NULL");
+    if (layer < 0 || layer >= h->cfg.num_layers)
+        return fail(MOE_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, h->cfg.num_layers);
+    moe_status s;
+    if ((s = check_tensor(d->router, MOE_DT_BF16, "router")) != MOE_OK) return s;
+    if ((s = check_tensor(d->w13, MOE_DT_E2M1X2, "w13")) != MOE_OK) return s;
+    if ((s = check_tensor(d->w13_s, MOE_DT_E8M0, "w13_s")) != MOE_OK) return s;
+    if ((s = check_tensor(d->w2, MOE_DT_E2M1X2, "w2")) != MOE_OK) return s;
+    if ((s = check_tensor(d->w2_s, MOE_DT_E8M0, "w2_s")) != MOE_OK) return s;
+    if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
+    uint8_t* m = h->layer_mem[layer];
+    hipError_t e = moe::launch_repack(h->sh, d->router.ptr, d->w13.ptr, d->w13_s.ptr, d->w2.ptr, d->w2_s.ptr, m,
+                                      m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "repack launch failed: %s", hipGetErrorString(e));
+    h->layer_set[layer] = 1;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, const moe_outputs* out,
+                                     void* stream) {
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!x || (uintptr_t)x % 16) return fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+    if (T < 1 || T > h->cfg.max_tokens)
+        return fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [1, %d]", T, h->cfg.max_tokens);
+    if (out && out->struct_size != sizeof(moe_outputs))
+        return fail(MOE_ERR_INVALID_ARG, "outputs struct_size %u != %zu", out->struct_size, sizeof(moe_outputs));
+    const int L = h->cfg.num_layers;
+    for (int l = 0; l < L; ++l)
+        if (!h->layer_set[l]) return fail(MOE_ERR_STATE, "layer %d has not been set", l);
+    moe_outputs o{};
+    if (out) o = *out;
+    if (o.x_out && (uintptr_t)o.x_out % 4) return fail(MOE_ERR_INVALID_ARG, "x_out not 4-byte aligned");
+    if (o.x_codes && (uintptr_t)o.x_codes % 2) return fail(MOE_ERR_INVALID_ARG, "x_codes not 2-byte aligned");
+    if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
+    const Shape& sh = h->sh;
+    const bool norm = (h->cfg.flags & MOE_F_RMSNORM_INPUT) != 0;
+    const size_t TH = (size_t)T * sh.H;
+    for (int l = 0; l < L; ++l) {
+        const uint8_t* m = h->layer_mem[l];
+        moe::LayerPtrs lp{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s};
+        moe::RunPtrs p{};
+        p.x = l == 0 ? (const uint16_t*)x : h->xbuf[l & 1];
+        const bool last = l == L - 1;
+        if (!last) p.xnext = h->xbuf[(l + 1) & 1];
+        else p.xnext = (uint16_t*)o.x_out;
+        p.y = last ? o.y : nullptr;
+        p.ids = o.topk_ids ? o.topk_ids + (size_t)l * T * sh.k : nullptr;
+        p.w = o.topk_w ? o.topk_w + (size_t)l * T * sh.k : nullptr;
+        p.trace = o.x_trace ? (uint16_t*)o.x_trace + (size_t)l * TH : nullptr;
+        p.x_scale = o.x_scale ? o.x_scale + (size_t)l * T : nullptr;
+        p.x_codes = o.x_codes ? o.x_codes + (size_t)l * TH : nullptr;
+        p.xin = h->xin;
+        p.partial = h->partial;
+        p.ticket = h->ticket;
+        p.slots = h->slots;
+        p.h = h->h;
+        p.hamax = h->hamax;
+        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_info* info) {
+    if (!h || !info) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+    if (info->struct_size != sizeof(moe_decode_info))
+        return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
+    const Shape& sh = h->sh;
+    memset(info->variant, 0, sizeof info->variant);
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-router%d-gu%dw-dn%dx%d", moe::kRouterWaves,
+             sh.H / moe::kGuSlice, sh.down_ksub(), sh.down_iters());
+    info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
+    info->workspace_bytes = h->ws_bytes;
+    const uint64_t expert = sh.w13_bytes_per_expert() + sh.w13s_bytes_per_expert() + sh.w2_bytes_per_expert() +
+                            sh.w2s_bytes_per_expert();
+    info->bytes_per_layer_t1 = (uint64_t)sh.E * sh.H * 2 + (uint64_t)(sh.k + sh.S) * expert;
+    int n = 0;
+    for (char c : h->layer_set) n += c ? 1 : 0;
+    info->layers_set = n;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_destroy(moe_decode_handle* h) {
+    if (!h) return MOE_OK;
+    (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    free_handle(h);
+    return MOE_OK;
+}

@@ -1,0 +1,44 @@
+// moe_launch.h -- host-side launcher interface between the C ABI (moe_api.cpp) and the kernels
+// (moe_kernels.hip).  Private to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_layout.h"
+
+namespace moe {
+
+struct LayerPtrs {
+    const void *router, *w13, *w13s, *w2, *w2s;  // repacked tensors of one layer
+};
+
+struct RunPtrs {
+    const uint16_t* x;  // layer input residual x_l, bf16 [T][H]
+    uint16_t* xnext;    // bf16(x_l + y) or null
+    float* y;           // fp32 [T][H] or null
+    int32_t* ids;       // [T][k] or null
+    float* w;           // [T][k] or null
+    uint16_t* trace;    // copy of x_l or null
+    float* x_scale;     // [T] or null
+    uint8_t* x_codes;   // [T][H] or null
+    // workspace
+    uint16_t* xin;
+    float* partial;
+    unsigned* ticket;
+    SlotTable* slots;
+    float* h;
+    float* hamax;
+};
+
+hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,
+                         const void* w2s, void* d_router, void* d_w13, void* d_w13s, void* d_w2, void* d_w2s,
+                         hipStream_t stream);
+hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                        hipStream_t stream);
+bool down_supported(int I);
+
+}  // namespace moe
+
+// Records a message for moe_last_error() and returns s (defined in moe_api.cpp).
+#include "../../include/moe_decode.h"
+moe_status moe_fail(moe_status s, const char* fmt, ...);

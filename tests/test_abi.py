@@ -1,0 +1,87 @@
+"""The C-ABI library loads without a GPU, exports every function include/moe_decode.h declares,
+and validates its arguments before any HIP call (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_expert_gemv_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+
+
+def _status(cfg_kwargs):
+    c = dict(hidden=2560, num_experts=512, top_k=8, num_shared=1, inter=768, max_tokens=4, num_layers=1, flags=0)
+    c.update(cfg_kwargs)
+    cfg = moe.Config(ctypes.sizeof(moe.Config), *[c[f] for f in ("hidden", "num_experts", "top_k", "num_shared",
+                                                                  "inter", "max_tokens", "num_layers", "flags")])
+    if "struct_size" in cfg_kwargs:
+        cfg.struct_size = cfg_kwargs["struct_size"]
+    h = ctypes.c_void_p()
+    return moe.lib().moe_decode_create(ctypes.byref(cfg), None, ctypes.byref(h))
+
+
+@pytest.mark.parametrize("bad,status", [
+    ({"struct_size": 4}, -1), ({"hidden": 0}, -1), ({"top_k": 9, "num_experts": 8}, -1),
+    ({"hidden": 2500}, -2), ({"hidden": 4096}, -2), ({"num_experts": 1024}, -2), ({"top_k": 9}, -2),
+    ({"num_shared": 2}, -2), ({"inter": 96}, -2), ({"inter": 1024}, -2), ({"max_tokens": 5}, -2),
+    ({"flags": 0x80}, -1),
+])
+def test_create_rejects_bad_configs_before_any_hip_call(bad, status):
+    assert _status(bad) == status
+    assert moe.lib().moe_last_error()
+
+
+def test_valid_config_without_device_is_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _status({}) == -6
+    assert _status({"hidden": 256, "num_experts": 16, "top_k": 2, "inter": 64}) == -6
+
+
+def test_null_arguments():
+    L = moe.lib()
+    assert L.moe_decode_create(None, None, None) == -1
+    assert L.moe_decode_set_layer(None, 0, None, None) == -1
+    assert L.moe_decode_run(None, None, 1, None, None) == -1
+    assert L.moe_decode_query(None, None) == -1
+    assert L.moe_decode_destroy(None) == 0
+    assert L.fp8_head_run(None, None, 1, None, None, None) == -1
+    assert L.fp8_head_destroy(None) == 0
+    t = moe.Tensor(None, moe.DT_E4M3)
+    h = ctypes.c_void_p()
+    assert L.fp8_head_create(100, 2560, t, moe.Tensor(None, moe.DT_FP32), None, ctypes.byref(h)) == -1
+    assert L.moe_status_string(-3) == b"dtype tag mismatch"
+
+
+def test_head_dtype_tags_checked_before_device():
+    L = moe.lib()
+    h = ctypes.c_void_p()
+    buf = ctypes.create_string_buffer(64)
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    # bf16-tagged weights where E4M3 is required: the silent-reinterpretation trap is an error
+    assert L.fp8_head_create(100, 2560, moe.Tensor(addr, moe.DT_BF16), moe.Tensor(addr, moe.DT_FP32), None,
+                             ctypes.byref(h)) == -3
+    assert L.fp8_head_create(100, 2560, moe.Tensor(addr, moe.DT_E4M3), moe.Tensor(addr, moe.DT_BF16), None,
+                             ctypes.byref(h)) == -3
+    assert L.fp8_head_create(100, 2000, moe.Tensor(addr, moe.DT_E4M3), moe.Tensor(addr, moe.DT_FP32), None,
+                             ctypes.byref(h)) == -2

@@ -1,0 +1,78 @@
+"""GPU parity of the full-size 42-layer MoE decode stack (hidden 2560, 512 experts, top-8 + 1
+shared, width 768, ~67.6 GB of resident MXFP4 experts), at 1 and 4 tokens, teacher-forced: for
+sampled layers the oracle recomputes the layer from the GPU's own input residual x_l (traced by the
+library) and checks ids, FP8 activation codes, and the layer's effect on the residual.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_expert_gemv_amd as moe
+import oracle
+import synth
+from gpu_cases import MANIFEST, DeviceLayer, Y_TOL, create, normwise_err, run_layer
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = (0, 1, 2, 21, 40, 41)
+
+
+@pytest.fixture(scope="module")
+def stack():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    st = MANIFEST["stack"]
+    shape, L = synth.FLASH, st["layers"]
+    h = create(shape, max_tokens=4, num_layers=L, flags=moe.F_RMSNORM_INPUT)
+    layers = []
+    for l in range(L):
+        lay = DeviceLayer(shape, st["seed"], l, st["router_attempts"][l])
+        lay.set_into(h, l)
+        torch.cuda.synchronize()
+        layers.append((lay.router_host, st["seed"], l))
+        del lay
+    yield shape, h, layers, st
+    moe.moe_decode_destroy(h)
+
+
+def _ulp_bf16(v):
+    a = np.abs(v.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_stack_teacher_forced(stack, T):
+    shape, h, layers, st = stack
+    L = len(layers)
+    x0 = synth.tokens(shape.hidden, st["seed"], 4, st["x_attempt"])[:T]
+    gpu = run_layer(h, shape, x0, num_layers=L)
+    assert (gpu["x_trace"][0] == x0).all()
+    diverged = [l for l in range(L) if gpu["topk_ids"][l].tolist() != st["ids_t4"][l][:T]]
+    print(f"T={T}: layers whose ids differ from the oracle's own trajectory: {diverged}")
+    for l in SAMPLE:
+        router_host, seed, _ = layers[l]
+        x_l = gpu["x_trace"][l]
+        xin = oracle.rmsnorm_bf16(x_l)
+        ro = oracle.route(shape, router_host, xin)
+        well_posed = all(oracle.topk_margin_ok(ro["logits"][t], ro["bounds"][t], shape.top_k) for t in range(T))
+        experts = {e: synth.expert(shape, seed, l, e) for e in sorted(set(ro["ids"].reshape(-1).tolist())) + [512]}
+        y_o, tr = oracle.moe_layer(shape, router_host, experts, xin)
+        if well_posed:
+            assert (gpu["topk_ids"][l] == tr["ids"]).all(), l
+        assert np.abs(gpu["topk_w"][l] - tr["w"]).max() <= 1e-5
+        assert (gpu["x_scale"][l] == tr["sx"]).all(), l
+        assert (gpu["x_codes"][l] == tr["qx"]).all(), l
+        if l < L - 1:
+            # x_{l+1} = bf16(x_l + y): within half a bf16 ulp of x_l + y_gpu, y_gpu within Y_TOL of y_ref
+            x_next = oracle.bf16_decode(gpu["x_trace"][l + 1]).astype(np.float64)
+            exact = oracle.bf16_decode(x_l).astype(np.float64) + y_o.astype(np.float64)
+            slack = 0.5 * _ulp_bf16(x_next) * (1 + 2.0 ** -7) + Y_TOL * np.abs(y_o).max(axis=1, keepdims=True)
+            assert (np.abs(x_next - exact) <= slack).all(), l
+        else:
+            err = normwise_err(gpu["y"], y_o)
+            print(f"T={T}: last-layer normwise y error {err}")
+            assert (err <= Y_TOL).all()
+            x_out = oracle.bf16_decode(gpu["x_out"]).astype(np.float64)
+            exact = oracle.bf16_decode(x_l).astype(np.float64) + gpu["y"].astype(np.float64)
+            assert (np.abs(x_out - exact) <= 0.5 * _ulp_bf16(x_out) * (1 + 2.0 ** -7)).all()
