@@ -117,8 +117,7 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     for (int t = 0; t < T; ++t) red[wv][t][lane] = acc[t];
     __syncthreads();
 
-    if (wv < T) {
-        const int t = wv;
+    for (int t = wv; t < T; t += NW) {
         float s = 0.0f;
         for (int w = 0; w < NW; ++w) s += red[w][t][lane];
         const int row = vt * kWave + lane;
@@ -141,8 +140,7 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    if (wv < T) {
-        const int t = wv;
+    for (int t = wv; t < T; t += NW) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         for (int i = lane; i < VT; i += kWave)

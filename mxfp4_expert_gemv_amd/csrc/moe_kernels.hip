@@ -506,24 +506,28 @@ __global__ __launch_bounds__(640) void gateup_kernel(GateUpArgs a) {
         if (j < ntok) red[wv][j][lane] = acc[j];
     __syncthreads();
 
-    // 4. sum the K slices, h = SiLU(g) * u, tile max |h|
-    if (tid < kGuHalf * ntok) {
-        const int j = tid >> 5, r = tid & 31;
-        float g = 0.0f, u = 0.0f;
-        for (int w = 0; w < NW; ++w) {
-            g += red[w][j][r];
-            u += red[w][j][kGuHalf + r];
-        }
-        float s = sx[0];
+    // 4. sum the K slices, h = SiLU(g) * u, tile max |h| (one half-wave per token and pass)
+    for (int base = 0; base < kGuHalf * ntok; base += blockDim.x) {
+        const int idx = base + tid, j = idx >> 5, r = idx & 31;
+        const bool act = idx < kGuHalf * ntok;
+        float hv = 0.0f;
+        if (act) {
+            float g = 0.0f, u = 0.0f;
+            for (int w = 0; w < NW; ++w) {
+                g += red[w][j][r];
+                u += red[w][j][kGuHalf + r];
+            }
+            float s = sx[0];
 #pragma unroll
-        for (int t = 1; t < T; ++t)
-            if (tok[j] == t) s = sx[t];
-        g *= s;
-        u *= s;
-        const float hv = g / (1.0f + expf(-g)) * u;
-        a.h[((size_t)slot * kMaxTokens + j) * I + tile * kGuHalf + r] = hv;
+            for (int t = 1; t < T; ++t)
+                if (tok[j] == t) s = sx[t];
+            g *= s;
+            u *= s;
+            hv = g / (1.0f + expf(-g)) * u;
+            a.h[((size_t)slot * kMaxTokens + j) * I + tile * kGuHalf + r] = hv;
+        }
         const float m = wave_max(fabsf(hv), 32);
-        if (r == 0) a.hamax[((size_t)slot * kMaxTokens + j) * (I / kGuHalf) + tile] = m;
+        if (act && r == 0) a.hamax[((size_t)slot * kMaxTokens + j) * (I / kGuHalf) + tile] = m;
     }
 }
 
@@ -661,8 +665,8 @@ __global__ __launch_bounds__(768) void down_kernel(DownArgs a) {
         for (int t = 0; t < T; ++t) red[wv][t][lane / KSUB] = acc[t];
     }
     __syncthreads();
-    if (tid < R * T) {
-        const int t = tid / R, r = tid - t * R;
+    for (int idx = tid; idx < R * T; idx += blockDim.x) {
+        const int t = idx / R, r = idx - t * R;
         float ysum = 0.0f;
         for (int w = 0; w < NW; ++w) ysum += red[w][t][r];
         const size_t o = (size_t)t * H + (size_t)tile * R + r;
