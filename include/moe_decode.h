@@ -157,6 +157,22 @@ moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, f
                         void* stream);
 moe_status fp8_head_destroy(fp8_head_handle* h);
 
+/* Kernel timing instrumentation.  moe_decode_timing_enable(h, max_runs) makes the next up to
+ * max_runs calls of moe_decode_run record HIP events on their stream around every kernel launch
+ * (one event before the first kernel of each layer and one after each kernel); 0 disables.
+ * moe_decode_timing_read waits for those events and returns, per kernel class, the number of
+ * launches and the summed event-to-event time, then clears the record.  Timing adds one event
+ * record per launch to the stream, so it is meant for a measurement pass of its own. */
+#define MOE_TIMING_CLASSES 3 /* 0 router + top-k, 1 gate/up, 2 down + combine */
+typedef struct {
+    uint32_t struct_size;                     /* sizeof(moe_decode_timing) */
+    int32_t runs;                             /* runs recorded */
+    uint64_t launches[MOE_TIMING_CLASSES];
+    double total_ms[MOE_TIMING_CLASSES];
+} moe_decode_timing;
+moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs);
+moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_timing* out);
+
 const char* moe_status_string(moe_status s);
 /* Message of the last failed call made by this thread ("" if none). */
 const char* moe_last_error(void);

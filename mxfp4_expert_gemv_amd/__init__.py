@@ -22,7 +22,7 @@ F_RMSNORM_INPUT = 0x1
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
-           "moe_decode_destroy", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
+           "moe_decode_destroy", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
            "moe_status_string", "moe_last_error")
 
 
@@ -58,6 +58,14 @@ class Info(ctypes.Structure):
                 ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
 
 
+TIMING_CLASSES = ("router", "gateup", "down")
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("runs", ctypes.c_int32),
+                ("launches", ctypes.c_uint64 * 3), ("total_ms", ctypes.c_double * 3)]
+
+
 _lib = None
 
 
@@ -75,6 +83,8 @@ def lib():
             "moe_decode_run": [vp, vp, i32, ctypes.POINTER(Outputs), vp],
             "moe_decode_query": [vp, ctypes.POINTER(Info)],
             "moe_decode_destroy": [vp],
+            "moe_decode_timing_enable": [vp, i32],
+            "moe_decode_timing_read": [vp, ctypes.POINTER(Timing)],
             "fp8_head_create": [i32, i32, Tensor, Tensor, vp, ctypes.POINTER(vp)],
             "fp8_head_run": [vp, vp, i32, vp, vp, vp],
             "fp8_head_destroy": [vp],
@@ -151,6 +161,18 @@ def moe_decode_query(handle) -> dict:
 
 def moe_decode_destroy(handle) -> None:
     _check(lib().moe_decode_destroy(handle))
+
+
+def moe_decode_timing_enable(handle, max_runs: int) -> None:
+    _check(lib().moe_decode_timing_enable(handle, max_runs))
+
+
+def moe_decode_timing_read(handle) -> dict:
+    t = Timing()
+    t.struct_size = ctypes.sizeof(Timing)
+    _check(lib().moe_decode_timing_read(handle, ctypes.byref(t)))
+    return {"runs": t.runs, **{c: {"launches": t.launches[i], "total_ms": t.total_ms[i]}
+                               for i, c in enumerate(TIMING_CLASSES)}}
 
 
 def fp8_head_create(w, row_scale, stream=None) -> ctypes.c_void_p:

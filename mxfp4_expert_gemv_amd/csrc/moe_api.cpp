@@ -48,7 +48,16 @@ struct moe_decode_handle {
     moe::SlotTable* slots;
     float* h;
     float* hamax;
+    // timing instrumentation: 4 events per layer per recorded run
+    std::vector<hipEvent_t> events;
+    int timing_max_runs = 0, timing_runs = 0;
 };
+
+static void free_events(moe_decode_handle* h) {
+    for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+    h->events.clear();
+    h->timing_max_runs = h->timing_runs = 0;
+}
 
 extern "C" const char* moe_status_string(moe_status s) {
     switch (s) {
@@ -96,6 +105,7 @@ static moe_status device_present() {
 }
 
 static void free_handle(moe_decode_handle* h) {
+    free_events(h);
     for (uint8_t* p : h->layer_mem)
         if (p) (void)hipFree(p);
     if (h->ws) (void)hipFree(h->ws);
@@ -234,9 +244,57 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
         p.slots = h->slots;
         p.h = h->h;
         p.hamax = h->hamax;
-        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, (hipStream_t)stream);
+        hipEvent_t* ev = nullptr;
+        if (h->timing_runs < h->timing_max_runs) ev = &h->events[((size_t)h->timing_runs * L + l) * 4];
+        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, (hipStream_t)stream, ev);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
     }
+    if (h->timing_runs < h->timing_max_runs) ++h->timing_runs;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs) {
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (max_runs < 0 || max_runs > 100000) return fail(MOE_ERR_INVALID_ARG, "max_runs %d out of range", max_runs);
+    if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
+    free_events(h);
+    const size_t n = (size_t)max_runs * h->cfg.num_layers * 4;
+    h->events.reserve(n);
+    for (size_t i = 0; i < n; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            free_events(h);
+            return fail(MOE_ERR_HIP, "hipEventCreate failed");
+        }
+        h->events.push_back(e);
+    }
+    h->timing_max_runs = max_runs;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_timing* out) {
+    if (!h || !out) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+    if (out->struct_size != sizeof(moe_decode_timing))
+        return fail(MOE_ERR_INVALID_ARG, "timing struct_size %u != %zu", out->struct_size, sizeof(moe_decode_timing));
+    const uint32_t ss = out->struct_size;
+    memset(out, 0, sizeof *out);
+    out->struct_size = ss;
+    out->runs = h->timing_runs;
+    const int L = h->cfg.num_layers;
+    for (int r = 0; r < h->timing_runs; ++r) {
+        for (int l = 0; l < L; ++l) {
+            hipEvent_t* ev = &h->events[((size_t)r * L + l) * 4];
+            if (hipEventSynchronize(ev[3]) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
+            for (int c = 0; c < MOE_TIMING_CLASSES; ++c) {
+                float ms = 0.0f;
+                if (hipEventElapsedTime(&ms, ev[c], ev[c + 1]) != hipSuccess)
+                    return fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
+                out->total_ms[c] += ms;
+                out->launches[c] += 1;
+            }
+        }
+    }
+    h->timing_runs = 0;
     return MOE_OK;
 }
 

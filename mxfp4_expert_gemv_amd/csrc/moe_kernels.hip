@@ -713,15 +713,18 @@ int max_slots(const Shape& sh, int T) {
 
 template <int T>
 static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, hipEvent_t* ev) {
+    if (ev) (void)hipEventRecord(ev[0], stream);
     RouterArgs ra{(const uint4*)L.router, P.x, P.xin, P.trace, P.partial, P.ticket, P.slots, P.ids, P.w,
                   sh.H, sh.E, sh.k, sh.S, normalize ? 1 : 0};
     router_kernel<T><<<dim3(sh.H / kRouterSlice, sh.RT()), 256, 0, stream>>>(ra);
+    if (ev) (void)hipEventRecord(ev[1], stream);
 
     const int slots = max_slots(sh, T);
     GateUpArgs ga{(const uint4*)L.w13, (const uint2*)L.w13s, P.xin, P.slots, P.h, P.hamax, P.x_scale, P.x_codes,
                   sh.H, sh.I};
     gateup_kernel<T><<<dim3(sh.I / kGuHalf, slots), 64 * (sh.H / kGuSlice), (size_t)T * sh.H * 2, stream>>>(ga);
+    if (ev) (void)hipEventRecord(ev[2], stream);
 
     DownArgs da{(const uint4*)L.w2, (const uint8_t*)L.w2s, P.slots, P.h, P.hamax, P.xnext ? P.x : nullptr,
                 P.xnext, P.y, sh.H, sh.I};
@@ -739,16 +742,17 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     else if (ksub == 4 && iters == 4) down_kernel<4, 4, T, S><<<grid, block, lds, stream>>>(da);
     else if (ksub == 4 && iters == 6) down_kernel<4, 6, T, S><<<grid, block, lds, stream>>>(da);
     else return hipErrorInvalidValue;
+    if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError();
 }
 
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t* ev) {
     switch (T) {
-        case 1: return launch_layer_t<1>(sh, L, P, normalize, stream);
-        case 2: return launch_layer_t<2>(sh, L, P, normalize, stream);
-        case 3: return launch_layer_t<3>(sh, L, P, normalize, stream);
-        case 4: return launch_layer_t<4>(sh, L, P, normalize, stream);
+        case 1: return launch_layer_t<1>(sh, L, P, normalize, stream, ev);
+        case 2: return launch_layer_t<2>(sh, L, P, normalize, stream, ev);
+        case 3: return launch_layer_t<3>(sh, L, P, normalize, stream, ev);
+        case 4: return launch_layer_t<4>(sh, L, P, normalize, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -33,8 +33,9 @@ struct RunPtrs {
 hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,
                          const void* w2s, void* d_router, void* d_w13, void* d_w13s, void* d_w2, void* d_w2s,
                          hipStream_t stream);
+// ev (nullable) = 4 events recorded before the router and after each of the three kernels.
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
-                        hipStream_t stream);
+                        hipStream_t stream, hipEvent_t* ev);
 bool down_supported(int I);
 
 }  // namespace moe
