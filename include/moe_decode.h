@@ -77,17 +77,19 @@ typedef enum {
 
 /* flags of moe_decode_config */
 #define MOE_F_RMSNORM_INPUT 0x1u /* each layer's MoE input is RMSNorm(x), eps 1e-6, unweighted */
+#define MOE_F_DIRECT_LAUNCH 0x2u /* launch the kernels on the stream at every run instead of replaying
+                                    a HIP graph captured on the first run with the same arguments */
 
 typedef struct moe_decode_handle moe_decode_handle;
 typedef struct fp8_head_handle fp8_head_handle;
 
 typedef struct {
     uint32_t struct_size; /* sizeof(moe_decode_config) */
-    int32_t hidden;       /* H: multiple of 256, 256..2560 */
+    int32_t hidden;       /* H: multiple of 256, 256..2560 (the library checks that it has a kernel) */
     int32_t num_experts;  /* E routed experts: 1..512 */
     int32_t top_k;        /* k: 1..8, <= E */
     int32_t num_shared;   /* S: 0 or 1; the shared expert is stored at expert index E */
-    int32_t inter;        /* I: SwiGLU width: 64, 128, 256, 512 or 768 */
+    int32_t inter;        /* I: SwiGLU width: 64, 128, 256 or 768 */
     int32_t max_tokens;   /* 1..4 tokens per run */
     int32_t num_layers;   /* L >= 1 */
     uint32_t flags;       /* MOE_F_* */
@@ -138,7 +140,10 @@ moe_status moe_decode_create(const moe_decode_config* cfg, void* stream, moe_dec
 moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_layer_desc* desc, void* stream);
 
 /* Runs all L layers on x (BF16 [T][H], device, 16-byte aligned), 1 <= T <= max_tokens.
- * Every layer must have been set.  Only enqueues work on `stream`. */
+ * Every layer must have been set.  Only enqueues work on `stream`.  Unless MOE_F_DIRECT_LAUNCH is
+ * set, the first call with a given (x, T, outputs) captures the kernel sequence into a HIP graph
+ * owned by the handle and every later call with the same arguments replays it (up to 16 graphs;
+ * they hold pointers, not data, so new contents of x and new weights are picked up). */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t num_tokens, const moe_outputs* out,
                           void* stream);
 

@@ -41,13 +41,23 @@ struct moe_decode_handle {
     // workspace
     uint8_t* ws;
     uint64_t ws_bytes;
-    uint16_t* xin;
+    uint8_t* xq;
+    float* xs;
     uint16_t* xbuf[2];
-    float* partial;
-    unsigned* ticket;
+    float* logits;
     moe::SlotTable* slots;
     float* h;
     float* hamax;
+    float* dshared;
+    // captured launch sequences of whole runs, keyed by their arguments
+    struct GraphEntry {
+        const void* x;
+        int32_t T;
+        moe_outputs out;
+        hipGraphExec_t exec;
+    };
+    std::vector<GraphEntry> graphs;
+    hipStream_t capture_stream = nullptr;
     // timing instrumentation: 4 events per layer per recorded run
     std::vector<hipEvent_t> events;
     int timing_max_runs = 0, timing_runs = 0;
@@ -84,14 +94,17 @@ static moe_status check_config(const moe_decode_config* c) {
         return fail(MOE_ERR_INVALID_ARG, "sizes must be positive");
     if (c->top_k > c->num_experts) return fail(MOE_ERR_INVALID_ARG, "top_k %d > num_experts %d", c->top_k, c->num_experts);
     if (c->num_shared > 1) return fail(MOE_ERR_UNSUPPORTED, "num_shared %d (0 or 1 supported)", c->num_shared);
-    if (c->hidden % moe::kGuSlice || c->hidden > 2560)
+    if (c->hidden % 256 || c->hidden > 2560)
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", c->hidden);
     if (c->num_experts > 512) return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > 512", c->num_experts);
     if (c->top_k > moe::kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k %d > 8", c->top_k);
     if (c->max_tokens > moe::kMaxTokens) return fail(MOE_ERR_UNSUPPORTED, "max_tokens %d > 4", c->max_tokens);
-    if (c->inter % moe::kGuHalf || !moe::down_supported(c->inter) || c->inter > 768)
-        return fail(MOE_ERR_UNSUPPORTED, "inter %d (64, 128, 256, 512 or 768 supported)", c->inter);
-    if (c->flags & ~(uint32_t)MOE_F_RMSNORM_INPUT) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+    const moe::Shape sh{c->hidden, c->num_experts, c->top_k, c->num_shared, c->inter};
+    if (c->inter % moe::kBlock || !moe::shape_supported(sh))
+        return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
+                    c->hidden, c->inter);
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH))
+        return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
 
@@ -104,8 +117,15 @@ static moe_status device_present() {
     return MOE_OK;
 }
 
+static void free_graphs(moe_decode_handle* h) {
+    for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
+    h->graphs.clear();
+}
+
 static void free_handle(moe_decode_handle* h) {
     free_events(h);
+    free_graphs(h);
+    if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
     for (uint8_t* p : h->layer_mem)
         if (p) (void)hipFree(p);
     if (h->ws) (void)hipFree(h->ws);
@@ -143,16 +163,17 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
         }
     }
     // workspace
-    const int T = moe::kMaxTokens, G = sh.H / moe::kRouterSlice;
+    const int T = moe::kMaxTokens;
     uint64_t o = 0;
-    const uint64_t o_xin = o; o += align256((uint64_t)T * sh.H * 2);
+    const uint64_t o_xq = o; o += align256((uint64_t)T * sh.H);
+    const uint64_t o_xs = o; o += 256;
     const uint64_t o_xb0 = o; o += align256((uint64_t)T * sh.H * 2);
     const uint64_t o_xb1 = o; o += align256((uint64_t)T * sh.H * 2);
-    const uint64_t o_part = o; o += align256((uint64_t)G * T * sh.RT() * moe::kRouterRows * 4);
-    const uint64_t o_tick = o; o += 256;
+    const uint64_t o_lg = o; o += align256((uint64_t)T * sh.E * 4);
     const uint64_t o_slot = o; o += align256(sizeof(moe::SlotTable));
-    const uint64_t o_h = o; o += align256((uint64_t)moe::kMaxSlots * T * sh.I * 4);
-    const uint64_t o_ham = o; o += align256((uint64_t)moe::kMaxSlots * T * (sh.I / moe::kGuHalf) * 4);
+    const uint64_t o_h = o; o += align256((uint64_t)sh.pairs(T) * sh.I * 4);
+    const uint64_t o_ham = o; o += align256((uint64_t)sh.pairs(T) * sh.gu_tiles() * 4);
+    const uint64_t o_ds = o; o += align256((uint64_t)T * sh.H * 4);
     h->ws_bytes = o;
     if (hipMalloc(&h->ws, o) != hipSuccess) {
         (void)hipGetLastError();
@@ -163,14 +184,19 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
         free_handle(h);
         return fail(MOE_ERR_HIP, "workspace clear failed");
     }
-    h->xin = (uint16_t*)(h->ws + o_xin);
+    if (hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking) != hipSuccess) {
+        free_handle(h);
+        return fail(MOE_ERR_HIP, "hipStreamCreate failed");
+    }
+    h->xq = h->ws + o_xq;
+    h->xs = (float*)(h->ws + o_xs);
     h->xbuf[0] = (uint16_t*)(h->ws + o_xb0);
     h->xbuf[1] = (uint16_t*)(h->ws + o_xb1);
-    h->partial = (float*)(h->ws + o_part);
-    h->ticket = (unsigned*)(h->ws + o_tick);
+    h->logits = (float*)(h->ws + o_lg);
     h->slots = (moe::SlotTable*)(h->ws + o_slot);
     h->h = (float*)(h->ws + o_h);
     h->hamax = (float*)(h->ws + o_ham);
+    h->dshared = (float*)(h->ws + o_ds);
     *out = h;
     g_err[0] = 0;
     return MOE_OK;
@@ -205,6 +231,41 @@ extern "C" moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, 
     return MOE_OK;
 }
 
+// Enqueues the kernels of every layer on `stream` (timing: with the event records).
+static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, const moe_outputs& o, hipStream_t stream,
+                              bool timing) {
+    const Shape& sh = h->sh;
+    const bool norm = (h->cfg.flags & MOE_F_RMSNORM_INPUT) != 0;
+    const int L = h->cfg.num_layers;
+    const size_t TH = (size_t)T * sh.H;
+    for (int l = 0; l < L; ++l) {
+        const uint8_t* m = h->layer_mem[l];
+        moe::LayerPtrs lp{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s};
+        moe::RunPtrs p{};
+        p.x = l == 0 ? (const uint16_t*)x : h->xbuf[l & 1];
+        const bool last = l == L - 1;
+        p.xnext = last ? (uint16_t*)o.x_out : h->xbuf[(l + 1) & 1];
+        p.y = last ? o.y : nullptr;
+        p.ids = o.topk_ids ? o.topk_ids + (size_t)l * T * sh.k : nullptr;
+        p.w = o.topk_w ? o.topk_w + (size_t)l * T * sh.k : nullptr;
+        p.trace = o.x_trace ? (uint16_t*)o.x_trace + (size_t)l * TH : nullptr;
+        p.x_scale = o.x_scale ? o.x_scale + (size_t)l * T : nullptr;
+        p.x_codes = o.x_codes ? o.x_codes + (size_t)l * TH : nullptr;
+        p.xq = h->xq;
+        p.xs = h->xs;
+        p.logits = h->logits;
+        p.slots = h->slots;
+        p.h = h->h;
+        p.hamax = h->hamax;
+        p.dshared = h->dshared;
+        hipEvent_t* ev = nullptr;
+        if (timing) ev = &h->events[((size_t)h->timing_runs * L + l) * 4];
+        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
+    }
+    return MOE_OK;
+}
+
 extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, const moe_outputs* out,
                                      void* stream) {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
@@ -221,35 +282,37 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
     if (o.x_out && (uintptr_t)o.x_out % 4) return fail(MOE_ERR_INVALID_ARG, "x_out not 4-byte aligned");
     if (o.x_codes && (uintptr_t)o.x_codes % 2) return fail(MOE_ERR_INVALID_ARG, "x_codes not 2-byte aligned");
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
-    const Shape& sh = h->sh;
-    const bool norm = (h->cfg.flags & MOE_F_RMSNORM_INPUT) != 0;
-    const size_t TH = (size_t)T * sh.H;
-    for (int l = 0; l < L; ++l) {
-        const uint8_t* m = h->layer_mem[l];
-        moe::LayerPtrs lp{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s};
-        moe::RunPtrs p{};
-        p.x = l == 0 ? (const uint16_t*)x : h->xbuf[l & 1];
-        const bool last = l == L - 1;
-        if (!last) p.xnext = h->xbuf[(l + 1) & 1];
-        else p.xnext = (uint16_t*)o.x_out;
-        p.y = last ? o.y : nullptr;
-        p.ids = o.topk_ids ? o.topk_ids + (size_t)l * T * sh.k : nullptr;
-        p.w = o.topk_w ? o.topk_w + (size_t)l * T * sh.k : nullptr;
-        p.trace = o.x_trace ? (uint16_t*)o.x_trace + (size_t)l * TH : nullptr;
-        p.x_scale = o.x_scale ? o.x_scale + (size_t)l * T : nullptr;
-        p.x_codes = o.x_codes ? o.x_codes + (size_t)l * TH : nullptr;
-        p.xin = h->xin;
-        p.partial = h->partial;
-        p.ticket = h->ticket;
-        p.slots = h->slots;
-        p.h = h->h;
-        p.hamax = h->hamax;
-        hipEvent_t* ev = nullptr;
-        if (h->timing_runs < h->timing_max_runs) ev = &h->events[((size_t)h->timing_runs * L + l) * 4];
-        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, (hipStream_t)stream, ev);
-        if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
+    const bool timing = h->timing_runs < h->timing_max_runs;
+    if (timing || (h->cfg.flags & MOE_F_DIRECT_LAUNCH)) {
+        moe_status st = enqueue_run(h, x, T, o, (hipStream_t)stream, timing);
+        if (st == MOE_OK && timing) ++h->timing_runs;
+        return st;
     }
-    if (h->timing_runs < h->timing_max_runs) ++h->timing_runs;
+    // replay the captured launch sequence of this exact call (capture it on first use)
+    for (auto& g : h->graphs) {
+        if (g.x == x && g.T == T && memcmp(&g.out, &o, sizeof o) == 0) {
+            if (hipGraphLaunch(g.exec, (hipStream_t)stream) != hipSuccess)
+                return fail(MOE_ERR_HIP, "hipGraphLaunch failed");
+            return MOE_OK;
+        }
+    }
+    if (h->graphs.size() >= 16) free_graphs(h);
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
+        return fail(MOE_ERR_HIP, "hipStreamBeginCapture failed");
+    moe_status st = enqueue_run(h, x, T, o, h->capture_stream, false);
+    hipError_t e = hipStreamEndCapture(h->capture_stream, &graph);
+    if (st != MOE_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    h->graphs.push_back({x, T, o, exec});
+    if (hipGraphLaunch(exec, (hipStream_t)stream) != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphLaunch failed");
     return MOE_OK;
 }
 
@@ -304,8 +367,8 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
         return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
     const Shape& sh = h->sh;
     memset(info->variant, 0, sizeof info->variant);
-    snprintf(info->variant, sizeof info->variant, "gfx950-3k-router%d-gu%dw-dn%dx%d", moe::kRouterWaves,
-             sh.H / moe::kGuSlice, sh.down_ksub(), sh.down_iters());
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s", sh.gw(), sh.bpl(), sh.ksub(),
+             sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph");
     info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
     info->workspace_bytes = h->ws_bytes;
     const uint64_t expert = sh.w13_bytes_per_expert() + sh.w13s_bytes_per_expert() + sh.w2_bytes_per_expert() +

@@ -1,17 +1,18 @@
 // moe_kernels.hip -- gfx950 kernels of the W4A8 sparse-MoE decode step.
 //
-// One layer is three launches on the caller's stream:
-//   router_kernel  bf16 router GEMV, split over (K slice, 64-row tile) workgroups; the last
-//                  workgroup to finish (atomic ticket) sums the partial logits, takes the top-k
-//                  per token in one wavefront (lower index first on ties), computes the softmax
-//                  weights and writes the list of distinct experts ("slots") of this call.
-//   gateup_kernel  one workgroup per (32-row h tile, slot): streams the MXFP4 gate and up rows,
-//                  dequantises E2M1 codes to f16 pairs in VGPRs, dot2 with the FP8-quantised
-//                  activation held in LDS, and writes h = SiLU(gate) * up plus the tile's max |h|.
-//   down_kernel    one workgroup per output-row tile, all experts: requantises every (slot,
-//                  token) h vector to FP8 in LDS, streams the MXFP4 down rows of every slot and
-//                  sums the routing-weighted results in a fixed order (no float atomics), then
-//                  writes y and the updated bf16 residual.
+// One layer is three launches (replayed from a HIP graph by the library):
+//   k1_router_shared  router GEMV, one wave per expert row (bf16 x bf16 products, fp32 FMA), and the
+//                     shared expert's gate/up tiles (it needs no routing decision).
+//   k2_gateup         every workgroup redoes the top-k from the logits (one wave per token, lower
+//                     index first on ties), builds the list of distinct routed experts, then streams
+//                     its 32-row MXFP4 gate/up tile: E2M1 pairs are converted to f16 in VGPRs and
+//                     dot2-multiplied with the FP8-quantised activation held in LDS; writes
+//                     h = SiLU(gate) * up and the tile's max |h|.  Extra workgroups compute the
+//                     shared expert's down projection.
+//   k3_down           one workgroup per 8-row output tile and every routed expert: requantises each
+//                     (token, expert) h vector to FP8 in LDS, streams the MXFP4 down rows and sums
+//                     the routing-weighted results and the shared expert's in a fixed order (no
+//                     float atomics); writes y and the bf16 residual.
 //
 // What is computed follows the MoE decode step described on the pages (tanhow.com, "NVIDIA 在单台
 // DGX Spark 上叠加三项优化..." sections "Ling 3.0 是什么" (8 of 512 routed experts + 1 shared) and
@@ -27,12 +28,14 @@
 namespace moe {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------------------
 // small helpers
 // ------------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float((b & 0xffffu) << 16); }
 
 // fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -61,10 +64,13 @@ __device__ __forceinline__ half2_t e2m1x2_to_f16x2(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
-// Streaming (non-temporal) 128-bit and 64-bit loads of weights that are read once per pass.
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Streaming (non-temporal) loads of weights that are read once per pass.
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
     const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -74,11 +80,21 @@ __device__ __forceinline__ uint2 ld_nt(const uint2* p) {
     return make_uint2(v.x, v.y);
 }
 
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
+// Scale bytes of one lane: BPL = 8 -> 8 bytes, BPL = 4 -> 4 bytes.
+template <int BPL>
+struct ScaleBytes;
+template <>
+struct ScaleBytes<8> {
+    uint2 v;
+    __device__ void load(const uint8_t* p) { v = ld_nt((const uint2*)p); }
+    __device__ uint32_t get(int i) const { return (i < 4 ? v.x >> (8 * i) : v.y >> (8 * (i - 4))) & 0xffu; }
+};
+template <>
+struct ScaleBytes<4> {
+    uint32_t v;
+    __device__ void load(const uint8_t* p) { v = __builtin_nontemporal_load((const uint32_t*)p); }
+    __device__ uint32_t get(int i) const { return (v >> (8 * i)) & 0xffu; }
+};
 
 // Dot product of one 16-byte MX block (32 E2M1 codes) with 32 f16 activations per token (xp[j]
 // points at the block's 16 half2 pairs in LDS), accumulated into p in fp32.  Every product is
@@ -105,487 +121,759 @@ __device__ __forceinline__ void block_dot(const uint4& w, const half2_t* const (
     }
 }
 
-__device__ __forceinline__ float wave_max(float v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, width));
+// Lane exchange without LDS: stage S pairs every lane with one partner (0: lane^1, 1: lane^2,
+// 2: mirror within 8 lanes, 3: mirror within 16 lanes, 4: lane^16, 5: lane^32).  Applying an
+// associative, commutative op with stages 0..n-1 reduces over groups of 2^n lanes.
+template <int S>
+__device__ __forceinline__ uint32_t xchg(uint32_t v) {
+    if constexpr (S == 0) return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+    else if constexpr (S == 1) return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    else if constexpr (S == 3) return __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, true);  // row_mirror
+    else if constexpr (S == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+    }
+}
+template <int S>
+__device__ __forceinline__ float xchg(float v) { return __uint_as_float(xchg<S>(__float_as_uint(v))); }
+template <int S>
+__device__ __forceinline__ double xchg(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = ((uint64_t)xchg<S>((uint32_t)(u >> 32)) << 32) | xchg<S>((uint32_t)u);
+    return __builtin_bit_cast(double, r);
+}
+template <int S>
+__device__ __forceinline__ uint64_t xchg(uint64_t u) {
+    return ((uint64_t)xchg<S>((uint32_t)(u >> 32)) << 32) | xchg<S>((uint32_t)u);
+}
+
+// max over groups of 16 lanes / over the wave; sums over the wave (every lane gets the result)
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, xchg<0>(v));
+    v = fmaxf(v, xchg<1>(v));
+    v = fmaxf(v, xchg<2>(v));
+    return fmaxf(v, xchg<3>(v));
+}
+__device__ __forceinline__ float max64(float v) {
+    v = max16(v);
+    v = fmaxf(v, xchg<4>(v));
+    return fmaxf(v, xchg<5>(v));
+}
+__device__ __forceinline__ float sum64(float v) {
+    v += xchg<0>(v);
+    v += xchg<1>(v);
+    v += xchg<2>(v);
+    v += xchg<3>(v);
+    v += xchg<4>(v);
+    return v + xchg<5>(v);
+}
+__device__ __forceinline__ double sum64(double v) {
+    v += xchg<0>(v);
+    v += xchg<1>(v);
+    v += xchg<2>(v);
+    v += xchg<3>(v);
+    v += xchg<4>(v);
+    return v + xchg<5>(v);
+}
+// sum over the KSUB consecutive lanes of a row group (KSUB = 1, 2, 4 or 8)
+template <int KSUB>
+__device__ __forceinline__ float sum_ksub(float v) {
+    if constexpr (KSUB >= 2) v += xchg<0>(v);
+    if constexpr (KSUB >= 4) v += xchg<1>(v);
+    if constexpr (KSUB >= 8) v += xchg<2>(v);
     return v;
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+template <int T>
+__device__ __forceinline__ float pick(const float (&v)[T], int t) {
+    float r = v[0];
+#pragma unroll
+    for (int i = 1; i < T; ++i)
+        if (t == i) r = v[i];
+    return r;
 }
 
 // ------------------------------------------------------------------------------------------------
 // repack kernels (canonical row-major -> lane tiles; pure permutations of 16-byte units / bytes)
 // ------------------------------------------------------------------------------------------------
 
-__global__ void repack_router(const uint16_t* __restrict__ src, uint4* __restrict__ dst, int E, int H, int RT) {
-    const int NU = H / kRouterUnitElems;
-    const uint64_t total = (uint64_t)RT * NU * kWave;
+__device__ __forceinline__ int gu_row(int lane, int tile, int I) {
+    const int r = lane >> 1;
+    return r < kGuOut ? tile * kGuOut + r : I + tile * kGuOut + r - kGuOut;
+}
+
+__global__ void repack_w13(const uint4* __restrict__ src, uint4* __restrict__ dst, int nexp, int I, int H, int bpl) {
+    const int NB = H / kBlock, GW = NB / (2 * bpl), tiles = I / kGuOut;
+    const uint64_t total = (uint64_t)nexp * tiles * GW * bpl * kWave;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
          u += (uint64_t)gridDim.x * blockDim.x) {
         const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int unit = (int)(r1 % NU);
-        const int rt = (int)(r1 / NU);
-        const int row = rt * kRouterRows + lane;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < E) v = *(const uint4*)(src + (uint64_t)row * H + (uint64_t)unit * kRouterUnitElems);
-        dst[u] = v;
+        uint64_t r = u / kWave;
+        const int step = (int)(r % bpl);
+        r /= bpl;
+        const int w = (int)(r % GW);
+        r /= GW;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        const int c = (w * bpl + step) * 2 + (lane & 1);
+        dst[u] = src[(e * 2 * I + gu_row(lane, tile, I)) * NB + c];
     }
 }
 
-__global__ void repack_w13(const uint4* __restrict__ src, uint4* __restrict__ dst, int nexp, int I, int H) {
-    const int NB = H / kBlock, tiles = I / kGuHalf;
-    const uint64_t total = (uint64_t)nexp * tiles * NB * kWave;
+__global__ void repack_w13s(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nexp, int I, int H,
+                            int bpl) {
+    const int NB = H / kBlock, GW = NB / (2 * bpl), tiles = I / kGuOut;
+    const uint64_t total = (uint64_t)nexp * tiles * GW * kWave * bpl;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
          u += (uint64_t)gridDim.x * blockDim.x) {
-        const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int c = (int)(r1 % NB);
-        const uint64_t r2 = r1 / NB;
-        const int tile = (int)(r2 % tiles);
-        const uint64_t e = r2 / tiles;
-        const int row = lane < kGuHalf ? tile * kGuHalf + lane : I + tile * kGuHalf + lane - kGuHalf;
-        dst[u] = src[(e * 2 * I + row) * NB + c];
-    }
-}
-
-__global__ void repack_w13s(const uint8_t* __restrict__ src, uint2* __restrict__ dst, int nexp, int I, int H) {
-    const int NB = H / kBlock, NG = NB / kGuBlocksPerWave, tiles = I / kGuHalf;
-    const uint64_t total = (uint64_t)nexp * tiles * NG * kWave;
-    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
-         u += (uint64_t)gridDim.x * blockDim.x) {
-        const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int g = (int)(r1 % NG);
-        const uint64_t r2 = r1 / NG;
-        const int tile = (int)(r2 % tiles);
-        const uint64_t e = r2 / tiles;
-        const int row = lane < kGuHalf ? tile * kGuHalf + lane : I + tile * kGuHalf + lane - kGuHalf;
-        dst[u] = *(const uint2*)(src + (e * 2 * I + row) * NB + g * kGuBlocksPerWave);
+        const int step = (int)(u % bpl);
+        uint64_t r = u / bpl;
+        const int lane = (int)(r % kWave);
+        r /= kWave;
+        const int w = (int)(r % GW);
+        r /= GW;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        const int c = (w * bpl + step) * 2 + (lane & 1);
+        dst[u] = src[(e * 2 * I + gu_row(lane, tile, I)) * NB + c];
     }
 }
 
 __global__ void repack_w2(const uint4* __restrict__ src, uint4* __restrict__ dst, int nexp, int H, int I, int ksub) {
-    const int NB = I / kBlock, R = kWave / ksub, iters = NB / ksub, tiles = H / R;
+    const int NI = I / kBlock, R = kWave / ksub, iters = NI / ksub, tiles = H / R;
     const uint64_t total = (uint64_t)nexp * tiles * iters * kWave;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
          u += (uint64_t)gridDim.x * blockDim.x) {
         const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int it = (int)(r1 % iters);
-        const uint64_t r2 = r1 / iters;
-        const int tile = (int)(r2 % tiles);
-        const uint64_t e = r2 / tiles;
-        const int row = tile * R + lane / ksub;
-        const int c = it * ksub + lane % ksub;
-        dst[u] = src[(e * H + row) * NB + c];
+        uint64_t r = u / kWave;
+        const int it = (int)(r % iters);
+        r /= iters;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        dst[u] = src[(e * H + tile * R + lane / ksub) * NI + it * ksub + lane % ksub];
     }
 }
 
-__global__ void repack_w2s(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nexp, int H, int I, int ksub) {
-    const int NB = I / kBlock, R = kWave / ksub, iters = NB / ksub, tiles = H / R;
+__global__ void repack_w2s(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nexp, int H, int I,
+                           int ksub) {
+    const int NI = I / kBlock, R = kWave / ksub, iters = NI / ksub, tiles = H / R;
     const uint64_t total = (uint64_t)nexp * tiles * iters * kWave;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
          u += (uint64_t)gridDim.x * blockDim.x) {
         const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int it = (int)(r1 % iters);
-        const uint64_t r2 = r1 / iters;
-        const int tile = (int)(r2 % tiles);
-        const uint64_t e = r2 / tiles;
-        const int row = tile * R + lane / ksub;
-        const int c = it * ksub + lane % ksub;
-        dst[u] = src[(e * H + row) * NB + c];
+        uint64_t r = u / kWave;
+        const int it = (int)(r % iters);
+        r /= iters;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        dst[u] = src[(e * H + tile * R + lane / ksub) * NI + it * ksub + lane % ksub];
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// router GEMV + top-k + softmax + slot list
+// shared pieces: MoE input, FP8 quantisation of the input, gate/up tile
 // ------------------------------------------------------------------------------------------------
 
-struct RouterArgs {
-    const uint4* w;         // repacked router of this layer
-    const uint16_t* x;      // [T][H] residual x_l (or the MoE input when normalize == 0)
-    uint16_t* xin;          // [T][H] MoE input, written by the rt == 0 workgroups
-    uint16_t* trace;        // [T][H] copy of x, or null
-    float* partial;         // [G][T][RT*64]
-    unsigned* ticket;       // zero between calls
-    SlotTable* slots;
-    int32_t* ids_out;       // [T][k] or null
-    float* w_out;           // [T][k] or null
-    int H, E, k, S, normalize;
-};
-
+// x_in = x, or bf16(fl32(x * r)) with r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64; stored as
+// bf16 bits in LDS xb[T][H].  One 16-byte load per thread and token (H/8 <= threads), all issued
+// before any use.
 template <int T>
-__device__ void router_finish(const RouterArgs& a, int G, int RT) {
-    __shared__ float lg[T][512];
-    __shared__ int s_ids[T][kMaxTopK];
-    __shared__ float s_lv[T][kMaxTopK];
-    __shared__ float s_w[T][kMaxTopK];
-    __shared__ short slot_of[512];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int E = a.E, k = a.k, Ep = RT * kRouterRows;
-    for (int i = tid; i < T * E; i += blockDim.x) {
-        const int t = i / E, e = i - t * E;
-        float s = 0.0f;
-        for (int g = 0; g < G; ++g) s += __builtin_nontemporal_load(a.partial + ((size_t)g * T + t) * Ep + e);
-        lg[t][e] = s;
-    }
-    for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
-    __syncthreads();
-    if (wv < T) {
-        const int t = wv;
-        float v[8];
-        unsigned taken = 0;
+__device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize, uint16_t* xb, double* red_d) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
+    const bool has = tid < NC;
+    uint4 v[T];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int e = lane + 64 * j;
-            v[j] = e < E ? lg[t][e] : -INFINITY;
-        }
-        for (int r = 0; r < k; ++r) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int e = lane + 64 * j;
-                if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
-                    bv = v[j];
-                    bi = e;
-                }
-            }
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            if (lane == 0) {
-                s_ids[t][r] = bi;
-                s_lv[t][r] = bv;
-            }
-        }
-        if (lane == 0) {
-            const float m = s_lv[t][0];
-            float z[kMaxTopK], Z = 0.0f;
-            for (int r = 0; r < k; ++r) {
-                z[r] = expf(s_lv[t][r] - m);
-                Z += z[r];
-            }
-            for (int r = 0; r < k; ++r) {
-                const float w = z[r] / Z;
-                s_w[t][r] = w;
-                if (a.ids_out) a.ids_out[t * k + r] = s_ids[t][r];
-                if (a.w_out) a.w_out[t * k + r] = w;
-            }
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        SlotTable* st = a.slots;
-        int n = 0;
-        for (int t = 0; t < T; ++t) {
-            for (int r = 0; r < k; ++r) {
-                const int e = s_ids[t][r];
-                int s = slot_of[e];
-                if (s < 0) {
-                    s = n++;
-                    slot_of[e] = (short)s;
-                    st->expert[s] = e;
-                    st->ntok[s] = 0;
-                }
-                const int j = st->ntok[s]++;
-                st->tok[s][j] = t;
-                st->w[s][j] = s_w[t][r];
-            }
-        }
-        if (a.S) {
-            const int s = n++;
-            st->expert[s] = E;
-            st->ntok[s] = T;
-            for (int t = 0; t < T; ++t) {
-                st->tok[s][t] = t;
-                st->w[s][t] = 1.0f;
-            }
-        }
-        st->n = n;
-        *a.ticket = 0u;
-    }
-}
-
-template <int T>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-    __shared__ float xs[T][kRouterSlice];
-    __shared__ double red_d[kRouterWaves][T];
-    __shared__ float redf[kRouterWaves][T][kWave];
-    __shared__ int is_last;
-    const int g = blockIdx.x, rt = blockIdx.y, G = gridDim.x, RT = gridDim.y;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int H = a.H, NU = H / kRouterUnitElems;
-
-    // 1. weight loads for this wave's 8 units (64 K elements) of the 64-row tile
-    uint4 wr[kRouterUnitsPerWave];
-    {
-        const uint4* p = a.w + ((size_t)rt * NU + (size_t)g * (kRouterSlice / kRouterUnitElems) +
-                                wv * kRouterUnitsPerWave) * kWave + lane;
-#pragma unroll
-        for (int i = 0; i < kRouterUnitsPerWave; ++i) wr[i] = ld_nt(p + i * kWave);
-    }
-
-    // 2. MoE input of this workgroup's K slice: x itself, or bf16(fl32(x * r)) with
-    //    r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64
-    const int c = g * kRouterSlice + tid;
-    double r[T];
-    if (a.normalize) {
+    for (int t = 0; t < T; ++t)
+        if (has) v[t] = *(const uint4*)(x + (size_t)t * H + tid * 8);
+    if (normalize) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             double ss = 0.0;
-            for (int i = tid; i < H; i += blockDim.x) {
-                const double v = (double)bf16_to_f32(a.x[(size_t)t * H + i]);
-                ss += v * v;
+            if (has) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const double a = (double)bf16_to_f32(comp(v[t], q)), b = (double)bf16_to_f32(comp(v[t], q) >> 16);
+                    ss += a * a + b * b;
+                }
             }
-            ss = wave_sum_d(ss);
-            if (lane == 0) red_d[wv][t] = ss;
+            ss = sum64(ss);
+            if (lane == 0) red_d[wv * T + t] = ss;
         }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             double ss = 0.0;
-            for (int w = 0; w < kRouterWaves; ++w) ss += red_d[w][t];
-            r[t] = 1.0 / sqrt(ss / (double)H + 1e-6);
-        }
-    }
+            for (int w = 0; w < NW; ++w) ss += red_d[w * T + t];
+            const double r = 1.0 / sqrt(ss / (double)H + 1e-6);
+            if (has) {
+                uint32_t o[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const uint16_t xb = a.x[(size_t)t * H + c];
-        uint16_t ib = xb;
-        if (a.normalize) ib = f32_to_bf16((float)((double)bf16_to_f32(xb) * r[t]));
-        xs[t][tid] = bf16_to_f32(ib);
-        if (rt == 0) {
-            a.xin[(size_t)t * H + c] = ib;
-            if (a.trace) a.trace[(size_t)t * H + c] = xb;
-        }
-    }
-    __syncthreads();
-
-    // 3. partial logits: fp32 FMA of exact bf16 x bf16 products
-    float acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kRouterUnitsPerWave; ++i) {
-        const int k0 = wv * (kRouterUnitsPerWave * kRouterUnitElems) + i * kRouterUnitElems;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t d = comp(wr[i], q);
-            const float wlo = __uint_as_float(d << 16), whi = __uint_as_float(d & 0xffff0000u);
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                acc[t] = fmaf(wlo, xs[t][k0 + 2 * q], acc[t]);
-                acc[t] = fmaf(whi, xs[t][k0 + 2 * q + 1], acc[t]);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t d = comp(v[t], q);
+                    const uint32_t lo = f32_to_bf16((float)((double)bf16_to_f32(d) * r));
+                    const uint32_t hi = f32_to_bf16((float)((double)bf16_to_f32(d >> 16) * r));
+                    o[q] = lo | (hi << 16);
+                }
+                v[t] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) redf[wv][t][lane] = acc[t];
+    for (int t = 0; t < T; ++t)
+        if (has) *(uint4*)(xb + t * H + tid * 8) = v[t];
     __syncthreads();
-    if (tid < T * kWave) {
-        const int t = tid >> 6, l = tid & 63;
-        float s = 0.0f;
-        for (int w = 0; w < kRouterWaves; ++w) s += redf[w][t][l];
-        a.partial[((size_t)g * T + t) * (RT * kRouterRows) + rt * kRouterRows + l] = s;
-    }
-
-    // 4. the last workgroup to arrive finishes the routing
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(a.ticket, 1u) == (unsigned)(G * RT - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    router_finish<T>(a, G, RT);
 }
 
-// ------------------------------------------------------------------------------------------------
-// gate/up GEMV with fused SiLU(gate) * up
-// ------------------------------------------------------------------------------------------------
-
-struct GateUpArgs {
-    const uint4* w13;       // repacked codes of this layer
-    const uint2* w13s;      // repacked scales
-    const uint16_t* xin;    // [T][H] MoE input (bf16)
-    const SlotTable* slots;
-    float* h;               // [kMaxSlots][kMaxTokens][I]
-    float* hamax;           // [kMaxSlots][kMaxTokens][I/32]
-    float* x_scale_out;     // [T] or null
-    uint8_t* x_codes_out;   // [T][H] or null
-    int H, I;
-};
-
+// Per-token FP8 quantisation of the bf16 input xb[T][H] (LDS): s = max|x| / 448 (1 when x = 0),
+// codes = RNE(x / s).  The exact f16 values of the codes go to xh[T][H/2] (LDS); when codes_out is
+// set the codes and scales are also stored to global memory.
 template <int T>
-__global__ __launch_bounds__(640) void gateup_kernel(GateUpArgs a) {
-    extern __shared__ uint4 smem_gu[];
-    half2_t* xh = (half2_t*)smem_gu;  // [T][H/2]
-    __shared__ float wmax[16][T];
-    __shared__ float red[16][T][kWave];
-    const int tile = blockIdx.x, slot = blockIdx.y;
-    const SlotTable* st = a.slots;
-    const int n = st->n;
-    if (slot >= n) return;
-    const int H = a.H, I = a.I, NB = H / kBlock, tiles = I / kGuHalf, Hh = H / 2;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    const int e = st->expert[slot], ntok = st->ntok[slot];
-    int tok[T];
-#pragma unroll
-    for (int j = 0; j < T; ++j) tok[j] = j < ntok ? st->tok[slot][j] : 0;
-
-    // 1. weight loads: 8 MX blocks of this lane's row
-    uint4 wr[kGuBlocksPerWave];
-    const size_t tbase = (size_t)e * tiles + tile;
-    {
-        const uint4* p = a.w13 + (tbase * NB + (size_t)wv * kGuBlocksPerWave) * kWave + lane;
-#pragma unroll
-        for (int i = 0; i < kGuBlocksPerWave; ++i) wr[i] = ld_nt(p + i * kWave);
-    }
-    const uint2 sc = ld_nt(a.w13s + (tbase * (NB / kGuBlocksPerWave) + wv) * kWave + lane);
-
-    // 2. per-token FP8 quantisation of the input into LDS (as exact f16 values)
+__device__ void quantize_input(const uint16_t* xb, int H, half2_t* xh, float* wmax, float* sx_lds,
+                               uint8_t* codes_out, float* scale_out, uint8_t* codes_dbg = nullptr,
+                               float* scale_dbg = nullptr) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
+    const bool has = tid < NC;
+    uint4 v[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         float m = 0.0f;
-        for (int i = tid; i < H; i += blockDim.x) m = fmaxf(m, fabsf(bf16_to_f32(a.xin[(size_t)t * H + i])));
-        m = wave_max(m, 64);
-        if (lane == 0) wmax[wv][t] = m;
+        if (has) {
+            v[t] = *(const uint4*)(xb + t * H + tid * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(comp(v[t], q))), fabsf(bf16_to_f32(comp(v[t], q) >> 16))));
+        }
+        m = max64(m);
+        if (lane == 0) wmax[wv * T + t] = m;
     }
     __syncthreads();
-    float sx[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         float m = 0.0f;
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, wmax[w][t]);
-        sx[t] = m > 0.0f ? m / 448.0f : 1.0f;
-    }
-    const bool dump = a.x_codes_out && tile == 0 && slot == 0;
-    for (int p = tid; p < Hh; p += blockDim.x) {
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, wmax[w * T + t]);
+        const float sx = m > 0.0f ? m / 448.0f : 1.0f;
+        if (tid == 0) {
+            sx_lds[t] = sx;
+            if (scale_out) scale_out[t] = sx;
+            if (scale_dbg) scale_dbg[t] = sx;
+        }
+        if (has) {
+            uint32_t c[4];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint32_t xx = *(const uint32_t*)(a.xin + (size_t)t * H + 2 * p);
-            const uint32_t q = e4m3_pack2(bf16_to_f32((uint16_t)(xx & 0xffffu)) / sx[t],
-                                          bf16_to_f32((uint16_t)(xx >> 16)) / sx[t]);
-            xh[t * Hh + p] = e4m3x2_to_f16x2(q);
-            if (dump) *(uint16_t*)(a.x_codes_out + (size_t)t * H + 2 * p) = (uint16_t)q;
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t d = comp(v[t], q);
+                c[q] = e4m3_pack2(bf16_to_f32(d) / sx, bf16_to_f32(d >> 16) / sx);
+                xh[t * (H / 2) + tid * 4 + q] = e4m3x2_to_f16x2(c[q]);
+            }
+            const uint2 cw = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+            if (codes_out) *(uint2*)(codes_out + (size_t)t * H + tid * 8) = cw;
+            if (codes_dbg) *(uint2*)(codes_dbg + (size_t)t * H + tid * 8) = cw;
         }
     }
-    if (a.x_scale_out && tile == 0 && slot == 0 && tid < T) a.x_scale_out[tid] = sx[tid];
     __syncthreads();
+}
 
-    // 3. block dot products: 8 blocks of 32 codes per lane, for each routed token
+template <int BPL>
+struct GuLoads {
+    uint4 w[BPL];
+    ScaleBytes<BPL> s;
+    // expert e, tile `tile` of `tiles`, this wave's BPL steps
+    __device__ void issue(const uint4* w13, const uint8_t* w13s, int e, int tile, int tiles, int GW) {
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const size_t base = (((size_t)e * tiles + tile) * GW + wv);
+        const uint4* p = w13 + base * BPL * kWave + lane;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) w[i] = ld_nt(p + i * kWave);
+        s.load(w13s + (base * kWave + lane) * BPL);
+    }
+};
+
+// The gate/up tile of one expert: 16 gate + 16 up rows over all H, for the nt tokens tok[j] (their
+// h goes to pair pair[j]); sx: LDS scales per token.  red: LDS [kMaxWaves][T][32].
+template <int T, int BPL>
+__device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, const float* sx, int nt,
+                            const int (&tok)[T], const int (&pair)[T], int tile, int I, float* h, float* hamax,
+                            float* red) {
+    const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6, Hh = H / 2;
+    const int ks = lane & 1;
     float acc[T];
 #pragma unroll
     for (int j = 0; j < T; ++j) acc[j] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGuBlocksPerWave; ++i) {
-        const float scale = e8m0_to_f32(i < 4 ? sc.x >> (8 * i) : sc.y >> (8 * (i - 4)));
-        const int pbase = (wv * kGuBlocksPerWave + i) * (kBlock / 2);
+    for (int i = 0; i < BPL; ++i) {
+        const float scale = e8m0_to_f32(L.s.get(i));
+        const int pbase = ((wv * BPL + i) * 2 + ks) * (kBlock / 2);
         const half2_t* xp[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) xp[j] = xh + tok[j] * Hh + pbase;
         float p[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) p[j] = 0.0f;
-        block_dot<T>(wr[i], xp, p, ntok);
+        block_dot<T>(L.w[i], xp, p, nt);
 #pragma unroll
         for (int j = 0; j < T; ++j) acc[j] = fmaf(p[j], scale, acc[j]);
+        __builtin_amdgcn_sched_barrier(0);  // bound the live activation registers to one block
     }
 #pragma unroll
-    for (int j = 0; j < T; ++j)
-        if (j < ntok) red[wv][j][lane] = acc[j];
+    for (int j = 0; j < T; ++j) {
+        acc[j] += xchg<0>(acc[j]);
+        if (j < nt && ks == 0) red[(wv * T + j) * kGuRows + (lane >> 1)] = acc[j];
+    }
     __syncthreads();
-
-    // 4. sum the K slices, h = SiLU(g) * u, tile max |h| (one half-wave per token and pass)
-    for (int base = 0; base < kGuHalf * ntok; base += blockDim.x) {
-        const int idx = base + tid, j = idx >> 5, r = idx & 31;
-        const bool act = idx < kGuHalf * ntok;
+    const int tiles = I / kGuOut;
+    for (int base = 0; base < kGuOut * nt; base += nth) {
+        const int idx = base + tid, j = idx >> 4, r = idx & 15;
+        const bool act = idx < kGuOut * nt;
         float hv = 0.0f;
+        int pj = 0;
         if (act) {
             float g = 0.0f, u = 0.0f;
             for (int w = 0; w < NW; ++w) {
-                g += red[w][j][r];
-                u += red[w][j][kGuHalf + r];
+                g += red[(w * T + j) * kGuRows + r];
+                u += red[(w * T + j) * kGuRows + kGuOut + r];
             }
-            float s = sx[0];
+            int tk = tok[0];
+            pj = pair[0];
 #pragma unroll
-            for (int t = 1; t < T; ++t)
-                if (tok[j] == t) s = sx[t];
+            for (int q = 1; q < T; ++q)
+                if (j == q) {
+                    tk = tok[q];
+                    pj = pair[q];
+                }
+            const float s = sx[tk];
             g *= s;
             u *= s;
             hv = g / (1.0f + expf(-g)) * u;
-            a.h[((size_t)slot * kMaxTokens + j) * I + tile * kGuHalf + r] = hv;
+            h[(size_t)pj * I + tile * kGuOut + r] = hv;
         }
-        const float m = wave_max(fabsf(hv), 32);
-        if (act && r == 0) a.hamax[((size_t)slot * kMaxTokens + j) * (I / kGuHalf) + tile] = m;
+        const float m = max16(fabsf(hv));
+        if (act && r == 0) hamax[(size_t)pj * tiles + tile] = m;
+    }
+}
+
+// FP8 requantisation scale of each listed h vector: s_h = max|h| / 448 (1 when h = 0), from the
+// per-tile maxima hamax[pair][tiles].  pairs[i] < 0 entries are skipped.  out: LDS floats;
+// scratch_u: LDS uints (one per listed vector).  Ends with a barrier.
+__device__ void requant_scales(const float* hamax, int tiles, const int* pairs, int n, float* out, uint32_t* scratch_u) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int i = tid; i < n; i += nth) scratch_u[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n * tiles; i += nth) {
+        const int p = i / tiles, b = i - p * tiles;
+        if (pairs[p] >= 0) atomicMax(&scratch_u[p], __float_as_uint(hamax[(size_t)pairs[p] * tiles + b]));
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += nth) {
+        const float m = __uint_as_float(scratch_u[i]);
+        out[i] = m > 0.0f ? m / 448.0f : 1.0f;
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------------
+// k1: router rows + shared expert gate/up tiles (+ the FP8 codes of the input, stored once)
+// ------------------------------------------------------------------------------------------------
+
+struct K1Args {
+    const uint16_t* router;  // [E][H]
+    const uint4* w13;        // repacked codes (expert E = shared)
+    const uint8_t* w13s;
+    const uint16_t* x;       // [T][H] residual x_l (or the MoE input)
+    uint16_t* trace;         // [T][H] copy of x, or null (workgroup 0)
+    float* logits;           // [T][E]
+    uint8_t* xq;             // [T][H] FP8 codes of the MoE input (one workgroup stores them)
+    float* xs;               // [T] their scales
+    float* x_scale_out;      // [T] or null
+    uint8_t* x_codes_out;    // [T][H] or null
+    float* h;                // [pairs][I]
+    float* hamax;            // [pairs][I/16]
+    int H, E, k, S, I, normalize, n_router_wg;
+    int ntok;                // = T, passed at run time so the shared tile's token loop stays a loop
+};
+
+template <int T, int BPL>
+__global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
+    extern __shared__ uint4 smem1[];
+    uint16_t* xb = (uint16_t*)smem1;                      // [T][H] bf16 MoE input
+    half2_t* xh = (half2_t*)(xb + T * a.H);               // [T][H/2]
+    __shared__ double red_d[kMaxWaves * T];
+    __shared__ float wmax[kMaxWaves * T];
+    __shared__ float red[kMaxWaves * T * kGuRows];
+    __shared__ float sx[T];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    const int H = a.H;
+    const bool is_router = (int)blockIdx.x < a.n_router_wg;
+    // the workgroup that publishes the input's FP8 codes: shared tile 0, or router 0 without a shared expert
+    const bool publish = a.S ? (int)blockIdx.x == a.n_router_wg : blockIdx.x == 0;
+
+    if (is_router) {
+        // one expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row
+        const int e = blockIdx.x * NW + wv;
+        const int NU = H / 8;
+        uint4 wr[kMaxWaves];
+        if (e < a.E) {
+            const uint4* p = (const uint4*)(a.router + (size_t)e * H);
+#pragma unroll
+            for (int j = 0; j < kMaxWaves; ++j)
+                if (lane + 64 * j < NU) wr[j] = ld_nt(p + lane + 64 * j);
+        }
+        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
+        if (blockIdx.x == 0 && a.trace) {
+            for (int i = tid; i < T * H / 8; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
+        }
+        if (publish) quantize_input<T>(xb, H, xh, wmax, sx, a.xq, a.xs, a.x_codes_out, a.x_scale_out);
+        if (e < a.E) {
+            float acc[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kMaxWaves; ++j) {
+                const int u = lane + 64 * j;
+                if (u < NU) {
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const uint4 xv = *(const uint4*)(xb + t * H + u * 8);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t d = comp(wr[j], q), xx = comp(xv, q);
+                            acc[t] = fmaf(__uint_as_float(d << 16), __uint_as_float(xx << 16), acc[t]);
+                            acc[t] = fmaf(__uint_as_float(d & 0xffff0000u), __uint_as_float(xx & 0xffff0000u), acc[t]);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the LDS reads of later units from being hoisted
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float v = sum64(acc[t]);
+                if (lane == 0) a.logits[t * a.E + e] = v;
+            }
+        }
+    } else {
+        // shared expert (index E), gate/up tile, every token
+        const int tile = blockIdx.x - a.n_router_wg, tiles = a.I / kGuOut;
+        GuLoads<BPL> L;
+        L.issue(a.w13, a.w13s, a.E, tile, tiles, NW);
+        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
+        quantize_input<T>(xb, H, xh, wmax, sx, publish ? a.xq : nullptr, publish ? a.xs : nullptr,
+                          publish ? a.x_codes_out : nullptr, publish ? a.x_scale_out : nullptr);
+        int tok[T], pair[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            tok[j] = j;
+            pair[j] = j * (a.k + a.S) + a.k;
+        }
+        gateup_tile<T, BPL>(L, xh, H, sx, a.ntok, tok, pair, tile, a.I, a.h, a.hamax, red);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// down GEMV + routing-weighted combine + residual
+// k2: top-k + routed gate/up tiles + shared expert down rows
 // ------------------------------------------------------------------------------------------------
 
-struct DownArgs {
-    const uint4* w2;        // repacked codes of this layer
-    const uint8_t* w2s;     // repacked scales
+struct K2Args {
+    const float* logits;     // [T][E]
+    const uint8_t* xq;       // [T][H] FP8 codes of the MoE input
+    const float* xs;         // [T] their scales
+    const uint4* w13;
+    const uint8_t* w13s;
+    const uint4* w2;
+    const uint8_t* w2s;
+    SlotTable* slots_out;    // workgroup 0
+    int32_t* ids_out;        // [T][k] or null (workgroup 0)
+    float* w_out;            // [T][k] or null (workgroup 0)
+    float* h;                // [pairs][I]
+    float* hamax;            // [pairs][I/16]
+    float* dshared;          // [T][H]
+    int H, E, k, S, I, n_gu_wg;
+    int ntok;                // = T, at run time (keeps the shared expert's token loop a loop)
+};
+
+// Order-preserving 64-bit key of (logit, expert): larger logit first, then lower index first.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t max64u(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Top-k of every token (one wave per token: each lane keeps its 8 keys, k rounds of a wave-wide
+// maximum through lane exchanges, the winner's key is cleared), softmax weights over the selected
+// logits, and the list of distinct routed experts, all into LDS; identical in every workgroup.
+template <int T>
+__device__ void route(const K2Args& a, SlotTable* st, int (*ids)[kMaxTopK], float (*wts)[kMaxTopK]) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, E = a.E, k = a.k;
+    for (int t = wv; t < T; t += NW) {
+        uint64_t key[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = lane + 64 * j;
+            key[j] = e < E ? topk_key(a.logits[t * E + e], e) : 0ull;
+        }
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = key[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) best = max64u(best, key[j]);
+            best = max64u(best, xchg<0>(best));
+            best = max64u(best, xchg<1>(best));
+            best = max64u(best, xchg<2>(best));
+            best = max64u(best, xchg<3>(best));
+            best = max64u(best, xchg<4>(best));
+            best = max64u(best, xchg<5>(best));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (key[j] == best) key[j] = 0ull;  // taken (keys are unique)
+            if (lane == 0) {
+                const uint32_t o = (uint32_t)(best >> 32);
+                ids[t][r] = (int)(0xffffffffu - (uint32_t)best);
+                wts[t][r] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);  // the logit, for now
+            }
+        }
+    }
+    __syncthreads();
+    // softmax over the k selected logits of each token (one lane per token)
+    if (tid < T) {
+        const int t = tid;
+        const float m = wts[t][0];
+        float z = 0.0f;
+        for (int r = 0; r < k; ++r) z += expf(wts[t][r] - m);
+        float w[kMaxTopK];
+#pragma unroll
+        for (int r = 0; r < kMaxTopK; ++r) w[r] = r < k ? expf(wts[t][r] - m) / z : 0.0f;
+#pragma unroll
+        for (int r = 0; r < kMaxTopK; ++r)
+            if (r < k) wts[t][r] = w[r];
+    }
+    __syncthreads();
+    // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
+    if (wv == 0) {
+        const int np = T * k, p = lane;
+        const bool valid = p < np;
+        const int e = valid ? ids[p / k][p % k] : -1;
+        int first = p, j = 0, c = 0;  // first pair with this expert, position among them, count
+        for (int q = 0; q < np; ++q) {
+            const bool same = ids[q / k][q % k] == e;
+            if (same && q < first) first = q;
+            if (same && q < p) ++j;
+            if (same) ++c;
+        }
+        const uint64_t firsts = __ballot(valid && j == 0);
+        const int slot = __popcll(firsts & ((1ull << first) - 1ull));
+        if (valid) {
+            if (j == 0) {
+                st->expert[slot] = e;
+                st->ntok[slot] = c;
+            }
+            st->tok[slot][j] = p / k;
+            st->rank[slot][j] = p % k;
+            st->w[slot][j] = wts[p / k][p % k];
+        }
+        if (lane == 0) st->n = __popcll(firsts);
+    }
+    __syncthreads();
+}
+
+template <int T, int BPL, int KSUB, int ITERS>
+__global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
+    extern __shared__ uint4 smem2[];
+    half2_t* xh = (half2_t*)smem2;                          // [T][H/2]
+    __shared__ SlotTable st;
+    __shared__ int ids[T][kMaxTopK];
+    __shared__ float wts[T][kMaxTopK];
+    __shared__ float red[kMaxWaves * T * kGuRows];
+    __shared__ float sx[T];
+    __shared__ float sh[T];
+    __shared__ uint32_t shu[T];
+    __shared__ int shp[T];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    const int H = a.H, I = a.I, k = a.k, tiles = I / kGuOut, NC = H / 8;
+
+    if ((int)blockIdx.x < a.n_gu_wg) {
+        // FP8 codes of the input: one 8-byte load per thread and token, issued first
+        uint2 xc[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            if (tid < NC) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + tid * 8);
+        if (tid < T) sx[tid] = a.xs[tid];
+        route<T>(a, &st, ids, wts);
+        const int slot = blockIdx.x / tiles, tile = blockIdx.x - slot * tiles;
+        if (slot >= st.n) return;
+        GuLoads<BPL> L;
+        L.issue(a.w13, a.w13s, st.expert[slot], tile, tiles, NW);
+        if (blockIdx.x == 0) {
+            for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
+                ((int*)a.slots_out)[i] = ((const int*)&st)[i];
+            for (int i = tid; i < T * k; i += blockDim.x) {
+                if (a.ids_out) a.ids_out[i] = ids[i / k][i % k];
+                if (a.w_out) a.w_out[i] = wts[i / k][i % k];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (tid < NC) {
+                half2_t* o = xh + t * (H / 2) + tid * 4;
+                o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
+                o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
+                o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
+                o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
+            }
+        }
+        __syncthreads();
+        const int nt = st.ntok[slot];
+        int tok[T], pair[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            tok[j] = j < nt ? st.tok[slot][j] : 0;
+            pair[j] = j < nt ? tok[j] * (k + a.S) + st.rank[slot][j] : 0;
+        }
+        gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
+    } else {
+        // shared expert down: each wave one R-row tile, every token
+        constexpr int R = kWave / KSUB;
+        const int rt = (blockIdx.x - a.n_gu_wg) * NW + wv, rtiles = H / R;
+        const int Ih = I / 2, ks = lane % KSUB;
+        uint4 wr[ITERS];
+        uint32_t sb[ITERS];
+        if (rt < rtiles) {
+            const size_t base = (((size_t)a.E * rtiles + rt) * ITERS) * kWave + lane;
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                wr[it] = ld_nt(a.w2 + base + (size_t)it * kWave);
+                sb[it] = __builtin_nontemporal_load(a.w2s + base + (size_t)it * kWave);
+            }
+        }
+        // the shared expert's h of every token, loaded up front (<= 8 float2 per thread)
+        constexpr int MAXV = 8;
+        float2 hv[MAXV];
+        const int nv = a.ntok * Ih;
+#pragma unroll
+        for (int m = 0; m < MAXV; ++m) {
+            const int i = tid + m * (int)blockDim.x;
+            if (i < nv) {
+                const int t = i / Ih, q = i - t * Ih;
+                hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
+            }
+        }
+        // requantisation scales s_h = max|h| / 448
+        if (tid < T) shp[tid] = tid < a.ntok ? tid * (k + a.S) + k : -1;
+        __syncthreads();
+        requant_scales(a.hamax, tiles, shp, T, sh, shu);
+        half2_t* hh = xh;  // [T][I/2]
+#pragma unroll
+        for (int m = 0; m < MAXV; ++m) {
+            const int i = tid + m * (int)blockDim.x;
+            if (i < nv) {
+                const float sc = sh[i / Ih];
+                hh[i] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / sc, hv[m].y / sc));
+            }
+        }
+        for (int i = tid + MAXV * (int)blockDim.x; i < nv; i += blockDim.x) {  // remainder (other shapes)
+            const int t = i / Ih, q = i - t * Ih;
+            const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
+            hh[i] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sh[t], v.y / sh[t]));
+        }
+        __syncthreads();
+        if (rt < rtiles) {
+            float p[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) p[t] = 0.0f;
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const float scale = e8m0_to_f32(sb[it]);
+                const int pbase = (it * KSUB + ks) * (kBlock / 2);
+                const half2_t* xp[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) xp[t] = hh + t * Ih + pbase;
+                float q[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) q[t] = 0.0f;
+                block_dot<T>(wr[it], xp, q, a.ntok);
+#pragma unroll
+                for (int t = 0; t < T; ++t) p[t] = fmaf(q[t], scale, p[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                p[t] = sum_ksub<KSUB>(p[t]);
+                if (ks == 0) a.dshared[(size_t)t * H + rt * R + lane / KSUB] = sh[t] * p[t];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// k3: routed down rows + combine + residual
+// ------------------------------------------------------------------------------------------------
+
+struct K3Args {
     const SlotTable* slots;
-    const float* h;         // [kMaxSlots][kMaxTokens][I]
-    const float* hamax;     // [kMaxSlots][kMaxTokens][I/32]
-    const uint16_t* xres;   // [T][H] residual x_l, or null
-    uint16_t* xnext;        // [T][H] bf16(x_l + y), or null
-    float* y;               // [T][H] or null
-    int H, I;
+    const uint4* w2;
+    const uint8_t* w2s;
+    const float* h;          // [pairs][I]
+    const float* hamax;      // [pairs][I/16]
+    const float* dshared;    // [T][H] or null (no shared expert)
+    const uint16_t* xres;    // [T][H] residual x_l, or null
+    uint16_t* xnext;         // [T][H] bf16(x_l + y), or null
+    float* y;                // [T][H] or null
+    int H, k, S, I;
 };
 
 template <int KSUB, int ITERS, int T, int SPW>
-__global__ __launch_bounds__(768) void down_kernel(DownArgs a) {
+__global__ __launch_bounds__(768) void k3_down(K3Args a) {
     constexpr int R = kWave / KSUB;
-    constexpr int kMaxPairs = kMaxTokens * kMaxTopK + kMaxTokens;
-    extern __shared__ uint4 smem_dn[];
-    half2_t* hh = (half2_t*)smem_dn;  // [pairs][I/2]
-    __shared__ int pr_slot[kMaxPairs], pr_j[kMaxPairs];
-    __shared__ float pr_sh[kMaxPairs], pr_coef[kMaxPairs];
-    __shared__ int slot_pair0[kMaxSlots];
-    __shared__ int s_npairs;
+    constexpr int MAXV = T == 1 ? 6 : T == 2 ? 12 : 18;  // float2 of h per thread, loaded up front
+    extern __shared__ uint4 smem3[];
+    half2_t* hh = (half2_t*)smem3;  // [T*k][I/2], routed pair t*k + r
+    __shared__ float s_h[kMaxTokens * kMaxTopK];
+    __shared__ uint32_t s_hu[kMaxTokens * kMaxTopK];
+    __shared__ int s_pair[kMaxTokens * kMaxTopK];
+    __shared__ int s_expert[kMaxSlots], s_ntok[kMaxSlots], s_tok[kMaxSlots][kMaxTokens], s_rank[kMaxSlots][kMaxTokens];
+    __shared__ float s_w[kMaxSlots][kMaxTokens];
+    __shared__ int s_n;
     __shared__ float red[16][T][R];
+    const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6;
+    const int H = a.H, I = a.I, k = a.k, Ih = I / 2, tiles = I / kGuOut, rtiles = H / R;
+    const int tile = blockIdx.x, ks = lane % KSUB;
+    const int npairs = T * k, nv = npairs * Ih;
+
+    // 1. independent loads: slot list, h of every routed pair (first MAXV * nth values)
     const SlotTable* st = a.slots;
-    const int n = st->n;
-    const int H = a.H, I = a.I, NB = I / kBlock, Ih = I / 2, tiles = H / R;
-    const int tile = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-
-    if (tid == 0) {
-        int p = 0;
-        for (int s = 0; s < n; ++s) {
-            slot_pair0[s] = p;
-            const int nt = st->ntok[s];
-            for (int j = 0; j < nt; ++j) {
-                pr_slot[p] = s;
-                pr_j[p] = j;
-                ++p;
-            }
+    if (tid == 0) s_n = st->n;
+    if (tid < kMaxSlots) {
+        s_expert[tid] = st->expert[tid];
+        s_ntok[tid] = st->ntok[tid];
+#pragma unroll
+        for (int j = 0; j < kMaxTokens; ++j) {
+            s_tok[tid][j] = st->tok[tid][j];
+            s_rank[tid][j] = st->rank[tid][j];
+            s_w[tid][j] = st->w[tid][j];
         }
-        s_npairs = p;
     }
+    float2 hv[MAXV];
+#pragma unroll
+    for (int m = 0; m < MAXV; ++m) {
+        const int i = tid + m * nth;
+        if (i < nv) {
+            const int p = i / Ih, q = i - p * Ih, t = p / k, r = p - t * k;
+            hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q);
+        }
+    }
+    if (tid < npairs) s_pair[tid] = (tid / k) * (k + a.S) + tid % k;
+    __syncthreads();
+    const int n = s_n;
 
-    // 1. weight loads for this wave's slots
+    // 2. down weight loads of this wave's slots
     uint4 wr[SPW][ITERS];
     uint32_t sb[SPW][ITERS];
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
         const int s = wv + NW * m;
         if (s < n) {
-            const size_t base = (((size_t)st->expert[s] * tiles + tile) * ITERS) * kWave + lane;
+            const size_t base = (((size_t)s_expert[s] * rtiles + tile) * ITERS) * kWave + lane;
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
                 wr[m][it] = ld_nt(a.w2 + base + (size_t)it * kWave);
@@ -593,39 +881,37 @@ __global__ __launch_bounds__(768) void down_kernel(DownArgs a) {
             }
         }
     }
-    __syncthreads();
 
-    // 2. FP8 requantisation of every (slot, token) h vector: s_h = max|h| / 448
-    const int npairs = s_npairs;
-    if (tid < npairs) {
-        const int s = pr_slot[tid], j = pr_j[tid];
-        const float* am = a.hamax + ((size_t)s * kMaxTokens + j) * (I / kGuHalf);
-        float m = 0.0f;
-        for (int b = 0; b < I / kGuHalf; ++b) m = fmaxf(m, am[b]);
-        const float sh = m > 0.0f ? m / 448.0f : 1.0f;
-        pr_sh[tid] = sh;
-        pr_coef[tid] = st->w[s][j] * sh;
+    // 3. FP8 requantisation of every routed (token, rank) h vector into LDS
+    requant_scales(a.hamax, tiles, s_pair, npairs, s_h, s_hu);
+#pragma unroll
+    for (int m = 0; m < MAXV; ++m) {
+        const int i = tid + m * nth;
+        if (i < nv) {
+            const float sc = s_h[i / Ih];
+            hh[i] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / sc, hv[m].y / sc));
+        }
     }
-    __syncthreads();
-    for (int idx = tid; idx < npairs * Ih; idx += blockDim.x) {
-        const int p = idx / Ih, q = idx - p * Ih;
-        const float* hp = a.h + ((size_t)pr_slot[p] * kMaxTokens + pr_j[p]) * I;
-        const float2 v = *(const float2*)(hp + 2 * q);
-        const float sh = pr_sh[p];
-        hh[idx] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sh, v.y / sh));
+    for (int i = tid + MAXV * nth; i < nv; i += nth) {  // remainder (large T * k * I only)
+        const int p = i / Ih, q = i - p * Ih, t = p / k, r = p - t * k;
+        const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q);
+        const float sc = s_h[p];
+        hh[i] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sc, v.y / sc));
     }
     __syncthreads();
 
-    // 3. down block dot products, weighted into per-token accumulators
+    // 4. block dot products, routing-weighted into per-token accumulators
     float acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-    const int ks = lane % KSUB;
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
         const int s = wv + NW * m;
         if (s < n) {
-            const int p0 = slot_pair0[s], nt = st->ntok[s];
+            const int nt = s_ntok[s];
+            int pp[T];
+#pragma unroll
+            for (int j = 0; j < T; ++j) pp[j] = j < nt ? s_tok[s][j] * k + s_rank[s][j] : 0;
             float pj[T];
 #pragma unroll
             for (int j = 0; j < T; ++j) pj[j] = 0.0f;
@@ -635,19 +921,20 @@ __global__ __launch_bounds__(768) void down_kernel(DownArgs a) {
                 const int pbase = (it * KSUB + ks) * (kBlock / 2);
                 const half2_t* xp[T];
 #pragma unroll
-                for (int j = 0; j < T; ++j) xp[j] = hh + (p0 + j) * Ih + pbase;
+                for (int j = 0; j < T; ++j) xp[j] = hh + pp[j] * Ih + pbase;
                 float q[T];
 #pragma unroll
                 for (int j = 0; j < T; ++j) q[j] = 0.0f;
                 block_dot<T>(wr[m][it], xp, q, nt);
 #pragma unroll
                 for (int j = 0; j < T; ++j) pj[j] = fmaf(q[j], scale, pj[j]);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int j = 0; j < T; ++j) {
                 if (j < nt) {
-                    const int tk = st->tok[s][j];
-                    const float cf = pr_coef[p0 + j];
+                    const int tk = s_tok[s][j];
+                    const float cf = s_w[s][j] * s_h[pp[j]];
 #pragma unroll
                     for (int t = 0; t < T; ++t)
                         if (t == tk) acc[t] = fmaf(cf, pj[j], acc[t]);
@@ -656,20 +943,20 @@ __global__ __launch_bounds__(768) void down_kernel(DownArgs a) {
         }
     }
 
-    // 4. reduce over the KSUB lanes of a row, then over waves in wave order
+    // 5. reduce over the KSUB lanes of a row, then over waves in wave order; add the shared expert
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        for (int off = 1; off < KSUB; off <<= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+    for (int t = 0; t < T; ++t) acc[t] = sum_ksub<KSUB>(acc[t]);
     if (ks == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) red[wv][t][lane / KSUB] = acc[t];
     }
     __syncthreads();
-    for (int idx = tid; idx < R * T; idx += blockDim.x) {
+    for (int idx = tid; idx < R * T; idx += nth) {
         const int t = idx / R, r = idx - t * R;
         float ysum = 0.0f;
         for (int w = 0; w < NW; ++w) ysum += red[w][t][r];
         const size_t o = (size_t)t * H + (size_t)tile * R + r;
+        if (a.dshared) ysum += a.dshared[o];
         if (a.y) a.y[o] = ysum;
         if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(a.xres[o]) + ysum);
     }
@@ -691,77 +978,88 @@ hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, c
                          hipStream_t stream) {
     const int nexp = sh.E + sh.S;
     const unsigned B = 256;
-    repack_router<<<grid_for((uint64_t)sh.RT() * kRouterRows * sh.H / 8, B), B, 0, stream>>>(
-        (const uint16_t*)router, (uint4*)d_router, sh.E, sh.H, sh.RT());
+    hipError_t e = hipMemcpyAsync(d_router, router, sh.router_bytes(), hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
     repack_w13<<<grid_for((uint64_t)nexp * sh.I * sh.H / 16, B), B, 0, stream>>>((const uint4*)w13, (uint4*)d_w13,
-                                                                                  nexp, sh.I, sh.H);
-    repack_w13s<<<grid_for((uint64_t)nexp * 2 * sh.I * sh.H / 32 / 8, B), B, 0, stream>>>(
-        (const uint8_t*)w13s, (uint2*)d_w13s, nexp, sh.I, sh.H);
+                                                                                  nexp, sh.I, sh.H, sh.bpl());
+    repack_w13s<<<grid_for((uint64_t)nexp * 2 * sh.I * sh.H / 32, B), B, 0, stream>>>(
+        (const uint8_t*)w13s, (uint8_t*)d_w13s, nexp, sh.I, sh.H, sh.bpl());
     repack_w2<<<grid_for((uint64_t)nexp * sh.H * sh.I / 32, B), B, 0, stream>>>(
-        (const uint4*)w2, (uint4*)d_w2, nexp, sh.H, sh.I, sh.down_ksub());
+        (const uint4*)w2, (uint4*)d_w2, nexp, sh.H, sh.I, sh.ksub());
     repack_w2s<<<grid_for((uint64_t)nexp * sh.H * sh.I / 32, B), B, 0, stream>>>(
-        (const uint8_t*)w2s, (uint8_t*)d_w2s, nexp, sh.H, sh.I, sh.down_ksub());
+        (const uint8_t*)w2s, (uint8_t*)d_w2s, nexp, sh.H, sh.I, sh.ksub());
     return hipGetLastError();
 }
 
-int down_spw(int T) { return T == 1 ? 1 : T == 2 ? 2 : 3; }
+int routed_slots_max(const Shape& sh, int T) { return T * sh.k < sh.E ? T * sh.k : sh.E; }
 
-int max_slots(const Shape& sh, int T) {
-    const int routed = T * sh.k < sh.E ? T * sh.k : sh.E;
-    return routed + sh.S;
+template <int T, int BPL, int KSUB, int ITERS>
+static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                                 hipStream_t stream, hipEvent_t* ev) {
+    const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows(), rtiles = sh.H / R;
+    if (ev) (void)hipEventRecord(ev[0], stream);
+
+    const int n_router_wg = (sh.E + GW - 1) / GW;
+    K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.trace, P.logits,
+              P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0,
+              n_router_wg, T};
+    k1_router_shared<T, BPL><<<n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream>>>(a1);
+    if (ev) (void)hipEventRecord(ev[1], stream);
+
+    const int n_gu_wg = routed_slots_max(sh, T) * tiles;
+    const int n_sd_wg = sh.S ? (rtiles + GW - 1) / GW : 0;
+    K2Args a2{P.logits, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, (const uint4*)L.w2,
+              (const uint8_t*)L.w2s, P.slots, P.ids, P.w, P.h, P.hamax, P.dshared, sh.H, sh.E, sh.k, sh.S, sh.I,
+              n_gu_wg, T};
+    const size_t lds2 = (size_t)T * sh.H * 2;
+    k2_gateup<T, BPL, KSUB, ITERS><<<n_gu_wg + n_sd_wg, 64 * GW, lds2, stream>>>(a2);
+    if (ev) (void)hipEventRecord(ev[2], stream);
+
+    constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 3;
+    const int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
+    K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, sh.S ? P.dshared : nullptr,
+              P.xnext ? P.x : nullptr, P.xnext, P.y, sh.H, sh.k, sh.S, sh.I};
+    const size_t lds3 = (size_t)T * sh.k * sh.I * 2;
+    k3_down<KSUB, ITERS, T, SPW><<<rtiles, 64 * nw, lds3, stream>>>(a3);
+    if (ev) (void)hipEventRecord(ev[3], stream);
+    return hipGetLastError();
+}
+
+template <int T, int BPL>
+static hipError_t launch_layer_b(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                                 hipStream_t stream, hipEvent_t* ev) {
+    const int ks = sh.ksub(), it = sh.iters();
+    if (ks == 8 && it == 3) return launch_layer_t<T, BPL, 8, 3>(sh, L, P, normalize, stream, ev);
+    if (ks == 8 && it == 1) return launch_layer_t<T, BPL, 8, 1>(sh, L, P, normalize, stream, ev);
+    if (ks == 4 && it == 1) return launch_layer_t<T, BPL, 4, 1>(sh, L, P, normalize, stream, ev);
+    if (ks == 2 && it == 1) return launch_layer_t<T, BPL, 2, 1>(sh, L, P, normalize, stream, ev);
+    return hipErrorInvalidValue;
 }
 
 template <int T>
-static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
-                                 hipStream_t stream, hipEvent_t* ev) {
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    RouterArgs ra{(const uint4*)L.router, P.x, P.xin, P.trace, P.partial, P.ticket, P.slots, P.ids, P.w,
-                  sh.H, sh.E, sh.k, sh.S, normalize ? 1 : 0};
-    router_kernel<T><<<dim3(sh.H / kRouterSlice, sh.RT()), 256, 0, stream>>>(ra);
-    if (ev) (void)hipEventRecord(ev[1], stream);
-
-    const int slots = max_slots(sh, T);
-    GateUpArgs ga{(const uint4*)L.w13, (const uint2*)L.w13s, P.xin, P.slots, P.h, P.hamax, P.x_scale, P.x_codes,
-                  sh.H, sh.I};
-    gateup_kernel<T><<<dim3(sh.I / kGuHalf, slots), 64 * (sh.H / kGuSlice), (size_t)T * sh.H * 2, stream>>>(ga);
-    if (ev) (void)hipEventRecord(ev[2], stream);
-
-    DownArgs da{(const uint4*)L.w2, (const uint8_t*)L.w2s, P.slots, P.h, P.hamax, P.xnext ? P.x : nullptr,
-                P.xnext, P.y, sh.H, sh.I};
-    const int spw = down_spw(T);
-    const int nw = (slots + spw - 1) / spw;
-    const int pairs = T * sh.k + (sh.S ? T : 0);
-    const size_t lds = (size_t)pairs * sh.I * 2;
-    const int ksub = sh.down_ksub(), iters = sh.down_iters();
-    const dim3 grid(sh.H / sh.down_rows());
-    const unsigned block = 64 * nw;
-    constexpr int S = T == 1 ? 1 : T == 2 ? 2 : 3;
-    if (ksub == 2 && iters == 1) down_kernel<2, 1, T, S><<<grid, block, lds, stream>>>(da);
-    else if (ksub == 4 && iters == 1) down_kernel<4, 1, T, S><<<grid, block, lds, stream>>>(da);
-    else if (ksub == 4 && iters == 2) down_kernel<4, 2, T, S><<<grid, block, lds, stream>>>(da);
-    else if (ksub == 4 && iters == 4) down_kernel<4, 4, T, S><<<grid, block, lds, stream>>>(da);
-    else if (ksub == 4 && iters == 6) down_kernel<4, 6, T, S><<<grid, block, lds, stream>>>(da);
-    else return hipErrorInvalidValue;
-    if (ev) (void)hipEventRecord(ev[3], stream);
-    return hipGetLastError();
+static hipError_t launch_layer_tt(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                                  hipStream_t stream, hipEvent_t* ev) {
+    return sh.bpl() == 8 ? launch_layer_b<T, 8>(sh, L, P, normalize, stream, ev)
+                         : launch_layer_b<T, 4>(sh, L, P, normalize, stream, ev);
 }
 
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                         hipStream_t stream, hipEvent_t* ev) {
     switch (T) {
-        case 1: return launch_layer_t<1>(sh, L, P, normalize, stream, ev);
-        case 2: return launch_layer_t<2>(sh, L, P, normalize, stream, ev);
-        case 3: return launch_layer_t<3>(sh, L, P, normalize, stream, ev);
-        case 4: return launch_layer_t<4>(sh, L, P, normalize, stream, ev);
+        case 1: return launch_layer_tt<1>(sh, L, P, normalize, stream, ev);
+        case 2: return launch_layer_tt<2>(sh, L, P, normalize, stream, ev);
+        case 3: return launch_layer_tt<3>(sh, L, P, normalize, stream, ev);
+        case 4: return launch_layer_tt<4>(sh, L, P, normalize, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-bool down_supported(int I) {
-    const int nb = I / kBlock;
-    if (I % kBlock) return false;
-    if (nb == 2) return true;
-    return nb % 4 == 0 && (nb / 4 == 1 || nb / 4 == 2 || nb / 4 == 4 || nb / 4 == 6);
+bool shape_supported(const Shape& sh) {
+    if (sh.H % 256 || sh.H > 2560 || sh.I % kBlock) return false;
+    if (sh.gw() < 1 || sh.gw() > kMaxWaves) return false;
+    const int ks = sh.ksub(), it = sh.iters();
+    if (ks * it != sh.NI() || sh.NB() != sh.gw() * sh.bpl() * 2) return false;
+    return (ks == 8 && (it == 1 || it == 3)) || (ks == 4 && it == 1) || (ks == 2 && it == 1);
 }
 
 }  // namespace moe

@@ -22,12 +22,13 @@ struct RunPtrs {
     float* x_scale;     // [T] or null
     uint8_t* x_codes;   // [T][H] or null
     // workspace
-    uint16_t* xin;
-    float* partial;
-    unsigned* ticket;
+    uint8_t* xq;        // [T][H] FP8 codes of the MoE input
+    float* xs;          // [T] their scales
+    float* logits;      // [T][E]
     SlotTable* slots;
-    float* h;
-    float* hamax;
+    float* h;           // [T*(k+S)][I]
+    float* hamax;       // [T*(k+S)][I/16]
+    float* dshared;     // [T][H] shared expert output
 };
 
 hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,
@@ -36,7 +37,7 @@ hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, c
 // ev (nullable) = 4 events recorded before the router and after each of the three kernels.
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                         hipStream_t stream, hipEvent_t* ev);
-bool down_supported(int I);
+bool shape_supported(const Shape& sh);
 
 }  // namespace moe
 
