@@ -45,6 +45,7 @@ struct moe_decode_handle {
     float* xs;
     uint16_t* xbuf[2];
     float* logits;
+    unsigned* ticket;
     moe::SlotTable* slots;
     float* h;
     float* hamax;
@@ -170,6 +171,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     const uint64_t o_xb0 = o; o += align256((uint64_t)T * sh.H * 2);
     const uint64_t o_xb1 = o; o += align256((uint64_t)T * sh.H * 2);
     const uint64_t o_lg = o; o += align256((uint64_t)T * sh.E * 4);
+    const uint64_t o_tk = o; o += 256;
     const uint64_t o_slot = o; o += align256(sizeof(moe::SlotTable));
     const uint64_t o_h = o; o += align256((uint64_t)sh.pairs(T) * sh.I * 4);
     const uint64_t o_ham = o; o += align256((uint64_t)sh.pairs(T) * sh.gu_tiles() * 4);
@@ -193,6 +195,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->xbuf[0] = (uint16_t*)(h->ws + o_xb0);
     h->xbuf[1] = (uint16_t*)(h->ws + o_xb1);
     h->logits = (float*)(h->ws + o_lg);
+    h->ticket = (unsigned*)(h->ws + o_tk);
     h->slots = (moe::SlotTable*)(h->ws + o_slot);
     h->h = (float*)(h->ws + o_h);
     h->hamax = (float*)(h->ws + o_ham);
@@ -254,6 +257,7 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
         p.xq = h->xq;
         p.xs = h->xs;
         p.logits = h->logits;
+        p.ticket = h->ticket;
         p.slots = h->slots;
         p.h = h->h;
         p.hamax = h->hamax;

@@ -456,20 +456,120 @@ __device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, con
 }
 
 // FP8 requantisation scale of each listed h vector: s_h = max|h| / 448 (1 when h = 0), from the
-// per-tile maxima hamax[pair][tiles].  pairs[i] < 0 entries are skipped.  out: LDS floats;
-// scratch_u: LDS uints (one per listed vector).  Ends with a barrier.
-__device__ void requant_scales(const float* hamax, int tiles, const int* pairs, int n, float* out, uint32_t* scratch_u) {
-    const int tid = threadIdx.x, nth = blockDim.x;
-    for (int i = tid; i < n; i += nth) scratch_u[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n * tiles; i += nth) {
-        const int p = i / tiles, b = i - p * tiles;
-        if (pairs[p] >= 0) atomicMax(&scratch_u[p], __float_as_uint(hamax[(size_t)pairs[p] * tiles + b]));
+// per-tile maxima hamax[pair][tiles] (tiles <= 64).  One wave per vector, lanes over tiles, up to 4
+// vectors per wave and batch; pairs[i] < 0 gives 1.  out: LDS.  Ends with a barrier.
+__device__ void requant_scales(const float* hamax, int tiles, const int* pairs, int n, float* out) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    for (int base = wv; base < n; base += 4 * NW) {  // uniform per wave
+        int pr[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) pr[m] = base + NW * m < n ? pairs[base + NW * m] : -1;
+        float v[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = hamax[(size_t)max(pr[m], 0) * tiles + min(lane, tiles - 1)];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (pr[m] < 0 || lane >= tiles) v[m] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = base + NW * m;
+            if (i < n) {
+                const float mx = max64(v[m]);
+                if (lane == 0) out[i] = mx > 0.0f ? mx / 448.0f : 1.0f;
+            }
+        }
     }
     __syncthreads();
-    for (int i = tid; i < n; i += nth) {
-        const float m = __uint_as_float(scratch_u[i]);
-        out[i] = m > 0.0f ? m / 448.0f : 1.0f;
+}
+
+// Order-preserving 64-bit key of (logit, expert): larger logit first, then lower index first.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t max64u(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Top-k of every token (one wave per token: each lane keeps its 8 keys, k rounds of a wave-wide
+// maximum through lane exchanges, the winner's key is cleared), softmax weights over the selected
+// logits, and the list of distinct routed experts, all into LDS; identical in every workgroup.
+template <int T>
+__device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids, float* wts) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    for (int t = wv; t < T; t += NW) {
+        // all 8 loads unconditional (clamped index) so they are issued back to back
+        float lgv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            lgv[j] = __hip_atomic_load(logits + t * E + min(lane + 64 * j, E - 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t key[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = lane + 64 * j;
+            key[j] = e < E ? topk_key(lgv[j], e) : 0ull;
+        }
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = key[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) best = max64u(best, key[j]);
+            best = max64u(best, xchg<0>(best));
+            best = max64u(best, xchg<1>(best));
+            best = max64u(best, xchg<2>(best));
+            best = max64u(best, xchg<3>(best));
+            best = max64u(best, xchg<4>(best));
+            best = max64u(best, xchg<5>(best));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (key[j] == best) key[j] = 0ull;  // taken (keys are unique)
+            if (lane == 0) {
+                const uint32_t o = (uint32_t)(best >> 32);
+                ids[t * k + r] = (int)(0xffffffffu - (uint32_t)best);
+                wts[t * k + r] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);  // the logit, for now
+            }
+        }
+    }
+    __syncthreads();
+    // softmax over the k selected logits of each token (one lane per token)
+    if (tid < T) {
+        float* wt = wts + tid * k;
+        const float m = wt[0];
+        float z = 0.0f;
+        for (int r = 0; r < k; ++r) z += expf(wt[r] - m);
+        float w[kMaxTopK];
+#pragma unroll
+        for (int r = 0; r < kMaxTopK; ++r) w[r] = r < k ? expf(wt[r] - m) / z : 0.0f;
+#pragma unroll
+        for (int r = 0; r < kMaxTopK; ++r)
+            if (r < k) wt[r] = w[r];
+    }
+    __syncthreads();
+    // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
+    if (wv == 0) {
+        const int np = T * k, p = lane;
+        const bool valid = p < np;
+        const int e = valid ? ids[p] : -1;
+        int first = p, j = 0, c = 0;  // first pair with this expert, position among them, count
+        for (int q = 0; q < np; ++q) {
+            const bool same = ids[q] == e;
+            if (same && q < first) first = q;
+            if (same && q < p) ++j;
+            if (same) ++c;
+        }
+        const uint64_t firsts = __ballot(valid && j == 0);
+        const int slot = __popcll(firsts & ((1ull << first) - 1ull));
+        if (valid) {
+            if (j == 0) {
+                st->expert[slot] = e;
+                st->ntok[slot] = c;
+            }
+            const int t = p / k;
+            st->tok[slot][j] = t;
+            st->rank[slot][j] = p - t * k;
+            st->w[slot][j] = wts[p];
+        }
+        if (lane == 0) st->n = __popcll(firsts);
     }
     __syncthreads();
 }
@@ -491,6 +591,10 @@ struct K1Args {
     uint8_t* x_codes_out;    // [T][H] or null
     float* h;                // [pairs][I]
     float* hamax;            // [pairs][I/16]
+    unsigned* ticket;        // arrivals of router workgroups; zero between layers
+    SlotTable* slots_out;    // routed experts of this layer (written by the last router workgroup)
+    int32_t* ids_out;        // [T][k] or null
+    float* w_out;            // [T][k] or null
     int H, E, k, S, I, normalize, n_router_wg;
     int ntok;                // = T, passed at run time so the shared tile's token loop stays a loop
 };
@@ -504,6 +608,10 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
     __shared__ float wmax[kMaxWaves * T];
     __shared__ float red[kMaxWaves * T * kGuRows];
     __shared__ float sx[T];
+    __shared__ SlotTable st;
+    __shared__ int ids[T * kMaxTopK];
+    __shared__ float wts[T * kMaxTopK];
+    __shared__ int is_last;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
     const int H = a.H;
     const bool is_router = (int)blockIdx.x < a.n_router_wg;
@@ -515,11 +623,10 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
         const int e = blockIdx.x * NW + wv;
         const int NU = H / 8;
         uint4 wr[kMaxWaves];
-        if (e < a.E) {
-            const uint4* p = (const uint4*)(a.router + (size_t)e * H);
+        {
+            const uint4* p = (const uint4*)(a.router + (size_t)min(e, a.E - 1) * H);
 #pragma unroll
-            for (int j = 0; j < kMaxWaves; ++j)
-                if (lane + 64 * j < NU) wr[j] = ld_nt(p + lane + 64 * j);
+            for (int j = 0; j < kMaxWaves; ++j) wr[j] = ld_nt(p + min(lane + 64 * j, NU - 1));
         }
         moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
         if (blockIdx.x == 0 && a.trace) {
@@ -550,8 +657,26 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const float v = sum64(acc[t]);
-                if (lane == 0) a.logits[t * a.E + e] = v;
+                // write-through store: the last router workgroup reads it without any cache flush
+                if (lane == 0) __hip_atomic_store(a.logits + t * a.E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+        }
+        // the last router workgroup to arrive takes the top-k of every token for the whole layer
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's logit stores have completed
+        __syncthreads();
+        if (tid == 0)
+            is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (unsigned)(a.n_router_wg - 1);
+        __syncthreads();
+        if (is_last) {
+            route<T>(a.logits, a.E, a.k, &st, ids, wts);
+            for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
+                ((int*)a.slots_out)[i] = ((const int*)&st)[i];
+            for (int i = tid; i < T * a.k; i += blockDim.x) {
+                if (a.ids_out) a.ids_out[i] = ids[i];
+                if (a.w_out) a.w_out[i] = wts[i];
+            }
+            if (tid == 0) *a.ticket = 0u;  // read again only by the next layer's router, after this kernel
         }
     } else {
         // shared expert (index E), gate/up tile, every token
@@ -576,16 +701,13 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
 // ------------------------------------------------------------------------------------------------
 
 struct K2Args {
-    const float* logits;     // [T][E]
+    const SlotTable* slots;  // routed experts of this layer
     const uint8_t* xq;       // [T][H] FP8 codes of the MoE input
     const float* xs;         // [T] their scales
     const uint4* w13;
     const uint8_t* w13s;
     const uint4* w2;
     const uint8_t* w2s;
-    SlotTable* slots_out;    // workgroup 0
-    int32_t* ids_out;        // [T][k] or null (workgroup 0)
-    float* w_out;            // [T][k] or null (workgroup 0)
     float* h;                // [pairs][I]
     float* hamax;            // [pairs][I/16]
     float* dshared;          // [T][H]
@@ -593,102 +715,13 @@ struct K2Args {
     int ntok;                // = T, at run time (keeps the shared expert's token loop a loop)
 };
 
-// Order-preserving 64-bit key of (logit, expert): larger logit first, then lower index first.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t max64u(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Top-k of every token (one wave per token: each lane keeps its 8 keys, k rounds of a wave-wide
-// maximum through lane exchanges, the winner's key is cleared), softmax weights over the selected
-// logits, and the list of distinct routed experts, all into LDS; identical in every workgroup.
-template <int T>
-__device__ void route(const K2Args& a, SlotTable* st, int (*ids)[kMaxTopK], float (*wts)[kMaxTopK]) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, E = a.E, k = a.k;
-    for (int t = wv; t < T; t += NW) {
-        uint64_t key[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int e = lane + 64 * j;
-            key[j] = e < E ? topk_key(a.logits[t * E + e], e) : 0ull;
-        }
-        for (int r = 0; r < k; ++r) {
-            uint64_t best = key[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) best = max64u(best, key[j]);
-            best = max64u(best, xchg<0>(best));
-            best = max64u(best, xchg<1>(best));
-            best = max64u(best, xchg<2>(best));
-            best = max64u(best, xchg<3>(best));
-            best = max64u(best, xchg<4>(best));
-            best = max64u(best, xchg<5>(best));
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (key[j] == best) key[j] = 0ull;  // taken (keys are unique)
-            if (lane == 0) {
-                const uint32_t o = (uint32_t)(best >> 32);
-                ids[t][r] = (int)(0xffffffffu - (uint32_t)best);
-                wts[t][r] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);  // the logit, for now
-            }
-        }
-    }
-    __syncthreads();
-    // softmax over the k selected logits of each token (one lane per token)
-    if (tid < T) {
-        const int t = tid;
-        const float m = wts[t][0];
-        float z = 0.0f;
-        for (int r = 0; r < k; ++r) z += expf(wts[t][r] - m);
-        float w[kMaxTopK];
-#pragma unroll
-        for (int r = 0; r < kMaxTopK; ++r) w[r] = r < k ? expf(wts[t][r] - m) / z : 0.0f;
-#pragma unroll
-        for (int r = 0; r < kMaxTopK; ++r)
-            if (r < k) wts[t][r] = w[r];
-    }
-    __syncthreads();
-    // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
-    if (wv == 0) {
-        const int np = T * k, p = lane;
-        const bool valid = p < np;
-        const int e = valid ? ids[p / k][p % k] : -1;
-        int first = p, j = 0, c = 0;  // first pair with this expert, position among them, count
-        for (int q = 0; q < np; ++q) {
-            const bool same = ids[q / k][q % k] == e;
-            if (same && q < first) first = q;
-            if (same && q < p) ++j;
-            if (same) ++c;
-        }
-        const uint64_t firsts = __ballot(valid && j == 0);
-        const int slot = __popcll(firsts & ((1ull << first) - 1ull));
-        if (valid) {
-            if (j == 0) {
-                st->expert[slot] = e;
-                st->ntok[slot] = c;
-            }
-            st->tok[slot][j] = p / k;
-            st->rank[slot][j] = p % k;
-            st->w[slot][j] = wts[p / k][p % k];
-        }
-        if (lane == 0) st->n = __popcll(firsts);
-    }
-    __syncthreads();
-}
-
 template <int T, int BPL, int KSUB, int ITERS>
 __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     extern __shared__ uint4 smem2[];
     half2_t* xh = (half2_t*)smem2;                          // [T][H/2]
-    __shared__ SlotTable st;
-    __shared__ int ids[T][kMaxTopK];
-    __shared__ float wts[T][kMaxTopK];
     __shared__ float red[kMaxWaves * T * kGuRows];
     __shared__ float sx[T];
     __shared__ float sh[T];
-    __shared__ uint32_t shu[T];
     __shared__ int shp[T];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
     const int H = a.H, I = a.I, k = a.k, tiles = I / kGuOut, NC = H / 8;
@@ -699,20 +732,21 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
             if (tid < NC) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + tid * 8);
-        if (tid < T) sx[tid] = a.xs[tid];
-        route<T>(a, &st, ids, wts);
+        const float sxv = a.xs[tid < T ? tid : 0];
         const int slot = blockIdx.x / tiles, tile = blockIdx.x - slot * tiles;
-        if (slot >= st.n) return;
-        GuLoads<BPL> L;
-        L.issue(a.w13, a.w13s, st.expert[slot], tile, tiles, NW);
-        if (blockIdx.x == 0) {
-            for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
-                ((int*)a.slots_out)[i] = ((const int*)&st)[i];
-            for (int i = tid; i < T * k; i += blockDim.x) {
-                if (a.ids_out) a.ids_out[i] = ids[i / k][i % k];
-                if (a.w_out) a.w_out[i] = wts[i / k][i % k];
-            }
+        // this workgroup's routed expert and its tokens (uniform loads)
+        const int n = a.slots->n, expert = a.slots->expert[slot < kMaxSlots ? slot : 0];
+        const int nt = a.slots->ntok[slot < kMaxSlots ? slot : 0];
+        int tok[T], pair[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            tok[j] = a.slots->tok[slot][j];
+            pair[j] = tok[j] * (k + a.S) + a.slots->rank[slot][j];
         }
+        if (slot >= n) return;
+        GuLoads<BPL> L;
+        L.issue(a.w13, a.w13s, expert, tile, tiles, NW);
+        if (tid < T) sx[tid] = sxv;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             if (tid < NC) {
@@ -724,13 +758,9 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
             }
         }
         __syncthreads();
-        const int nt = st.ntok[slot];
-        int tok[T], pair[T];
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-            tok[j] = j < nt ? st.tok[slot][j] : 0;
-            pair[j] = j < nt ? tok[j] * (k + a.S) + st.rank[slot][j] : 0;
-        }
+        for (int j = 0; j < T; ++j)
+            if (j >= nt) tok[j] = pair[j] = 0;
         gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
     } else {
         // shared expert down: each wave one R-row tile, every token
@@ -747,35 +777,37 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
                 sb[it] = __builtin_nontemporal_load(a.w2s + base + (size_t)it * kWave);
             }
         }
-        // the shared expert's h of every token, loaded up front (<= 8 float2 per thread)
-        constexpr int MAXV = 8;
-        float2 hv[MAXV];
-        const int nv = a.ntok * Ih;
+        // the shared expert's h of every token, loaded up front: thread -> column pairs q0, q0 + threads
+        const int nth = blockDim.x;
+        float2 hv[2][T];
 #pragma unroll
-        for (int m = 0; m < MAXV; ++m) {
-            const int i = tid + m * (int)blockDim.x;
-            if (i < nv) {
-                const int t = i / Ih, q = i - t * Ih;
-                hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
-            }
+        for (int c = 0; c < 2; ++c) {
+            const int q = tid + c * nth;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (q < Ih && t < a.ntok) hv[c][t] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
         }
         // requantisation scales s_h = max|h| / 448
         if (tid < T) shp[tid] = tid < a.ntok ? tid * (k + a.S) + k : -1;
         __syncthreads();
-        requant_scales(a.hamax, tiles, shp, T, sh, shu);
+        requant_scales(a.hamax, tiles, shp, T, sh);
         half2_t* hh = xh;  // [T][I/2]
 #pragma unroll
-        for (int m = 0; m < MAXV; ++m) {
-            const int i = tid + m * (int)blockDim.x;
-            if (i < nv) {
-                const float sc = sh[i / Ih];
-                hh[i] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / sc, hv[m].y / sc));
-            }
+        for (int c = 0; c < 2; ++c) {
+            const int q = tid + c * nth;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (q < Ih && t < a.ntok)
+                    hh[t * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(hv[c][t].x / sh[t], hv[c][t].y / sh[t]));
         }
-        for (int i = tid + MAXV * (int)blockDim.x; i < nv; i += blockDim.x) {  // remainder (other shapes)
-            const int t = i / Ih, q = i - t * Ih;
-            const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
-            hh[i] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sh[t], v.y / sh[t]));
+        for (int q = tid + 2 * nth; q < Ih; q += nth) {  // more than two columns per thread (small H only)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if (t < a.ntok) {
+                    const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
+                    hh[t * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sh[t], v.y / sh[t]));
+                }
+            }
         }
         __syncthreads();
         if (rt < rtiles) {
@@ -825,11 +857,10 @@ struct K3Args {
 template <int KSUB, int ITERS, int T, int SPW>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     constexpr int R = kWave / KSUB;
-    constexpr int MAXV = T == 1 ? 6 : T == 2 ? 12 : 18;  // float2 of h per thread, loaded up front
+    constexpr int MAXP = T == 1 ? 8 : T == 3 ? 12 : 16;  // h columns (pairs) per thread, loaded up front
     extern __shared__ uint4 smem3[];
     half2_t* hh = (half2_t*)smem3;  // [T*k][I/2], routed pair t*k + r
     __shared__ float s_h[kMaxTokens * kMaxTopK];
-    __shared__ uint32_t s_hu[kMaxTokens * kMaxTopK];
     __shared__ int s_pair[kMaxTokens * kMaxTopK];
     __shared__ int s_expert[kMaxSlots], s_ntok[kMaxSlots], s_tok[kMaxSlots][kMaxTokens], s_rank[kMaxSlots][kMaxTokens];
     __shared__ float s_w[kMaxSlots][kMaxTokens];
@@ -838,31 +869,55 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6;
     const int H = a.H, I = a.I, k = a.k, Ih = I / 2, tiles = I / kGuOut, rtiles = H / R;
     const int tile = blockIdx.x, ks = lane % KSUB;
-    const int npairs = T * k, nv = npairs * Ih;
+    const int npairs = T * k;
+    // epilogue operands of this thread's output element (shared expert output, residual), loaded first
+    const int oe = tid < R * T ? tid : 0;
+    const size_t oo = (size_t)(oe / R) * H + (size_t)tile * R + oe % R;
+    const float ds_pre = a.dshared ? a.dshared[oo] : 0.0f;
+    const uint16_t xr_pre = a.xnext ? a.xres[oo] : (uint16_t)0;
+    // thread -> (column pair q, pair group g); G groups cover the pairs g, g + G, ...
+    const int G = nth / Ih, q0 = tid % Ih, g0 = tid / Ih;
+    const bool loader = G > 0 && g0 < G;
 
     // 1. independent loads: slot list, h of every routed pair (first MAXV * nth values)
     const SlotTable* st = a.slots;
-    if (tid == 0) s_n = st->n;
-    if (tid < kMaxSlots) {
-        s_expert[tid] = st->expert[tid];
-        s_ntok[tid] = st->ntok[tid];
+    {
+        const int sl = tid & (kMaxSlots - 1);  // every thread loads (no branch), the first kMaxSlots store
+        const int nn = st->n, ex = st->expert[sl], nt = st->ntok[sl];
+        int tk[kMaxTokens], rk[kMaxTokens];
+        float ww[kMaxTokens];
 #pragma unroll
         for (int j = 0; j < kMaxTokens; ++j) {
-            s_tok[tid][j] = st->tok[tid][j];
-            s_rank[tid][j] = st->rank[tid][j];
-            s_w[tid][j] = st->w[tid][j];
+            tk[j] = st->tok[sl][j];
+            rk[j] = st->rank[sl][j];
+            ww[j] = st->w[sl][j];
         }
-    }
-    float2 hv[MAXV];
+        if (tid == 0) s_n = nn;
+        if (tid < kMaxSlots) {
+            s_expert[tid] = ex;
+            s_ntok[tid] = nt;
 #pragma unroll
-    for (int m = 0; m < MAXV; ++m) {
-        const int i = tid + m * nth;
-        if (i < nv) {
-            const int p = i / Ih, q = i - p * Ih, t = p / k, r = p - t * k;
-            hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q);
+            for (int j = 0; j < kMaxTokens; ++j) {
+                s_tok[tid][j] = tk[j];
+                s_rank[tid][j] = rk[j];
+                s_w[tid][j] = ww[j];
+            }
         }
     }
     if (tid < npairs) s_pair[tid] = (tid / k) * (k + a.S) + tid % k;
+    // pair p = t*k + r lives at h row t*(k+S) + r = p + (p / k) * S; walk it without dividing
+    float2 hv[MAXP];
+    if (loader) {
+        int p = g0, t = 0, r = g0;
+        while (r >= k) { r -= k; ++t; }
+#pragma unroll
+        for (int m = 0; m < MAXP; ++m) {
+            if (p < npairs) hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q0);
+            p += G;
+            r += G;
+            while (r >= k) { r -= k; ++t; }
+        }
+    }
     __syncthreads();
     const int n = s_n;
 
@@ -883,20 +938,20 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     }
 
     // 3. FP8 requantisation of every routed (token, rank) h vector into LDS
-    requant_scales(a.hamax, tiles, s_pair, npairs, s_h, s_hu);
+    requant_scales(a.hamax, tiles, s_pair, npairs, s_h);
+    if (loader) {
 #pragma unroll
-    for (int m = 0; m < MAXV; ++m) {
-        const int i = tid + m * nth;
-        if (i < nv) {
-            const float sc = s_h[i / Ih];
-            hh[i] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / sc, hv[m].y / sc));
+        for (int m = 0; m < MAXP; ++m) {
+            const int p = g0 + m * G;
+            if (p < npairs) hh[p * Ih + q0] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / s_h[p], hv[m].y / s_h[p]));
         }
     }
-    for (int i = tid + MAXV * nth; i < nv; i += nth) {  // remainder (large T * k * I only)
-        const int p = i / Ih, q = i - p * Ih, t = p / k, r = p - t * k;
+    // pairs beyond the up-front batch, or every pair when there are fewer threads than columns
+    const int p0 = G > 0 ? (G * MAXP < npairs ? G * MAXP : npairs) : 0;
+    for (int i = tid; i < (npairs - p0) * Ih; i += nth) {
+        const int p = p0 + i / Ih, q = i % Ih, t = p / k, r = p - t * k;
         const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q);
-        const float sc = s_h[p];
-        hh[i] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sc, v.y / sc));
+        hh[p * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / s_h[p], v.y / s_h[p]));
     }
     __syncthreads();
 
@@ -951,14 +1006,14 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         for (int t = 0; t < T; ++t) red[wv][t][lane / KSUB] = acc[t];
     }
     __syncthreads();
-    for (int idx = tid; idx < R * T; idx += nth) {
+    for (int idx = tid; idx < R * T; idx += nth) {  // one pass: R * T <= threads
         const int t = idx / R, r = idx - t * R;
         float ysum = 0.0f;
         for (int w = 0; w < NW; ++w) ysum += red[w][t][r];
         const size_t o = (size_t)t * H + (size_t)tile * R + r;
-        if (a.dshared) ysum += a.dshared[o];
+        ysum += idx == tid ? ds_pre : (a.dshared ? a.dshared[o] : 0.0f);
         if (a.y) a.y[o] = ysum;
-        if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(a.xres[o]) + ysum);
+        if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(idx == tid ? xr_pre : a.xres[o]) + ysum);
     }
 }
 
@@ -1001,22 +1056,22 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
 
     const int n_router_wg = (sh.E + GW - 1) / GW;
     K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.trace, P.logits,
-              P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0,
-              n_router_wg, T};
+              P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, P.ticket, P.slots, P.ids, P.w, sh.H, sh.E, sh.k,
+              sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
     k1_router_shared<T, BPL><<<n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream>>>(a1);
     if (ev) (void)hipEventRecord(ev[1], stream);
 
     const int n_gu_wg = routed_slots_max(sh, T) * tiles;
     const int n_sd_wg = sh.S ? (rtiles + GW - 1) / GW : 0;
-    K2Args a2{P.logits, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, (const uint4*)L.w2,
-              (const uint8_t*)L.w2s, P.slots, P.ids, P.w, P.h, P.hamax, P.dshared, sh.H, sh.E, sh.k, sh.S, sh.I,
-              n_gu_wg, T};
+    K2Args a2{P.slots, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, (const uint4*)L.w2,
+              (const uint8_t*)L.w2s, P.h, P.hamax, P.dshared, sh.H, sh.E, sh.k, sh.S, sh.I, n_gu_wg, T};
     const size_t lds2 = (size_t)T * sh.H * 2;
     k2_gateup<T, BPL, KSUB, ITERS><<<n_gu_wg + n_sd_wg, 64 * GW, lds2, stream>>>(a2);
     if (ev) (void)hipEventRecord(ev[2], stream);
 
     constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 3;
-    const int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
+    int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
+    if (T >= 3 && nw < 12 && sh.I / 2 * 2 <= 64 * 12) nw = 12;  // two pair groups of h columns per thread block
     K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, sh.S ? P.dshared : nullptr,
               P.xnext ? P.x : nullptr, P.xnext, P.y, sh.H, sh.k, sh.S, sh.I};
     const size_t lds3 = (size_t)T * sh.k * sh.I * 2;

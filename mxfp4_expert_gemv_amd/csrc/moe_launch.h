@@ -25,6 +25,7 @@ struct RunPtrs {
     uint8_t* xq;        // [T][H] FP8 codes of the MoE input
     float* xs;          // [T] their scales
     float* logits;      // [T][E]
+    unsigned* ticket;   // router arrivals (zero between layers)
     SlotTable* slots;
     float* h;           // [T*(k+S)][I]
     float* hamax;       // [T*(k+S)][I/16]
