@@ -7,8 +7,9 @@ back to back through the C ABI.  One step = one pass through all 42 layers.  ``v
 algorithmic HBM bytes of a pass (router + the touched experts, counted from the returned ids)
 divided by the pass time.  Also reported: the same stack at 4 tokens (disjoint top-8 sets, 33
 experts per layer), single layers at 1 and 4 tokens with the 256 MB last-level cache flushed
-between passes, the roofline of the dominant kernel (gate/up), and the CPU oracle timed on a
-bounded sample of the same stack on the host cores.
+between passes, the roofline of the dominant kernel of a 1-token layer (kernel times from HIP
+events stamped by the kernel launches themselves), and the CPU oracle timed on a bounded sample of
+the same stack on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -38,7 +39,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")
+    ap.add_argument("--summarize", metavar="DIR", nargs="+",
+                    help="print a summary of the rocprofv3 CSV output in the DIRs (no GPU) and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode",
               file=sys.stderr)
@@ -114,6 +122,15 @@ def main():
         moe.moe_decode_timing_enable(h, 0)
         return {c: t[c]["total_ms"] / max(t[c]["launches"], 1) * 1e3 for c in moe.TIMING_CLASSES}  # us/launch
 
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: 4 copies of {COPY_PROBE_BYTES} bytes")
+
     results = {}
     for T in (1, 4):
         nbytes, distinct = pass_bytes(T)
@@ -158,13 +175,19 @@ def main():
             moe.moe_decode_destroy(h1)
         del flush
 
-    # roofline of the dominant kernel (gate/up: 61% of a 1-token layer's bytes)
-    gu_bytes = (shape.top_k + shape.num_shared) * (shape.w13_bytes + shape.w13s_bytes)
-    gu_us = results[1]["kernel_us"]["gateup"]
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gateup_kernel<1>",
-                "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3)}
+    # roofline of the dominant kernel of a 1-token layer (the one with the largest kernel time)
+    kb = kernel_bytes(shape, 1, shape.top_k)
+    kt1 = results[1]["kernel_us"]
+    names = kernel_names(info["variant"], 1)
+    per_kernel = {c: {"kernel": names[c], "bytes_per_launch": kb[c], "us_per_launch": round(kt1[c], 3),
+                      "gb_s": round(kb[c] / (kt1[c] * 1e-6) / 1e9, 1)} for c in moe.TIMING_CLASSES}
+    dom = max(moe.TIMING_CLASSES, key=lambda c: kt1[c])
+    achieved = per_kernel[dom]["gb_s"]
+    traffic = measured_traffic(names[dom])
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": names[dom],
+                "bytes_per_launch": kb[dom], "us_per_launch": round(kt1[dom], 3), "all_kernels_t1": per_kernel}
+    log(f"roofline: dominant {names[dom]} {kt1[dom]:.2f} us/launch, {achieved:.0f} GB/s; {per_kernel}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -182,6 +205,119 @@ def main():
            "single_layer": single, "variant": info["variant"], "roofline": roofline, "cpu_baseline": cpu}
     moe.moe_decode_destroy(h)
     print(json.dumps(out), flush=True)
+
+
+COPY_PROBE_BYTES = 256 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "mxfp4_expert_gemv_amd", "csrc", "moe_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_stack_t1.md")
+
+
+def source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
+    none or the kernel source has changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    block = text.split("```json")[1].split("```")[0] if "```json" in text else None
+    if block is None:
+        return None
+    rec = json.loads(block)
+    if rec.get("kernel_source_sha256_16") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def summarize(dirs):
+    """Markdown summary of rocprofv3 output in the given directories: the kernel statistics (--stats)
+    and, when counter files are present, FETCH_SIZE / WRITE_SIZE per dispatch, each scaled by what
+    the same counter reads for the 256 MiB copy probe (known to read and write 256 MiB)."""
+    import csv
+    import glob
+
+    def rows(pattern):
+        out = []
+        for d in dirs:
+            for f in sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True)):
+                with open(f) as fh:
+                    out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows("*kernel_stats.csv")
+    if stats:
+        print("| kernel | calls | average us | min us | max us | share % |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for r in stats:
+            print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    counters = rows("*counter_collection.csv")
+    if counters:
+        # the probe copies are the copy-kernel dispatches of the largest size; other copies (router
+        # rows at set-up) are smaller and are left out
+        probe = {}
+        for r in counters:
+            if "copyBuffer" in r["Kernel_Name"]:
+                probe.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        scale = {}
+        for c, vals in probe.items():
+            big = [v for v in vals if v >= 0.5 * max(vals)]
+            scale[c] = (COPY_PROBE_BYTES / 1024) / (sum(big) / len(big))
+        acc = {}
+        for r in counters:
+            if "copyBuffer" in r["Kernel_Name"]:
+                continue
+            a = acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), [0.0, 0])
+            a[0] += float(r["Counter_Value"])
+            a[1] += 1
+        kib = {k: v[0] / v[1] for k, v in acc.items()}
+        print()
+        print("| kernel | counter | KiB per dispatch | dispatches | scale (copy probe) | bytes per dispatch |")
+        print("|---|---|---:|---:|---:|---:|")
+        rec = {"kernel_source_sha256_16": source_digest(), "copy_probe_bytes": COPY_PROBE_BYTES, "scale": scale,
+               "kernels": {}}
+        for (n, c), v in sorted(kib.items()):
+            sc = scale.get(c)
+            b = v * 1024 * sc if sc else None
+            print(f"| `{n}` | {c} | {v:.1f} | {acc[(n, c)][1]} | {sc if sc is None else round(sc, 4)} | "
+                  f"{'' if b is None else int(b)} |")
+            if b is not None:
+                k = rec["kernels"].setdefault(n, {"hbm_bytes_per_launch": 0})
+                k[c] = int(b)
+                k["hbm_bytes_per_launch"] += int(b)
+        print()
+        print("```json")
+        print(json.dumps(rec, indent=1))
+        print("```")
+
+
+def kernel_bytes(shape, T, distinct):
+    """Algorithmic HBM bytes of one launch of each kernel of a layer: the weights it must read once
+    (router; gate/up and down halves of the touched experts) plus the activations it reads or writes
+    in HBM; per-call scratch that stays in the L2 (logits, slot list, h) is not counted."""
+    w13 = shape.w13_bytes + shape.w13s_bytes
+    w2 = shape.w2_bytes + shape.w2s_bytes
+    x = T * shape.hidden * 2
+    return {"router": shape.num_experts * shape.hidden * 2 + shape.num_shared * w13 + x,
+            "gateup": distinct * w13 + shape.num_shared * w2,
+            "down": distinct * w2 + 2 * x}
+
+
+def kernel_names(variant, T):
+    """Full names of the three kernels as the profiler lists them, from the library's variant string
+    (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-...)."""
+    gu, dn = variant.split("-")[2:4]
+    bpl = int(gu[2:].split("x")[1])
+    ksub, iters = (int(v) for v in dn[2:].split("x"))
+    spw = 1 if T == 1 else 2 if T == 2 else 3
+    return {"router": f"void moe::k1_router_shared<{T}, {bpl}>(moe::K1Args)",
+            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {ksub}, {iters}>(moe::K2Args)",
+            "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}
 
 
 def cpu_baseline(shape, st, x_host, expert_bytes, router_bytes, budget_s=12.0):

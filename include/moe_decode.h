@@ -163,11 +163,11 @@ moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, f
 moe_status fp8_head_destroy(fp8_head_handle* h);
 
 /* Kernel timing instrumentation.  moe_decode_timing_enable(h, max_runs) makes the next up to
- * max_runs calls of moe_decode_run record HIP events on their stream around every kernel launch
- * (one event before the first kernel of each layer and one after each kernel); 0 disables.
- * moe_decode_timing_read waits for those events and returns, per kernel class, the number of
- * launches and the summed event-to-event time, then clears the record.  Timing adds one event
- * record per launch to the stream, so it is meant for a measurement pass of its own. */
+ * max_runs calls of moe_decode_run launch their kernels one by one on the caller's stream (no
+ * graph), each with a start and a stop HIP event that the runtime stamps with that kernel's own
+ * begin and end times (hipExtLaunchKernel); 0 disables.  moe_decode_timing_read waits for those
+ * events and returns, per kernel class, the number of launches and the summed kernel time, then
+ * clears the record.  Meant for a measurement pass of its own. */
 #define MOE_TIMING_CLASSES 3 /* 0 router + top-k, 1 gate/up, 2 down + combine */
 typedef struct {
     uint32_t struct_size;                     /* sizeof(moe_decode_timing) */

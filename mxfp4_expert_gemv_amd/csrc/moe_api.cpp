@@ -263,7 +263,7 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
         p.hamax = h->hamax;
         p.dshared = h->dshared;
         hipEvent_t* ev = nullptr;
-        if (timing) ev = &h->events[((size_t)h->timing_runs * L + l) * 4];
+        if (timing) ev = &h->events[((size_t)h->timing_runs * L + l) * 2 * MOE_TIMING_CLASSES];
         hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
     }
@@ -325,7 +325,7 @@ extern "C" moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max
     if (max_runs < 0 || max_runs > 100000) return fail(MOE_ERR_INVALID_ARG, "max_runs %d out of range", max_runs);
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     free_events(h);
-    const size_t n = (size_t)max_runs * h->cfg.num_layers * 4;
+    const size_t n = (size_t)max_runs * h->cfg.num_layers * 2 * MOE_TIMING_CLASSES;
     h->events.reserve(n);
     for (size_t i = 0; i < n; ++i) {
         hipEvent_t e;
@@ -350,11 +350,12 @@ extern "C" moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_ti
     const int L = h->cfg.num_layers;
     for (int r = 0; r < h->timing_runs; ++r) {
         for (int l = 0; l < L; ++l) {
-            hipEvent_t* ev = &h->events[((size_t)r * L + l) * 4];
-            if (hipEventSynchronize(ev[3]) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
+            hipEvent_t* ev = &h->events[((size_t)r * L + l) * 2 * MOE_TIMING_CLASSES];
+            if (hipEventSynchronize(ev[2 * MOE_TIMING_CLASSES - 1]) != hipSuccess)
+                return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
             for (int c = 0; c < MOE_TIMING_CLASSES; ++c) {
                 float ms = 0.0f;
-                if (hipEventElapsedTime(&ms, ev[c], ev[c + 1]) != hipSuccess)
+                if (hipEventElapsedTime(&ms, ev[2 * c], ev[2 * c + 1]) != hipSuccess)
                     return fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
                 out->total_ms[c] += ms;
                 out->launches[c] += 1;

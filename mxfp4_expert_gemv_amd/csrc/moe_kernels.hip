@@ -20,6 +20,7 @@
 // experts); devotd.net "dgx-spark-moe-inference-optimizations" section 2 (MXFP4 = blocked 4-bit
 // float, 4-bit weights with 8-bit activations)).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -491,9 +492,17 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
 
 __device__ __forceinline__ uint64_t max64u(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Top-k of every token (one wave per token: each lane keeps its 8 keys, k rounds of a wave-wide
-// maximum through lane exchanges, the winner's key is cleared), softmax weights over the selected
-// logits, and the list of distinct routed experts, all into LDS; identical in every workgroup.
+__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
+    const uint64_t hi = max64u(a, b), lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+}
+
+// Top-k of every token, one wave per token: each lane sorts its 8 keys (experts lane + 64j) in
+// descending order with Batcher's odd-even merge network; each of the k rounds takes the
+// wave-wide maximum of the lanes' heads through lane exchanges and the winning lane pops its head.
+// Lane r keeps the winner of round r, so the softmax over the selected logits runs across lanes
+// 0..k-1.  Then the list of distinct routed experts; everything lands in LDS.
 template <int T>
 __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids, float* wts) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
@@ -510,39 +519,38 @@ __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids
             const int e = lane + 64 * j;
             key[j] = e < E ? topk_key(lgv[j], e) : 0ull;
         }
+        cx_desc(key[0], key[1]); cx_desc(key[2], key[3]); cx_desc(key[4], key[5]); cx_desc(key[6], key[7]);
+        cx_desc(key[0], key[2]); cx_desc(key[1], key[3]); cx_desc(key[4], key[6]); cx_desc(key[5], key[7]);
+        cx_desc(key[1], key[2]); cx_desc(key[5], key[6]);
+        cx_desc(key[0], key[4]); cx_desc(key[1], key[5]); cx_desc(key[2], key[6]); cx_desc(key[3], key[7]);
+        cx_desc(key[2], key[4]); cx_desc(key[3], key[5]);
+        cx_desc(key[1], key[2]); cx_desc(key[3], key[4]); cx_desc(key[5], key[6]);
+        uint64_t mine = 0ull;
         for (int r = 0; r < k; ++r) {
             uint64_t best = key[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) best = max64u(best, key[j]);
             best = max64u(best, xchg<0>(best));
             best = max64u(best, xchg<1>(best));
             best = max64u(best, xchg<2>(best));
             best = max64u(best, xchg<3>(best));
             best = max64u(best, xchg<4>(best));
             best = max64u(best, xchg<5>(best));
+            const bool win = key[0] == best;  // keys are unique: exactly one lane pops
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (key[j] == best) key[j] = 0ull;  // taken (keys are unique)
-            if (lane == 0) {
-                const uint32_t o = (uint32_t)(best >> 32);
-                ids[t * k + r] = (int)(0xffffffffu - (uint32_t)best);
-                wts[t * k + r] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);  // the logit, for now
-            }
+            for (int j = 0; j < 7; ++j) key[j] = win ? key[j + 1] : key[j];
+            key[7] = win ? 0ull : key[7];
+            mine = lane == r ? best : mine;
         }
-    }
-    __syncthreads();
-    // softmax over the k selected logits of each token (one lane per token)
-    if (tid < T) {
-        float* wt = wts + tid * k;
-        const float m = wt[0];
-        float z = 0.0f;
-        for (int r = 0; r < k; ++r) z += expf(wt[r] - m);
-        float w[kMaxTopK];
-#pragma unroll
-        for (int r = 0; r < kMaxTopK; ++r) w[r] = r < k ? expf(wt[r] - m) / z : 0.0f;
-#pragma unroll
-        for (int r = 0; r < kMaxTopK; ++r)
-            if (r < k) wt[r] = w[r];
+        const uint32_t o = (uint32_t)(mine >> 32);
+        const float lg = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+        const float l0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg)));  // the maximum
+        const float z = lane < k ? expf(lg - l0) : 0.0f;
+        float zs = z + xchg<0>(z);
+        zs += xchg<1>(zs);
+        zs += xchg<2>(zs);  // lanes 0..7 now all hold the sum over lanes 0..7 (k <= 8)
+        if (lane < k) {
+            ids[t * k + lane] = (int)(0xffffffffu - (uint32_t)mine);
+            wts[t * k + lane] = z / zs;
+        }
     }
     __syncthreads();
     // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
@@ -1048,26 +1056,33 @@ hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, c
 
 int routed_slots_max(const Shape& sh, int T) { return T * sh.k < sh.E ? T * sh.k : sh.E; }
 
+// Plain launch, or (timing mode) a launch whose start/stop events carry the kernel's own begin and
+// end timestamps.
+template <typename Kern, typename Args>
+static void launch(Kern kern, unsigned grid, unsigned block, size_t lds, hipStream_t stream, hipEvent_t* ev,
+                   const Args& a) {
+    if (ev)
+        hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), (uint32_t)lds, stream, ev[0], ev[1], 0u, a);
+    else
+        kern<<<grid, block, lds, stream>>>(a);
+}
+
 template <int T, int BPL, int KSUB, int ITERS>
 static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev) {
     const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows(), rtiles = sh.H / R;
-    if (ev) (void)hipEventRecord(ev[0], stream);
-
     const int n_router_wg = (sh.E + GW - 1) / GW;
     K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.trace, P.logits,
               P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, P.ticket, P.slots, P.ids, P.w, sh.H, sh.E, sh.k,
               sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
-    k1_router_shared<T, BPL><<<n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream>>>(a1);
-    if (ev) (void)hipEventRecord(ev[1], stream);
+    launch(k1_router_shared<T, BPL>, n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream, ev, a1);
 
     const int n_gu_wg = routed_slots_max(sh, T) * tiles;
     const int n_sd_wg = sh.S ? (rtiles + GW - 1) / GW : 0;
     K2Args a2{P.slots, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, (const uint4*)L.w2,
               (const uint8_t*)L.w2s, P.h, P.hamax, P.dshared, sh.H, sh.E, sh.k, sh.S, sh.I, n_gu_wg, T};
     const size_t lds2 = (size_t)T * sh.H * 2;
-    k2_gateup<T, BPL, KSUB, ITERS><<<n_gu_wg + n_sd_wg, 64 * GW, lds2, stream>>>(a2);
-    if (ev) (void)hipEventRecord(ev[2], stream);
+    launch(k2_gateup<T, BPL, KSUB, ITERS>, n_gu_wg + n_sd_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
 
     constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 3;
     int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
@@ -1075,8 +1090,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, sh.S ? P.dshared : nullptr,
               P.xnext ? P.x : nullptr, P.xnext, P.y, sh.H, sh.k, sh.S, sh.I};
     const size_t lds3 = (size_t)T * sh.k * sh.I * 2;
-    k3_down<KSUB, ITERS, T, SPW><<<rtiles, 64 * nw, lds3, stream>>>(a3);
-    if (ev) (void)hipEventRecord(ev[3], stream);
+    launch(k3_down<KSUB, ITERS, T, SPW>, rtiles, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
     return hipGetLastError();
 }
 
