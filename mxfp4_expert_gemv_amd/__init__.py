@@ -19,10 +19,12 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_OOM", -5: "MOE_ERR_HIP", -6: "MOE_ERR_NO_DEVICE", -7: "MOE_ERR_STATE"}
 DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
 F_RMSNORM_INPUT = 0x1
+F_DIRECT_LAUNCH = 0x2
+F_THREE_KERNELS = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
-           "moe_decode_destroy", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
+           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
            "moe_status_string", "moe_last_error")
 
 
@@ -58,6 +60,8 @@ class Info(ctypes.Structure):
                 ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
 
 
+# kernel classes of the timing record: three kernels per layer (MOE_F_THREE_KERNELS), or the one
+# whole-pass kernel in class 0 (default)
 TIMING_CLASSES = ("router", "gateup", "down")
 
 
@@ -83,6 +87,7 @@ def lib():
             "moe_decode_run": [vp, vp, i32, ctypes.POINTER(Outputs), vp],
             "moe_decode_query": [vp, ctypes.POINTER(Info)],
             "moe_decode_destroy": [vp],
+            "moe_decode_check": [vp],
             "moe_decode_timing_enable": [vp, i32],
             "moe_decode_timing_read": [vp, ctypes.POINTER(Timing)],
             "fp8_head_create": [i32, i32, Tensor, Tensor, vp, ctypes.POINTER(vp)],
@@ -157,6 +162,11 @@ def moe_decode_query(handle) -> dict:
     return {"variant": info.variant.decode(), "weight_bytes": info.weight_bytes,
             "workspace_bytes": info.workspace_bytes, "bytes_per_layer_t1": info.bytes_per_layer_t1,
             "layers_set": info.layers_set}
+
+
+def moe_decode_check(handle) -> None:
+    """Waits for the device; raises MoeError if a run of this handle was aborted."""
+    _check(lib().moe_decode_check(handle))
 
 
 def moe_decode_destroy(handle) -> None:

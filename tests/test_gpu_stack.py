@@ -10,17 +10,19 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import MANIFEST, DeviceLayer, Y_TOL, create, normwise_err, run_layer
+from gpu_cases import MANIFEST, VARIANTS, DeviceLayer, Y_TOL, create, normwise_err, run_layer, set_variant
 
 pytestmark = pytest.mark.gpu
 
 SAMPLE = (0, 1, 2, 21, 40, 41)
 
 
-@pytest.fixture(scope="module")
-def stack():
+@pytest.fixture(scope="module", params=sorted(VARIANTS))
+def stack(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    print(f"variant {request.param}", flush=True)
+    set_variant(request.param)
     st = MANIFEST["stack"]
     shape, L = synth.FLASH, st["layers"]
     h = create(shape, max_tokens=4, num_layers=L, flags=moe.F_RMSNORM_INPUT)
@@ -31,6 +33,7 @@ def stack():
         torch.cuda.synchronize()
         layers.append((lay.router_host, st["seed"], l))
         del lay
+    set_variant("persistent")
     yield shape, h, layers, st
     moe.moe_decode_destroy(h)
 
