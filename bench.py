@@ -39,7 +39,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
-    ap.add_argument("--variant", choices=("persistent", "three_kernels"), default="persistent",
+    ap.add_argument("--variant", choices=("persistent", "three_kernels"), default="three_kernels",
                     help="kernel set: one persistent kernel per pass (default) or three kernels per layer")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")

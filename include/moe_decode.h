@@ -122,7 +122,7 @@ typedef struct {
     float* topk_w;         /* [L][T][k]: softmax weights of the selected experts */
     void* x_trace;         /* BF16 [L][T][H]: each layer's input residual x_l */
     float* x_scale;        /* FP32 [L][T]: per-token activation scale s_x of each layer */
-    uint8_t* x_codes;      /* E4M3 [L][T][H]: the quantised activation of each layer */
+    uint8_t* x_codes;      /* E4M3 [L][T][H]: the quantised activation of each layer (8-byte aligned) */
 } moe_outputs;
 
 typedef struct {

@@ -364,7 +364,7 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
     moe_outputs o{};
     if (out) o = *out;
     if (o.x_out && (uintptr_t)o.x_out % 4) return fail(MOE_ERR_INVALID_ARG, "x_out not 4-byte aligned");
-    if (o.x_codes && (uintptr_t)o.x_codes % 2) return fail(MOE_ERR_INVALID_ARG, "x_codes not 2-byte aligned");
+    if (o.x_codes && (uintptr_t)o.x_codes % 8) return fail(MOE_ERR_INVALID_ARG, "x_codes not 8-byte aligned");
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     const bool timing = h->timing_runs < h->timing_max_runs;
     if (h->persistent) {

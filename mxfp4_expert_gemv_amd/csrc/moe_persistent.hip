@@ -56,17 +56,37 @@ constexpr int DG = 2;              // gate/up units per prefetch buffer (two buf
 // control words
 constexpr int C_EPOCH = 0, C_ARRIVE = 1, C_ABORT = 2, C_CODE = 3, C_LAYER = 4, C_WG = 5;
 
+// Every device-memory access below goes through global-address-space pointers, so it compiles to
+// global_* instructions, which count only against vmcnt.  (Generic pointers, such as those read
+// from the layer table, would give flat_* instructions, which also count against lgkmcnt: every
+// LDS wait and workgroup barrier would then wait for all weight loads in flight.)
+#define GLOBAL __attribute__((address_space(1)))
+template <typename U>
+__device__ __forceinline__ GLOBAL U* gp(U* p) {
+    return (GLOBAL U*)p;
+}
+template <typename U>
+__device__ __forceinline__ const GLOBAL U* gp(const U* p) {
+    return (const GLOBAL U*)p;
+}
+
+__device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ldg_nt_u8(const uint8_t* p) { return __builtin_nontemporal_load(gp(p)); }
+
 __device__ __forceinline__ uint64_t aload64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t aload32(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void astore64(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void astore32(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t word(float v, uint32_t stamp) {
     return ((uint64_t)stamp << 32) | __float_as_uint(v);
@@ -87,7 +107,9 @@ struct Wait {
 
 // Marks the pass as failed (first failure wins the report) and raises the abort flag.
 __device__ void raise_abort(const Wait& w) {
-    if (atomicCAS(w.ctl + C_CODE, 0u, (uint32_t)w.code) == 0u) {
+    uint32_t expected = 0u;
+    if (__hip_atomic_compare_exchange_strong(gp(w.ctl + C_CODE), &expected, (uint32_t)w.code, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
         astore32(w.ctl + C_LAYER, (uint32_t)w.layer);
         astore32(w.ctl + C_WG, blockIdx.x);
     }
@@ -136,7 +158,7 @@ __device__ __forceinline__ void router_load(const uint16_t* router, int e, int H
     const int NU = H / 8;
     const uint4* p = (const uint4*)(router + (size_t)e * H);
 #pragma unroll
-    for (int j = 0; j < RU; ++j) w[j] = ld_nt(p + min(lane + 64 * j, NU - 1));
+    for (int j = 0; j < RU; ++j) w[j] = ldg_nt(p + min(lane + 64 * j, NU - 1));
 }
 
 template <int T>
@@ -170,23 +192,21 @@ __device__ __forceinline__ void router_dot(const uint4 (&w)[RU], int H, const ui
 // wave's lanes cover the 2 * H/32 MX blocks of the two rows in order (gate blocks, then up).
 struct GuUnit {
     uint4 w[GJ];
-    uint32_t sc;  // scale byte of block j in bits 8j..8j+7
+    uint32_t sc[GJ];  // scale byte of each block (kept apart: combining them would wait for the loads)
 };
 
 __device__ __forceinline__ void gu_load(const uint4* w13, const uint8_t* w13s, int e, int i, int I, int NB,
                                         GuUnit& u, int lane) {
     const size_t r0 = (size_t)e * 2 * I;
-    uint32_t sc = 0;
 #pragma unroll
     for (int j = 0; j < GJ; ++j) {
         const int f = min(lane + 64 * j, 2 * NB - 1);
         const int sel = f >= NB ? 1 : 0;
         const int blk = f - sel * NB;
         const size_t row = r0 + (size_t)(sel ? I + i : i);
-        u.w[j] = ld_nt(w13 + row * NB + blk);
-        sc |= (uint32_t)__builtin_nontemporal_load(w13s + row * NB + blk) << (8 * j);
+        u.w[j] = ldg_nt(w13 + row * NB + blk);
+        u.sc[j] = ldg_nt_u8(w13s + row * NB + blk);
     }
-    u.sc = sc;
 }
 
 // Gate and up sums (without the activation scale) of the nt tokens tok[q]; every lane gets them.
@@ -201,7 +221,7 @@ __device__ __forceinline__ void gu_dot(const GuUnit& u, int NB, const half2_t* x
         if (f < 2 * NB) {
             const bool is_up = f >= NB;
             const int blk = is_up ? f - NB : f;
-            const float scale = e8m0_to_f32(u.sc >> (8 * j));
+            const float scale = e8m0_to_f32(u.sc[j]);
             const half2_t* xp[T];
 #pragma unroll
             for (int q = 0; q < T; ++q) xp[q] = xh + tok[q] * Hh + blk * (kBlock / 2);
@@ -233,7 +253,7 @@ __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + e
 template <int ITERS>
 struct DnPass {
     uint4 w[ITERS];
-    uint32_t sc;
+    uint32_t sc[ITERS];
 };
 
 template <int KSUB, int ITERS>
@@ -241,14 +261,12 @@ __device__ __forceinline__ void dn_load(const uint4* w2, const uint8_t* w2s, int
                                         DnPass<ITERS>& d, int lane) {
     const int ks = lane % KSUB;
     const size_t r = (size_t)e * H + row;
-    uint32_t sc = 0;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const size_t b = r * NI + it * KSUB + ks;
-        d.w[it] = ld_nt(w2 + b);
-        sc |= (uint32_t)__builtin_nontemporal_load(w2s + b) << (8 * it);
+        d.w[it] = ldg_nt(w2 + b);
+        d.sc[it] = ldg_nt_u8(w2s + b);
     }
-    d.sc = sc;
 }
 
 // Row sums of the pass for the nt FP8 h vectors hq + q * Ih (scaled by sh[q]); reduced over the
@@ -261,7 +279,7 @@ __device__ __forceinline__ void dn_dot(const DnPass<ITERS>& d, const half2_t* hq
     for (int q = 0; q < T; ++q) out[q] = 0.0f;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-        const float scale = e8m0_to_f32(d.sc >> (8 * it));
+        const float scale = e8m0_to_f32(d.sc[it]);
         const half2_t* xp[T];
 #pragma unroll
         for (int q = 0; q < T; ++q) xp[q] = hq + q * Ih + (it * KSUB + ks) * (kBlock / 2);
@@ -277,33 +295,34 @@ __device__ __forceinline__ void dn_dot(const DnPass<ITERS>& d, const half2_t* hq
     for (int q = 0; q < T; ++q) out[q] = sum_ksub<KSUB>(out[q]);
 }
 
-// FP8 requantisation of nv vectors of I fp32 values held as polled words v (word i0 + m * NTH of
-// the concatenated vectors): s = max|h| / 448 (1 when h = 0) per vector into scale[], the exact
-// f16 values of the codes into out[vec][I] (LDS, as _Float16).  I is a multiple of 64, so each
-// 64-word chunk belongs to one vector.  cmax: LDS scratch of nv * I / 64 floats.
+// FP8 requantisation of nv vectors of I fp32 values v (value i0 + m * NTH of the concatenated
+// vectors, held by this thread): s = max|h| / 448 (1 when h = 0) per vector (into scale[], LDS, by the
+// first nv threads), the exact f16 values of the codes into out[vec][I] (LDS, as _Float16).  I is
+// a multiple of 64, so each 64-word chunk belongs to one vector.  cmax: LDS scratch of nv * I / 64
+// floats.  One barrier inside; the caller synchronises before reading out or scale.
 template <int M>
-__device__ void requant(const uint64_t (&v)[M], int i0, int nv, int I, float* scale, _Float16* out, float* cmax) {
+__device__ void requant(const float (&v)[M], int i0, int nv, int I, float* scale, _Float16* out, float* cmax) {
     const int lane = i0 & 63, n = nv * I, CH = I / 64;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = i0 + m * NTH;  // uniform chunk per wave: i / 64 is the same for all lanes
-        const float a = i < n ? fabsf(payload(v[m])) : 0.0f;
+        const float a = i < n ? fabsf(v[m]) : 0.0f;
         const float mx = max64(a);
         if (i < n && lane == 0) cmax[i / 64] = mx;
     }
     __syncthreads();
-    if (i0 < nv) {
+    auto scale_of = [&](int vec) {
         float mx = 0.0f;
-        for (int c = 0; c < CH; ++c) mx = fmaxf(mx, cmax[i0 * CH + c]);
-        scale[i0] = mx > 0.0f ? mx / 448.0f : 1.0f;
-    }
-    __syncthreads();
+        for (int c = 0; c < CH; ++c) mx = fmaxf(mx, cmax[vec * CH + c]);
+        return mx > 0.0f ? mx / 448.0f : 1.0f;
+    };
+    if (i0 < nv) scale[i0] = scale_of(i0);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = i0 + m * NTH;
         if (i < n) {
-            const float s = scale[i / I];
-            out[i] = e4m3x2_to_f16x2(e4m3_pack2(payload(v[m]) / s, 0.0f)).x;
+            const float s = scale_of((unsigned)i / (unsigned)I);
+            out[i] = e4m3x2_to_f16x2(e4m3_pack2(v[m] / s, 0.0f)).x;
         }
     }
 }
@@ -398,7 +417,7 @@ struct Sizes {
     static constexpr int MS = (T * 768 + NTH - 1) / NTH;            // shared h: T * I words
     static constexpr int MH = (kMaxTokens * 768 + NTH - 1) / NTH;   // routed h: ntok * I words
     static constexpr int MG = 2;                                    // gathered d: per batch
-    static constexpr int DPM = T <= 2 ? 2 : 3;                      // down passes prefetched per wave
+    static constexpr int DPM = 2;                                   // down passes prefetched per wave
 };
 
 template <int T, int KSUB, int ITERS>
@@ -410,8 +429,6 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
     __shared__ int ids[T * kMaxTopK];
     __shared__ float wts[T * kMaxTopK];
     __shared__ int qs[T * kMaxTopK], qj[T * kMaxTopK];  // (token, rank) -> slot, position in slot
-    __shared__ double redd[NWV * T];
-    __shared__ float redf[NWV * T];
     __shared__ float sx[T], shs[T], rhs[kMaxTokens];
     __shared__ uint32_t s_epoch;
     __shared__ int s_grp[2];  // own slot, its first workgroup
@@ -420,20 +437,32 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         const uint32_t ep = aload32(a.ctl + C_EPOCH);
         const uint32_t ab = aload32(a.ctl + C_ABORT);
         s_epoch = ab ? 0xFFFFFFFFu : ep;  // a raised abort flag makes every later pass exit at once
-        if (!ab) __hip_atomic_fetch_add(a.ctl + C_ARRIVE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!ab) __hip_atomic_fetch_add(gp(a.ctl + C_ARRIVE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t epoch = s_epoch;
     if (epoch == 0xFFFFFFFFu) return;
     const int L = a.L;
     Wait w{a.ctl, a.timeout, 0, 0};
+    // fixed per-workgroup ranges (32-bit arithmetic: every product stays below 2^31)
+    __shared__ int s_rng[6];
+    if (threadIdx.x == 0) {
+        const unsigned c = blockIdx.x, N = gridDim.x;
+        s_rng[0] = (int)(c * (unsigned)a.E / N);                          // router rows [0], [1]
+        s_rng[1] = (int)((c + 1) * (unsigned)a.E / N);
+        s_rng[2] = a.S ? (int)(c * (unsigned)a.I / N) : 0;                // shared SwiGLU outputs [2], [3]
+        s_rng[3] = a.S ? (int)((c + 1) * (unsigned)a.I / N) : 0;
+        s_rng[4] = 2 * (int)(c * (unsigned)(a.H / 2) / N);                // own hidden rows [4], [5]
+        s_rng[5] = 2 * (int)((c + 1) * (unsigned)(a.H / 2) / N);
+    }
+    __syncthreads();
 
     for (int l = 0; l < L; ++l) {
         // Everything below is recomputed per layer from laundered thread and workgroup indices, so
         // the compiler does not hoist per-lane addresses out of the loop and keep them live.
-        int tidv = threadIdx.x, cs = blockIdx.x;
+        int tidv = threadIdx.x;
         asm volatile("" : "+v"(tidv));
-        asm volatile("" : "+s"(cs));
+        const int cs = blockIdx.x;
         const int tid = tidv, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), ks = lane % KSUB;
         const int c = cs, N = gridDim.x;
         const int H = a.H, E = a.E, I = a.I, k = a.k, S = a.S;
@@ -448,10 +477,11 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         float* dsh = (float*)(hqr + kMaxTokens * Ih);         // [T][rmax] shared down output, own rows
         float* dg = dsh + T * a.rmax;                         // [T][k][rmax] gathered routed down outputs
         float* cmax = dg + T * kMaxTopK * a.rmax;             // [kMaxTokens * I / 64] chunk maxima
+        float* hsraw = cmax + kMaxTokens * I / 64;            // [T][I] shared expert's h (fp32)
         // per-workgroup ranges
-        const int eA = (int)((long)c * E / N), eB = (int)((long)(c + 1) * E / N);  // router rows
-        const int iA = S ? (int)((long)c * I / N) : 0, iB = S ? (int)((long)(c + 1) * I / N) : 0;  // shared h
-        const int oA = 2 * (int)((long)c * Hh / N), oB = 2 * (int)((long)(c + 1) * Hh / N);  // own hidden rows
+        const int eA = __builtin_amdgcn_readfirstlane(s_rng[0]), eB = __builtin_amdgcn_readfirstlane(s_rng[1]);
+        const int iA = __builtin_amdgcn_readfirstlane(s_rng[2]), iB = __builtin_amdgcn_readfirstlane(s_rng[3]);
+        const int oA = __builtin_amdgcn_readfirstlane(s_rng[4]), oB = __builtin_amdgcn_readfirstlane(s_rng[5]);
         const int nro = oB - oA;
         const int nr = eB - eA, nu0 = nr + (iB - iA);
         const int sh_passes = S ? (nro + UPW - 1) / UPW : 0;
@@ -479,7 +509,7 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
 
         // ---- round X: the layer input
         if (l == 0) {
-            for (int i = tid; i < T * H / 8; i += NTH) ((uint4*)xr)[i] = ((const uint4*)a.x_in)[i];
+            for (int i = tid; i < T * H / 8; i += NTH) ((u32x4*)xr)[i] = gp((const u32x4*)a.x_in)[i];
         } else {
             const uint64_t* src = a.xw + (size_t)par * kMaxTokens * Hh;
             uint64_t v[Z::MX];
@@ -496,114 +526,90 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         __syncthreads();
         PK_MARK(1);
         if (a.trace) {
-            uint16_t* tr = a.trace + (size_t)l * T * H;
+            GLOBAL uint16_t* tr = gp(a.trace) + (size_t)l * T * H;
             for (int i = tid; i < T * nro; i += NTH) {
                 const int t = i / nro, r = oA + i - t * nro;
                 tr[t * H + r] = xr[t * H + r];
             }
         }
 
-        // ---- MoE input: optional RMSNorm (sum of squares in fp64), per-token FP8 quantisation
+        // ---- MoE input: optional RMSNorm (sum of squares in fp64), per-token FP8 quantisation.
+        // Every wave reduces the whole vector itself, so no workgroup barrier is needed: the
+        // maximum of |bf16(x * r)| is bf16(max|x| * r) because rounding is monotonic.
         {
-            const int NU = H / 8;
-            double ss[T];
-            float mx[T];
+            const int NU = H / 8;  // 16-byte chunks per token
+            double rr[T];
+            float sxv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                ss[t] = 0.0;
-                mx[t] = 0.0f;
-            }
-            if (a.normalize) {
-                for (int i = tid; i < T * NU; i += NTH) {
-                    const int t = i / NU;
-                    const uint4 v = ((const uint4*)xr)[i];
-                    double d = 0.0;
+                double ss = 0.0;
+                float mx = 0.0f;
+                for (int u = lane; u < NU; u += 64) {
+                    const uint4 v = ((const uint4*)(xr + t * H))[u];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const double x0 = (double)bf16_to_f32(comp(v, q)), x1 = (double)bf16_to_f32(comp(v, q) >> 16);
-                        d += x0 * x0 + x1 * x1;
+                        const float x0 = bf16_to_f32(comp(v, q)), x1 = bf16_to_f32(comp(v, q) >> 16);
+                        mx = fmaxf(mx, fmaxf(fabsf(x0), fabsf(x1)));
+                        ss = fma((double)x0, (double)x0, ss);
+                        ss = fma((double)x1, (double)x1, ss);
                     }
-#pragma unroll
-                    for (int tt = 0; tt < T; ++tt)
-                        if (tt == t) ss[tt] += d;
                 }
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const double s = sum64(ss[t]);
-                    if (lane == 0) redd[wv * T + t] = s;
+                mx = max64(mx);
+                double r = 1.0;
+                float mxn = mx;
+                if (a.normalize) {
+                    r = 1.0 / sqrt(sum64(ss) / (double)H + 1e-6);
+                    mxn = bf16_to_f32(f32_to_bf16((float)((double)mx * r)));
                 }
-                __syncthreads();
-                double r[T];
+                rr[t] = r;
+                sxv[t] = mxn > 0.0f ? mxn / 448.0f : 1.0f;
+            }
+            if (tid < T) {
+                float s = sxv[0];
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    double s = 0.0;
-                    for (int q = 0; q < NWV; ++q) s += redd[q * T + t];
-                    r[t] = 1.0 / sqrt(s / (double)H + 1e-6);
-                }
-                for (int i = tid; i < T * NU; i += NTH) {
-                    const int t = i / NU;
-                    double rt = r[0];
+                for (int t = 1; t < T; ++t)
+                    if (tid == t) s = sxv[t];
+                sx[tid] = s;
+                if (a.x_scale && c == 0) gp(a.x_scale)[(size_t)l * T + tid] = s;
+            }
+            for (int i = tid; i < T * NU; i += NTH) {
+                int t = 0;
 #pragma unroll
-                    for (int tt = 1; tt < T; ++tt)
-                        if (tt == t) rt = r[tt];
-                    const uint4 v = ((const uint4*)xr)[i];
+                for (int tt = 1; tt < T; ++tt) t += i >= tt * NU ? 1 : 0;
+                double r = rr[0];
+                float sv = sxv[0];
+#pragma unroll
+                for (int tt = 1; tt < T; ++tt)
+                    if (t == tt) {
+                        r = rr[tt];
+                        sv = sxv[tt];
+                    }
+                uint4 v = ((const uint4*)xr)[i];
+                if (a.normalize) {
                     uint32_t o[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const uint32_t d = comp(v, q);
-                        const uint32_t lo = f32_to_bf16((float)((double)bf16_to_f32(d) * rt));
-                        const uint32_t hi = f32_to_bf16((float)((double)bf16_to_f32(d >> 16) * rt));
+                        const uint32_t lo = f32_to_bf16((float)((double)bf16_to_f32(d) * r));
+                        const uint32_t hi = f32_to_bf16((float)((double)bf16_to_f32(d >> 16) * r));
                         o[q] = lo | (hi << 16);
                     }
-                    ((uint4*)xn)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+                    v = make_uint4(o[0], o[1], o[2], o[3]);
                 }
-            } else {
-                for (int i = tid; i < T * NU; i += NTH) ((uint4*)xn)[i] = ((const uint4*)xr)[i];
-            }
-            __syncthreads();
-            for (int i = tid; i < T * NU; i += NTH) {
-                const int t = i / NU;
-                const uint4 v = ((const uint4*)xn)[i];
-                float m = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(comp(v, q))), fabsf(bf16_to_f32(comp(v, q) >> 16))));
-#pragma unroll
-                for (int tt = 0; tt < T; ++tt)
-                    if (tt == t) mx[tt] = fmaxf(mx[tt], m);
-            }
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const float m = max64(mx[t]);
-                if (lane == 0) redf[wv * T + t] = m;
-            }
-            __syncthreads();
-            if (tid < T) {
-                float m = 0.0f;
-                for (int q = 0; q < NWV; ++q) m = fmaxf(m, redf[q * T + tid]);
-                const float s = m > 0.0f ? m / 448.0f : 1.0f;
-                sx[tid] = s;
-                if (a.x_scale && c == 0) a.x_scale[(size_t)l * T + tid] = s;
-            }
-            __syncthreads();
-            for (int i = tid; i < T * NU; i += NTH) {
-                const int t = i / NU;
-                const float s = sx[t];
-                const uint4 v = ((const uint4*)xn)[i];
+                ((uint4*)xn)[i] = v;
                 uint32_t cd[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t d = comp(v, q);
-                    cd[q] = e4m3_pack2(bf16_to_f32(d) / s, bf16_to_f32(d >> 16) / s);
+                    cd[q] = e4m3_pack2(bf16_to_f32(d) / sv, bf16_to_f32(d >> 16) / sv);
                     xh[i * 4 + q] = e4m3x2_to_f16x2(cd[q]);
                 }
                 if (a.x_codes && c == 0)
-                    *(uint2*)(a.x_codes + (size_t)l * T * H + (size_t)i * 8) =
-                        make_uint2(cd[0] | (cd[1] << 16), cd[2] | (cd[3] << 16));
+                    *(GLOBAL uint64_t*)(gp(a.x_codes) + (size_t)l * T * H + (size_t)i * 8) =
+                        (uint64_t)(cd[0] | (cd[1] << 16)) | ((uint64_t)(cd[2] | (cd[3] << 16)) << 32);
             }
             __syncthreads();
         }
-
         PK_MARK(2);
         // ---- router rows and shared-expert gate/up units, published (round R)
         for (int u = wv; u < nu0; u += NWV) {
@@ -652,20 +658,26 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
                 const int i = tid + m * NTH;
                 if (i < T * E) lg[i] = payload(vl[m]);
             }
-            if (S) requant<Z::MS>(vs, tid, T, I, shs, (_Float16*)hqs, cmax);
+            if (S) {
+#pragma unroll
+                for (int m = 0; m < Z::MS; ++m) {
+                    const int i = tid + m * NTH;
+                    if (i < T * I) hsraw[i] = payload(vs[m]);
+                }
+            }
             __syncthreads();
             route_lds<T>(lg, E, k, &st, ids, wts, tid);
         }
         const int D = st.n;
         if (c == 0) {
             for (int i = tid; i < T * k; i += NTH) {
-                if (a.ids_out) a.ids_out[(size_t)l * T * k + i] = ids[i];
-                if (a.w_out) a.w_out[(size_t)l * T * k + i] = wts[i];
+                if (a.ids_out) gp(a.ids_out)[(size_t)l * T * k + i] = ids[i];
+                if (a.w_out) gp(a.w_out)[(size_t)l * T * k + i] = wts[i];
             }
         }
         if (tid < kMaxSlots) {  // own slot group: slot s owns workgroups [s*N/D, (s+1)*N/D)
             const int s = tid;
-            const int gA = (int)((long)s * N / D), gB = (int)((long)(s + 1) * N / D);
+            const int gA = (int)((unsigned)(s * N) / (unsigned)D), gB = (int)((unsigned)((s + 1) * N) / (unsigned)D);
             if (s < D && c >= gA && c < gB) {
                 s_grp[0] = s;
                 s_grp[1] = gA;
@@ -681,13 +693,13 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         }
         __syncthreads();
         const int ms = s_grp[0];
-        const int ns = (int)((long)(ms + 1) * N / D) - s_grp[1], cc = c - s_grp[1];
+        const int ns = (int)((unsigned)((ms + 1) * N) / (unsigned)D) - s_grp[1], cc = c - s_grp[1];
         const int me = st.expert[ms], mnt = st.ntok[ms];
         int mtok[T];
 #pragma unroll
         for (int q = 0; q < T; ++q) mtok[q] = q < mnt ? st.tok[ms][q] : 0;
-        const int hA = (int)((long)cc * I / ns), hB = (int)((long)(cc + 1) * I / ns);
-        const int dA = (int)((long)cc * H / ns), dB = (int)((long)(cc + 1) * H / ns);
+        const int hA = (int)((unsigned)(cc * I) / (unsigned)ns), hB = (int)((unsigned)((cc + 1) * I) / (unsigned)ns);
+        const int dA = (int)((unsigned)(cc * H) / (unsigned)ns), dB = (int)((unsigned)((cc + 1) * H) / (unsigned)ns);
         const int nd = dB - dA, rd_passes = (nd + UPW - 1) / UPW;
 
         PK_MARK(5);
@@ -708,6 +720,27 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             dn_load<KSUB, ITERS>(w2, w2s, me, dA + min(g * UPW + lane / KSUB, max(nd - 1, 0)), H, NI, dp[m], lane);
         }
 
+        // ---- shared expert: FP8 requantisation of its h, its down rows (own rows, every token) into
+        // LDS, while the routed weights are in flight
+        if (S) {
+            float hv[Z::MS];
+#pragma unroll
+            for (int m = 0; m < Z::MS; ++m) hv[m] = hsraw[min(tid + m * NTH, T * I - 1)];
+            requant<Z::MS>(hv, tid, T, I, shs, (_Float16*)hqs, cmax);
+            __syncthreads();
+        }
+        for (int g = wv; g < sh_passes; g += NWV) {
+            if (g != wv) dn_load<KSUB, ITERS>(w2, w2s, E, oA + min(g * UPW + lane / KSUB, nro - 1), H, NI, psd, lane);
+            float o[T];
+            dn_dot<KSUB, ITERS, T>(psd, hqs, Ih, T, o, lane);
+            const int v = g * UPW + lane / KSUB;
+            if (ks == 0 && v < nro) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) dsh[t * a.rmax + v] = o[t] * shs[t];
+            }
+        }
+
+        PK_MARK(6);
         // ---- routed gate/up: compute from one buffer while the other is in flight
         auto gu_unit = [&](const GuUnit& u, int m) {
             float g[T], up[T];
@@ -736,19 +769,6 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             }
         }
 
-        PK_MARK(6);
-        // ---- shared expert's down rows (own rows, every token), kept in LDS
-        for (int g = wv; g < sh_passes; g += NWV) {
-            if (g != wv) dn_load<KSUB, ITERS>(w2, w2s, E, oA + min(g * UPW + lane / KSUB, nro - 1), H, NI, psd, lane);
-            float o[T];
-            dn_dot<KSUB, ITERS, T>(psd, hqs, Ih, T, o, lane);
-            const int v = g * UPW + lane / KSUB;
-            if (ks == 0 && v < nro) {
-#pragma unroll
-                for (int t = 0; t < T; ++t) dsh[t * a.rmax + v] = o[t] * shs[t];
-            }
-        }
-
         PK_MARK(7);
         // ---- round H: own expert's h, FP8 requantisation
         {
@@ -759,7 +779,10 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             const bool ok = poll_wait<Z::MH>(src, tid, mnt * I, stamp, v, w);
             if (__syncthreads_or(!ok)) return;
             PK_MARK(8);
-            requant<Z::MH>(v, tid, mnt, I, rhs, (_Float16*)hqr, cmax);
+            float hv[Z::MH];
+#pragma unroll
+            for (int m = 0; m < Z::MH; ++m) hv[m] = payload(v[m]);
+            requant<Z::MH>(hv, tid, mnt, I, rhs, (_Float16*)hqr, cmax);
             __syncthreads();
         }
 
@@ -851,11 +874,11 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
                     if (S) y += dsh[t * a.rmax + v];
                     const int row = oA + v;
                     xb[h] = f32_to_bf16(bf16_to_f32(xr[t * H + row]) + y);
-                    if (last && a.y) a.y[(size_t)t * H + row] = y;
+                    if (last && a.y) gp(a.y)[(size_t)t * H + row] = y;
                 }
                 const uint32_t pairv = xb[0] | (xb[1] << 16);
                 if (!last) astore64(xdst + (size_t)t * Hh + (oA + v0) / 2, ((uint64_t)nstamp << 32) | pairv);
-                else if (a.x_out) *(uint32_t*)(a.x_out + (size_t)t * H + oA + v0) = pairv;
+                else if (a.x_out) *(GLOBAL uint32_t*)(gp(a.x_out) + (size_t)t * H + oA + v0) = pairv;
             }
         }
         PK_MARK(11);
@@ -890,7 +913,7 @@ size_t lds_bytes(const Shape& sh, int T, int rmax) {
     const size_t H = sh.H, E = sh.E, I = sh.I;
     return (size_t)T * H * 2 * 2 + (size_t)T * H * 2 + (size_t)T * ((E + 3) & ~3) * 4 + (size_t)T * I * 2 +
            (size_t)kMaxTokens * I * 2 + (size_t)T * rmax * 4 + (size_t)T * kMaxTopK * rmax * 4 +
-           (size_t)kMaxTokens * I / 64 * 4;
+           (size_t)kMaxTokens * I / 64 * 4 + (size_t)T * I * 4;
 }
 
 int grid_size(const Shape& sh, int cus) {
