@@ -56,6 +56,9 @@ struct moe_decode_handle {
     float* h;
     float* hamax;
     float* dshared;
+    uint16_t* xn;
+    uint8_t* hq;
+    float* hs;
     // captured launch sequences of whole runs, keyed by their arguments
     struct GraphEntry {
         const void* x;
@@ -182,6 +185,9 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     const uint64_t o_h = o; o += align256((uint64_t)sh.pairs(T) * sh.I * 4);
     const uint64_t o_ham = o; o += align256((uint64_t)sh.pairs(T) * sh.gu_tiles() * 4);
     const uint64_t o_ds = o; o += align256((uint64_t)T * sh.H * 4);
+    const uint64_t o_xn = o; o += align256((uint64_t)T * sh.H * 2);
+    const uint64_t o_hq = o; o += align256((uint64_t)sh.pairs(T) * sh.I);
+    const uint64_t o_hs = o; o += align256((uint64_t)sh.pairs(T) * 4);
     // persistent kernel: exchange buffers, control words, per-layer pointer table
     const uint64_t o_xw = o; o += align256(moe::pk::xw_bytes(sh));
     const uint64_t o_lw = o; o += align256(moe::pk::lw_bytes(sh));
@@ -214,6 +220,9 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->h = (float*)(h->ws + o_h);
     h->hamax = (float*)(h->ws + o_ham);
     h->dshared = (float*)(h->ws + o_ds);
+    h->xn = (uint16_t*)(h->ws + o_xn);
+    h->hq = h->ws + o_hq;
+    h->hs = (float*)(h->ws + o_hs);
     h->persistent = (cfg->flags & MOE_F_THREE_KERNELS) == 0;
     if (h->persistent) {
         int cus = 0, clock_khz = 0;
@@ -342,6 +351,9 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
         p.h = h->h;
         p.hamax = h->hamax;
         p.dshared = h->dshared;
+        p.xn = h->xn;
+        p.hq = h->hq;
+        p.hs = h->hs;
         hipEvent_t* ev = nullptr;
         if (timing) ev = &h->events[((size_t)h->timing_runs * L + l) * 2 * MOE_TIMING_CLASSES];
         hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev);

@@ -234,6 +234,128 @@ __device__ void quantize_input(const uint16_t* xb, int H, half2_t* xh, float* wm
     __syncthreads();
 }
 
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The MoE input of one layer, computed once per layer by one workgroup: x_in = x, or
+// bf16(fl32(x * r)) with r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64 (sum of squares in
+// fp64); its per-token FP8 quantisation s = max|x_in| / 448 (1 when x_in = 0), codes = RNE(x_in / s).
+// The maximum of |x_in| is bf16(max|x| * r) because rounding is monotonic.  x is read with
+// device-scope loads (other workgroups of the same kernel may have just written it), staged in
+// LDS xb[T][H].  Writes x_in (bf16) to xn, the codes to xq, the scales to xs, and the optional
+// per-layer copies (trace: x itself; x_scale; x_codes).
+template <int T>
+__device__ void norm_quant(const uint16_t* x, int H, bool normalize, uint16_t* xb, uint16_t* xn, uint8_t* xq,
+                           float* xs, uint16_t* trace, float* x_scale, uint8_t* x_codes, double* redd, float* redf) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, nth = blockDim.x;
+    const int NQ = H / 4;  // 4-element quads per token
+    double ss[T];
+    float mx[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        ss[t] = 0.0;
+        mx[t] = 0.0f;
+    }
+    for (int i = tid; i < T * NQ; i += nth) {
+        int t = 0;
+#pragma unroll
+        for (int tt = 1; tt < T; ++tt) t += i >= tt * NQ ? 1 : 0;
+        const uint64_t v = ld_agent64((const uint64_t*)x + i);
+        ((uint64_t*)xb)[i] = v;
+        if (trace) ((uint64_t*)trace)[i] = v;
+        double d = 0.0;
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float xv = bf16_to_f32((uint32_t)(v >> (16 * q)));
+            m = fmaxf(m, fabsf(xv));
+            d = fma((double)xv, (double)xv, d);
+        }
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+            if (tt == t) {
+                ss[tt] += d;
+                mx[tt] = fmaxf(mx[tt], m);
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const double sv = normalize ? sum64(ss[t]) : 0.0;
+        const float mv = max64(mx[t]);
+        if (lane == 0) {
+            redd[wv * T + t] = sv;
+            redf[wv * T + t] = mv;
+        }
+    }
+    __syncthreads();
+    double rr[T];
+    float sxv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        double sv = 0.0;
+        float mv = 0.0f;
+        for (int q = 0; q < NW; ++q) {
+            sv += redd[q * T + t];
+            mv = fmaxf(mv, redf[q * T + t]);
+        }
+        double r = 1.0;
+        if (normalize) {
+            r = 1.0 / sqrt(sv / (double)H + 1e-6);
+            mv = bf16_to_f32(f32_to_bf16((float)((double)mv * r)));
+        }
+        rr[t] = r;
+        sxv[t] = mv > 0.0f ? mv / 448.0f : 1.0f;
+    }
+    if (tid < T) {
+        float sv = sxv[0];
+#pragma unroll
+        for (int t = 1; t < T; ++t)
+            if (tid == t) sv = sxv[t];
+        xs[tid] = sv;
+        if (x_scale) x_scale[tid] = sv;
+    }
+    for (int i = tid; i < T * NQ; i += nth) {
+        int t = 0;
+#pragma unroll
+        for (int tt = 1; tt < T; ++tt) t += i >= tt * NQ ? 1 : 0;
+        double r = rr[0];
+        float sv = sxv[0];
+#pragma unroll
+        for (int tt = 1; tt < T; ++tt)
+            if (t == tt) {
+                r = rr[tt];
+                sv = sxv[tt];
+            }
+        uint2 v = ((const uint2*)xb)[i];
+        if (normalize) {
+            uint32_t o[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t d = q ? v.y : v.x;
+                const uint32_t lo = f32_to_bf16((float)((double)bf16_to_f32(d) * r));
+                const uint32_t hi = f32_to_bf16((float)((double)bf16_to_f32(d >> 16) * r));
+                o[q] = lo | (hi << 16);
+            }
+            v = make_uint2(o[0], o[1]);
+        }
+        ((uint2*)xn)[i] = v;
+        const uint32_t c0 = e4m3_pack2(bf16_to_f32(v.x) / sv, bf16_to_f32(v.x >> 16) / sv);
+        const uint32_t c1 = e4m3_pack2(bf16_to_f32(v.y) / sv, bf16_to_f32(v.y >> 16) / sv);
+        ((uint32_t*)xq)[i] = c0 | (c1 << 16);
+        if (x_codes) ((uint32_t*)x_codes)[i] = c0 | (c1 << 16);
+    }
+}
+
 template <int BPL>
 struct GuLoads {
     uint4 w[BPL];
@@ -340,10 +462,11 @@ __device__ void requant_scales(const float* hamax, int tiles, const int* pairs, 
 }
 
 // Top-k of every token, one wave per token: each lane sorts its 8 keys (experts lane + 64j) in
-// descending order with Batcher's odd-even merge network; each of the k rounds takes the
-// wave-wide maximum of the lanes' heads through lane exchanges and the winning lane pops its head.
-// Lane r keeps the winner of round r, so the softmax over the selected logits runs across lanes
-// 0..k-1.  Then the list of distinct routed experts; everything lands in LDS.
+// descending order; each of the k rounds takes the wave-wide maximum of the lanes' heads through
+// lane exchanges and the winning lane pops its head.  Lane r keeps the winner of round r, so the
+// softmax over the selected logits runs across lanes 0..k-1.  (A six-level bitonic merge tree
+// across lanes measured slower: a single wave is bound by its instruction count.)  Then the
+// list of distinct routed experts; everything lands in LDS.
 template <int T>
 __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids, float* wts) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
@@ -395,7 +518,16 @@ __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids
     }
     __syncthreads();
     // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
-    if (wv == 0) {
+    if (T == 1) {  // one token: its k experts are distinct, slot r is rank r
+        if (tid < k) {
+            st->expert[tid] = ids[tid];
+            st->ntok[tid] = 1;
+            st->tok[tid][0] = 0;
+            st->rank[tid][0] = tid;
+            st->w[tid][0] = wts[tid];
+        }
+        if (tid == 0) st->n = k;
+    } else if (wv == 0) {
         const int np = T * k, p = lane;
         const bool valid = p < np;
         const int e = valid ? ids[p] : -1;
@@ -424,6 +556,73 @@ __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids
 }
 
 // ------------------------------------------------------------------------------------------------
+// 3-4 tokens: the layer's MoE input once per layer (k0), and the FP8 requantisation of every
+// routed h vector once per layer (kq) instead of in every down workgroup
+// ------------------------------------------------------------------------------------------------
+
+struct K0Args {
+    const uint16_t* x;  // [T][H] residual x_l
+    uint16_t* xn;       // [T][H] MoE input (bf16)
+    uint8_t* xq;        // [T][H] its FP8 codes
+    float* xs;          // [T] their scales
+    uint16_t* trace;    // [T][H] or null
+    float* x_scale;     // [T] or null
+    uint8_t* x_codes;   // [T][H] or null
+    int H, normalize;
+};
+
+template <int T>
+__global__ __launch_bounds__(1024) void k0_input(K0Args a) {
+    extern __shared__ uint4 smem0[];
+    __shared__ double redd[16 * T];
+    __shared__ float redf[16 * T];
+    norm_quant<T>(a.x, a.H, a.normalize != 0, (uint16_t*)smem0, a.xn, a.xq, a.xs, a.trace, a.x_scale, a.x_codes,
+                  redd, redf);
+}
+
+struct KQArgs {
+    const float* h;      // [pairs][I]
+    const float* hamax;  // [pairs][I/16]
+    uint8_t* hq;         // [pairs][I] FP8 codes
+    float* hs;           // [pairs] scales
+    int I, k, S;
+};
+
+// One workgroup per routed (token, rank) pair p = t*k + r (h row t*(k+S) + r): s_h = max|h| / 448
+// (1 when h = 0) from the tile maxima, codes = RNE(h / s_h).
+__global__ __launch_bounds__(256) void kq_requant(KQArgs a) {
+    __shared__ float s;
+    const int p = blockIdx.x, t = p / a.k, row = p + t * a.S, tid = threadIdx.x, lane = tid & 63;
+    const int I = a.I, tiles = I / kGuOut, Ih = I / 2;
+    float2 v[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int q = tid + c * 256;
+        if (q < Ih) v[c] = *(const float2*)(a.h + (size_t)row * I + 2 * q);
+    }
+    if (tid < 64) {
+        float m = 0.0f;
+        for (int tl = lane; tl < tiles; tl += 64) m = fmaxf(m, a.hamax[(size_t)row * tiles + tl]);
+        m = max64(m);
+        if (lane == 0) {
+            s = m > 0.0f ? m / 448.0f : 1.0f;
+            a.hs[row] = s;
+        }
+    }
+    __syncthreads();
+    const float sv = s;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int q = tid + c * 256;
+        if (q < Ih) ((uint16_t*)(a.hq + (size_t)row * I))[q] = (uint16_t)e4m3_pack2(v[c].x / sv, v[c].y / sv);
+    }
+    for (int q = tid + 512; q < Ih; q += 256) {  // wider expert widths
+        const float2 w = *(const float2*)(a.h + (size_t)row * I + 2 * q);
+        ((uint16_t*)(a.hq + (size_t)row * I))[q] = (uint16_t)e4m3_pack2(w.x / sv, w.y / sv);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // k1: router rows + shared expert gate/up tiles (+ the FP8 codes of the input, stored once)
 // ------------------------------------------------------------------------------------------------
 
@@ -432,6 +631,7 @@ struct K1Args {
     const uint4* w13;        // repacked codes (expert E = shared)
     const uint8_t* w13s;
     const uint16_t* x;       // [T][H] residual x_l (or the MoE input)
+    const uint16_t* xn;      // [T][H] MoE input computed by the input kernel (3-4 tokens), else unused
     uint16_t* trace;         // [T][H] copy of x, or null (workgroup 0)
     float* logits;           // [T][E]
     uint8_t* xq;             // [T][H] FP8 codes of the MoE input (one workgroup stores them)
@@ -466,6 +666,9 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
     const bool is_router = (int)blockIdx.x < a.n_router_wg;
     // the workgroup that publishes the input's FP8 codes: shared tile 0, or router 0 without a shared expert
     const bool publish = a.S ? (int)blockIdx.x == a.n_router_wg : blockIdx.x == 0;
+    // 3-4 tokens: the MoE input and its codes come from the input kernel (once per layer) instead of
+    // being recomputed by every workgroup (its fp64 work grows with the token count)
+    constexpr bool CENTRAL = T >= 3;
 
     if (is_router) {
         // one expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row
@@ -477,11 +680,16 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
 #pragma unroll
             for (int j = 0; j < kMaxWaves; ++j) wr[j] = ld_nt(p + min(lane + 64 * j, NU - 1));
         }
-        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
-        if (blockIdx.x == 0 && a.trace) {
-            for (int i = tid; i < T * H / 8; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
+        if constexpr (CENTRAL) {
+            for (int i = tid; i < T * NU; i += blockDim.x) ((uint4*)xb)[i] = ((const uint4*)a.xn)[i];
+            __syncthreads();
+        } else {
+            moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
+            if (blockIdx.x == 0 && a.trace) {
+                for (int i = tid; i < T * H / 8; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
+            }
+            if (publish) quantize_input<T>(xb, H, xh, wmax, sx, a.xq, a.xs, a.x_codes_out, a.x_scale_out);
         }
-        if (publish) quantize_input<T>(xb, H, xh, wmax, sx, a.xq, a.xs, a.x_codes_out, a.x_scale_out);
         if (e < a.E) {
             float acc[T];
 #pragma unroll
@@ -532,9 +740,22 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
         const int tile = blockIdx.x - a.n_router_wg, tiles = a.I / kGuOut;
         GuLoads<BPL> L;
         L.issue(a.w13, a.w13s, a.E, tile, tiles, NW);
-        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
-        quantize_input<T>(xb, H, xh, wmax, sx, publish ? a.xq : nullptr, publish ? a.xs : nullptr,
-                          publish ? a.x_codes_out : nullptr, publish ? a.x_scale_out : nullptr);
+        if constexpr (CENTRAL) {
+            if (tid < T) sx[tid] = a.xs[tid];
+            for (int i = tid; i < T * H / 8; i += blockDim.x) {
+                const uint2 c = *(const uint2*)(a.xq + (size_t)i * 8);
+                half2_t* o = xh + i * 4;
+                o[0] = e4m3x2_to_f16x2(c.x & 0xffffu);
+                o[1] = e4m3x2_to_f16x2(c.x >> 16);
+                o[2] = e4m3x2_to_f16x2(c.y & 0xffffu);
+                o[3] = e4m3x2_to_f16x2(c.y >> 16);
+            }
+            __syncthreads();
+        } else {
+            moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
+            quantize_input<T>(xb, H, xh, wmax, sx, publish ? a.xq : nullptr, publish ? a.xs : nullptr,
+                              publish ? a.x_codes_out : nullptr, publish ? a.x_scale_out : nullptr);
+        }
         int tok[T], pair[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) {
@@ -696,6 +917,8 @@ struct K3Args {
     const uint8_t* w2s;
     const float* h;          // [pairs][I]
     const float* hamax;      // [pairs][I/16]
+    const uint8_t* hq;       // [pairs][I] FP8 codes of h (3-4 tokens: from the requantisation kernel)
+    const float* hs;         // [pairs] their scales
     const float* dshared;    // [T][H] or null (no shared expert)
     const uint16_t* xres;    // [T][H] residual x_l, or null
     uint16_t* xnext;         // [T][H] bf16(x_l + y), or null
@@ -706,7 +929,8 @@ struct K3Args {
 template <int KSUB, int ITERS, int T, int SPW>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     constexpr int R = kWave / KSUB;
-    constexpr int MAXP = T == 1 ? 8 : T == 3 ? 12 : 16;  // h columns (pairs) per thread, loaded up front
+    constexpr bool CODES = T >= 3;  // FP8 h codes from the requantisation kernel
+    constexpr int MAXP = CODES ? 1 : T == 1 ? 8 : 16;  // h columns (pairs) per thread, loaded up front
     extern __shared__ uint4 smem3[];
     half2_t* hh = (half2_t*)smem3;  // [T*k][I/2], routed pair t*k + r
     __shared__ float s_h[kMaxTokens * kMaxTopK];
@@ -726,7 +950,7 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     const uint16_t xr_pre = a.xnext ? a.xres[oo] : (uint16_t)0;
     // thread -> (column pair q, pair group g); G groups cover the pairs g, g + G, ...
     const int G = nth / Ih, q0 = tid % Ih, g0 = tid / Ih;
-    const bool loader = G > 0 && g0 < G;
+    const bool loader = !CODES && G > 0 && g0 < G;
 
     // 1. independent loads: slot list, h of every routed pair (first MAXV * nth values)
     const SlotTable* st = a.slots;
@@ -786,7 +1010,22 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         }
     }
 
-    // 3. FP8 requantisation of every routed (token, rank) h vector into LDS
+    // 3. FP8 requantisation of every routed (token, rank) h vector into LDS (or its codes)
+    if constexpr (CODES) {
+        const int I16 = I / 16;
+        for (int i = tid; i < npairs * I16; i += nth) {
+            const int p = (unsigned)i / (unsigned)I16, c = i - p * I16;
+            const uint4 cw = *(const uint4*)(a.hq + (size_t)(p + (p / k) * a.S) * I + c * 16);
+            half2_t* o = hh + p * Ih + c * 8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o[2 * q] = e4m3x2_to_f16x2(comp(cw, q) & 0xffffu);
+                o[2 * q + 1] = e4m3x2_to_f16x2(comp(cw, q) >> 16);
+            }
+        }
+        if (tid < npairs) s_h[tid] = a.hs[s_pair[tid]];
+        __syncthreads();
+    } else {
     requant_scales(a.hamax, tiles, s_pair, npairs, s_h);
     if (loader) {
 #pragma unroll
@@ -803,6 +1042,7 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         hh[p * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / s_h[p], v.y / s_h[p]));
     }
     __syncthreads();
+    }
 
     // 4. block dot products, routing-weighted into per-token accumulators
     float acc[T];
@@ -912,8 +1152,13 @@ template <int T, int BPL, int KSUB, int ITERS>
 static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev) {
     const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows(), rtiles = sh.H / R;
+    constexpr bool CENTRAL = T >= 3;  // input and h requantisation once per layer (k0, kq)
+    if (CENTRAL) {
+        K0Args a0{P.x, P.xn, P.xq, P.xs, P.trace, P.x_scale, P.x_codes, sh.H, normalize ? 1 : 0};
+        k0_input<T><<<1, 1024, (size_t)T * sh.H * 2, stream>>>(a0);
+    }
     const int n_router_wg = (sh.E + GW - 1) / GW;
-    K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.trace, P.logits,
+    K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.xn, P.trace, P.logits,
               P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, P.ticket, P.slots, P.ids, P.w, sh.H, sh.E, sh.k,
               sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
     launch(k1_router_shared<T, BPL>, n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream, ev, a1);
@@ -925,10 +1170,13 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     const size_t lds2 = (size_t)T * sh.H * 2;
     launch(k2_gateup<T, BPL, KSUB, ITERS>, n_gu_wg + n_sd_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
 
-    constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 3;
-    int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
-    if (T >= 3 && nw < 12 && sh.I / 2 * 2 <= 64 * 12) nw = 12;  // two pair groups of h columns per thread block
-    K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, sh.S ? P.dshared : nullptr,
+    if (CENTRAL) {
+        KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I, sh.k, sh.S};
+        kq_requant<<<T * sh.k, 256, 0, stream>>>(aq);
+    }
+    constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 4;  // 3-4 tokens: 8 waves, two workgroups per CU
+    const int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
+    K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, P.hq, P.hs, sh.S ? P.dshared : nullptr,
               P.xnext ? P.x : nullptr, P.xnext, P.y, sh.H, sh.k, sh.S, sh.I};
     const size_t lds3 = (size_t)T * sh.k * sh.I * 2;
     launch(k3_down<KSUB, ITERS, T, SPW>, rtiles, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);

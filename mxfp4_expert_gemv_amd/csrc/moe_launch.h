@@ -30,6 +30,10 @@ struct RunPtrs {
     float* h;           // [T*(k+S)][I]
     float* hamax;       // [T*(k+S)][I/16]
     float* dshared;     // [T][H] shared expert output
+    // 3-4 tokens: the layer's MoE input and the routed h codes, computed once per layer
+    uint16_t* xn;       // [T][H] MoE input (bf16)
+    uint8_t* hq;        // [T*(k+S)][I] FP8 codes of h
+    float* hs;          // [T*(k+S)] their scales
 };
 
 hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,

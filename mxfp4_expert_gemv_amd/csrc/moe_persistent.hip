@@ -302,26 +302,26 @@ __device__ __forceinline__ void dn_dot(const DnPass<ITERS>& d, const half2_t* hq
 // floats.  One barrier inside; the caller synchronises before reading out or scale.
 template <int M>
 __device__ void requant(const float (&v)[M], int i0, int nv, int I, float* scale, _Float16* out, float* cmax) {
-    const int lane = i0 & 63, n = nv * I, CH = I / 64;
+    const int lane = i0 & 63, n = nv * I, CH = I / 64;  // CH <= 16
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = i0 + m * NTH;  // uniform chunk per wave: i / 64 is the same for all lanes
-        const float a = i < n ? fabsf(v[m]) : 0.0f;
-        const float mx = max64(a);
-        if (i < n && lane == 0) cmax[i / 64] = mx;
+        if (i - lane < n) {
+            const float mx = max64(fabsf(v[m]));
+            if (lane == 0) cmax[i / 64] = mx;
+        }
     }
     __syncthreads();
-    auto scale_of = [&](int vec) {
-        float mx = 0.0f;
-        for (int c = 0; c < CH; ++c) mx = fmaxf(mx, cmax[vec * CH + c]);
-        return mx > 0.0f ? mx / 448.0f : 1.0f;
-    };
-    if (i0 < nv) scale[i0] = scale_of(i0);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = i0 + m * NTH;
-        if (i < n) {
-            const float s = scale_of((unsigned)i / (unsigned)I);
+        if (i - lane < n) {  // uniform per wave
+            const int vec = (unsigned)i / (unsigned)I;
+            float cm = lane < CH ? cmax[vec * CH + lane] : 0.0f;
+            cm = max16(cm);
+            const float mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cm)));
+            const float s = mx > 0.0f ? mx / 448.0f : 1.0f;
+            if (lane == 0 && (unsigned)(i - lane) % (unsigned)I == 0u) scale[vec] = s;
             out[i] = e4m3x2_to_f16x2(e4m3_pack2(v[m] / s, 0.0f)).x;
         }
     }
@@ -377,7 +377,16 @@ __device__ void route_lds(const float* lg, int E, int k, SlotTable* st, int* ids
         }
     }
     __syncthreads();
-    if (wv == 0) {
+    if (T == 1) {  // one token: its k experts are distinct, slot r is rank r
+        if (tid < k) {
+            st->expert[tid] = ids[tid];
+            st->ntok[tid] = 1;
+            st->tok[tid][0] = 0;
+            st->rank[tid][0] = tid;
+            st->w[tid][0] = wts[tid];
+        }
+        if (tid == 0) st->n = k;
+    } else if (wv == 0) {
         const int np = T * k, p = lane;
         const bool valid = p < np;
         const int e = valid ? ids[p] : -1;
@@ -430,6 +439,8 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
     __shared__ float wts[T * kMaxTopK];
     __shared__ int qs[T * kMaxTopK], qj[T * kMaxTopK];  // (token, rank) -> slot, position in slot
     __shared__ float sx[T], shs[T], rhs[kMaxTokens];
+    __shared__ double redd[NWV * T];
+    __shared__ float redf[NWV * T];
     __shared__ uint32_t s_epoch;
     __shared__ int s_grp[2];  // own slot, its first workgroup
 
@@ -456,6 +467,12 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         s_rng[5] = 2 * (int)((c + 1) * (unsigned)(a.H / 2) / N);
     }
     __syncthreads();
+
+    // weights prefetched one layer ahead: this wave's first router row or shared-expert unit, and
+    // its first pass over the shared expert's down rows
+    uint4 pr[RU];
+    GuUnit pu;
+    DnPass<ITERS> psd;
 
     for (int l = 0; l < L; ++l) {
         // Everything below is recomputed per layer from laundered thread and workgroup indices, so
@@ -497,15 +514,16 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         w.layer = l;
 
         PK_MARK(0);
-        // ---- prefetch: first router row or shared-expert unit of each wave, first shared down pass
         const int u0 = wv;
-        uint4 pr[RU];
-        GuUnit pu;
-        if (u0 < nr) router_load(router, eA + u0, H, pr, lane);
-        else if (u0 < nu0) gu_load(w13, w13s, E, iA + u0 - nr, I, NB, pu, lane);
-        DnPass<ITERS> psd;
-        if (wv < sh_passes)
-            dn_load<KSUB, ITERS>(w2, w2s, E, oA + min(wv * UPW + lane / KSUB, nro - 1), H, NI, psd, lane);
+        auto prefetch = [&](int lp) {
+            const LayerPtrs P = a.layers[lp];
+            if (u0 < nr) router_load((const uint16_t*)P.router, eA + u0, H, pr, lane);
+            else if (u0 < nu0) gu_load((const uint4*)P.w13, (const uint8_t*)P.w13s, E, iA + u0 - nr, I, NB, pu, lane);
+            if (wv < sh_passes)
+                dn_load<KSUB, ITERS>((const uint4*)P.w2, (const uint8_t*)P.w2s, E,
+                                     oA + min(wv * UPW + lane / KSUB, nro - 1), H, NI, psd, lane);
+        };
+        if (l == 0) prefetch(0);
 
         // ---- round X: the layer input
         if (l == 0) {
@@ -533,49 +551,80 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             }
         }
 
-        // ---- MoE input: optional RMSNorm (sum of squares in fp64), per-token FP8 quantisation.
-        // Every wave reduces the whole vector itself, so no workgroup barrier is needed: the
-        // maximum of |bf16(x * r)| is bf16(max|x| * r) because rounding is monotonic.
+        // ---- MoE input: optional RMSNorm (sum of squares in fp64), per-token FP8 quantisation.  Each
+        // thread owns 4-element quads; one barrier joins the per-wave partial sums.  The maximum of
+        // |bf16(x * r)| is bf16(max|x| * r) because rounding is monotonic.
         {
-            const int NU = H / 8;  // 16-byte chunks per token
+            const int NQ = H / 4;  // quads per token
+            double ss[T];
+            float mx[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                ss[t] = 0.0;
+                mx[t] = 0.0f;
+            }
+            for (int i = tid; i < T * NQ; i += NTH) {
+                int t = 0;
+#pragma unroll
+                for (int tt = 1; tt < T; ++tt) t += i >= tt * NQ ? 1 : 0;
+                const uint2 v = ((const uint2*)xr)[i];
+                double d = 0.0;
+                float m = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t w2 = q ? v.y : v.x;
+                    const float x0 = bf16_to_f32(w2), x1 = bf16_to_f32(w2 >> 16);
+                    m = fmaxf(m, fmaxf(fabsf(x0), fabsf(x1)));
+                    d = fma((double)x0, (double)x0, d);
+                    d = fma((double)x1, (double)x1, d);
+                }
+#pragma unroll
+                for (int tt = 0; tt < T; ++tt)
+                    if (tt == t) {
+                        ss[tt] += d;
+                        mx[tt] = fmaxf(mx[tt], m);
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const double sv = a.normalize ? sum64(ss[t]) : 0.0;
+                const float mv = max64(mx[t]);
+                if (lane == 0) {
+                    redd[wv * T + t] = sv;
+                    redf[wv * T + t] = mv;
+                }
+            }
+            __syncthreads();
             double rr[T];
             float sxv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                double ss = 0.0;
-                float mx = 0.0f;
-                for (int u = lane; u < NU; u += 64) {
-                    const uint4 v = ((const uint4*)(xr + t * H))[u];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float x0 = bf16_to_f32(comp(v, q)), x1 = bf16_to_f32(comp(v, q) >> 16);
-                        mx = fmaxf(mx, fmaxf(fabsf(x0), fabsf(x1)));
-                        ss = fma((double)x0, (double)x0, ss);
-                        ss = fma((double)x1, (double)x1, ss);
-                    }
+                double sv = 0.0;
+                float mv = 0.0f;
+                for (int q = 0; q < NWV; ++q) {
+                    sv += redd[q * T + t];
+                    mv = fmaxf(mv, redf[q * T + t]);
                 }
-                mx = max64(mx);
                 double r = 1.0;
-                float mxn = mx;
                 if (a.normalize) {
-                    r = 1.0 / sqrt(sum64(ss) / (double)H + 1e-6);
-                    mxn = bf16_to_f32(f32_to_bf16((float)((double)mx * r)));
+                    r = 1.0 / sqrt(sv / (double)H + 1e-6);
+                    mv = bf16_to_f32(f32_to_bf16((float)((double)mv * r)));
                 }
                 rr[t] = r;
-                sxv[t] = mxn > 0.0f ? mxn / 448.0f : 1.0f;
+                sxv[t] = mv > 0.0f ? mv / 448.0f : 1.0f;
             }
             if (tid < T) {
-                float s = sxv[0];
+                float sv = sxv[0];
 #pragma unroll
                 for (int t = 1; t < T; ++t)
-                    if (tid == t) s = sxv[t];
-                sx[tid] = s;
-                if (a.x_scale && c == 0) gp(a.x_scale)[(size_t)l * T + tid] = s;
+                    if (tid == t) sv = sxv[t];
+                sx[tid] = sv;
+                if (a.x_scale && c == 0) gp(a.x_scale)[(size_t)l * T + tid] = sv;
             }
-            for (int i = tid; i < T * NU; i += NTH) {
+            for (int i = tid; i < T * NQ; i += NTH) {
                 int t = 0;
 #pragma unroll
-                for (int tt = 1; tt < T; ++tt) t += i >= tt * NU ? 1 : 0;
+                for (int tt = 1; tt < T; ++tt) t += i >= tt * NQ ? 1 : 0;
                 double r = rr[0];
                 float sv = sxv[0];
 #pragma unroll
@@ -584,29 +633,28 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
                         r = rr[tt];
                         sv = sxv[tt];
                     }
-                uint4 v = ((const uint4*)xr)[i];
+                uint2 v = ((const uint2*)xr)[i];
                 if (a.normalize) {
-                    uint32_t o[4];
+                    uint32_t o[2];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t d = comp(v, q);
+                    for (int q = 0; q < 2; ++q) {
+                        const uint32_t d = q ? v.y : v.x;
                         const uint32_t lo = f32_to_bf16((float)((double)bf16_to_f32(d) * r));
                         const uint32_t hi = f32_to_bf16((float)((double)bf16_to_f32(d >> 16) * r));
                         o[q] = lo | (hi << 16);
                     }
-                    v = make_uint4(o[0], o[1], o[2], o[3]);
+                    v = make_uint2(o[0], o[1]);
                 }
-                ((uint4*)xn)[i] = v;
-                uint32_t cd[4];
+                ((uint2*)xn)[i] = v;
+                uint32_t cd[2];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t d = comp(v, q);
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t d = q ? v.y : v.x;
                     cd[q] = e4m3_pack2(bf16_to_f32(d) / sv, bf16_to_f32(d >> 16) / sv);
-                    xh[i * 4 + q] = e4m3x2_to_f16x2(cd[q]);
+                    xh[i * 2 + q] = e4m3x2_to_f16x2(cd[q]);
                 }
                 if (a.x_codes && c == 0)
-                    *(GLOBAL uint64_t*)(gp(a.x_codes) + (size_t)l * T * H + (size_t)i * 8) =
-                        (uint64_t)(cd[0] | (cd[1] << 16)) | ((uint64_t)(cd[2] | (cd[3] << 16)) << 32);
+                    *(GLOBAL uint32_t*)(gp(a.x_codes) + (size_t)l * T * H + (size_t)i * 4) = cd[0] | (cd[1] << 16);
             }
             __syncthreads();
         }
@@ -703,7 +751,10 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
         const int nd = dB - dA, rd_passes = (nd + UPW - 1) / UPW;
 
         PK_MARK(5);
-        // ---- routed loads: gate/up units in two buffers, then the first down passes
+        // ---- routed loads: gate/up units in two buffers, then the first down passes.  Every load
+        // issued earlier (the prefetch) has long completed; waiting for them here keeps the shared
+        // expert's work below from waiting for the routed loads.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         const int nu = hB - hA > wv ? (hB - hA - wv + NWV - 1) / NWV : 0;  // units of this wave
         const int ulast = nu > 0 ? hA + wv + (nu - 1) * NWV : hA;
         auto unit_i = [&](int m) { return min(hA + wv + m * NWV, ulast); };
@@ -740,7 +791,6 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             }
         }
 
-        PK_MARK(6);
         // ---- routed gate/up: compute from one buffer while the other is in flight
         auto gu_unit = [&](const GuUnit& u, int m) {
             float g[T], up[T];
@@ -769,6 +819,7 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             }
         }
 
+        PK_MARK(6);
         PK_MARK(7);
         // ---- round H: own expert's h, FP8 requantisation
         {
@@ -860,25 +911,33 @@ __global__ __launch_bounds__(NTH) void stack_kernel(StackArgs a) {
             }
             __syncthreads();
             PK_MARK(10);
+            if (l + 1 < L) prefetch(l + 1);
             const bool last = l == L - 1;
             const uint32_t nstamp = stamp_of(epoch, L, l + 1);
             uint64_t* xdst = a.xw + (size_t)(par ^ 1) * kMaxTokens * Hh;
-            for (int i = tid; i < T * (nro / 2); i += NTH) {
-                const int t = i / (nro / 2), v0 = 2 * (i - t * (nro / 2));
-                uint32_t xb[2];
+            for (int i0 = 0; i0 < T * nro; i0 += NTH) {  // uniform loop: thread (token, row), rows in pairs
+                const int i = i0 + tid;
+                const bool act = i < T * nro;
+                const int t = act ? (int)((unsigned)i / (unsigned)nro) : 0, v = act ? i - t * nro : 0;
+                float dv[kMaxTopK];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int v = v0 + h;
-                    float y = 0.0f;
-                    for (int r = 0; r < k; ++r) y = fmaf(wts[t * k + r], dg[(t * k + r) * a.rmax + v], y);
-                    if (S) y += dsh[t * a.rmax + v];
-                    const int row = oA + v;
-                    xb[h] = f32_to_bf16(bf16_to_f32(xr[t * H + row]) + y);
+                for (int r = 0; r < kMaxTopK; ++r) dv[r] = r < k ? dg[(t * k + r) * a.rmax + v] : 0.0f;
+                float y = 0.0f;
+#pragma unroll
+                for (int r = 0; r < kMaxTopK; ++r)
+                    if (r < k) y = fmaf(wts[t * k + r], dv[r], y);
+                if (S) y += dsh[t * a.rmax + v];
+                const int row = oA + v;
+                const uint32_t xb = f32_to_bf16(bf16_to_f32(xr[t * H + row]) + y);
+                const uint32_t other = xchg<0>(xb);  // the neighbouring row (nro is even: pairs stay in a lane pair)
+                if (act) {
                     if (last && a.y) gp(a.y)[(size_t)t * H + row] = y;
+                    if ((v & 1) == 0) {
+                        const uint32_t pairv = xb | (other << 16);
+                        if (!last) astore64(xdst + (size_t)t * Hh + row / 2, ((uint64_t)nstamp << 32) | pairv);
+                        else if (a.x_out) *(GLOBAL uint32_t*)(gp(a.x_out) + (size_t)t * H + row) = pairv;
+                    }
                 }
-                const uint32_t pairv = xb[0] | (xb[1] << 16);
-                if (!last) astore64(xdst + (size_t)t * Hh + (oA + v0) / 2, ((uint64_t)nstamp << 32) | pairv);
-                else if (a.x_out) *(GLOBAL uint32_t*)(gp(a.x_out) + (size_t)t * H + oA + v0) = pairv;
             }
         }
         PK_MARK(11);
