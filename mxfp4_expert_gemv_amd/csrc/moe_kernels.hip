@@ -978,6 +978,15 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         }
     }
     if (tid < npairs) s_pair[tid] = (tid / k) * (k + a.S) + tid % k;
+    // tile maxima of this wave's pairs (p = wave + m * waves), loaded with everything else up front
+    float hm[4];
+    if constexpr (!CODES) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int p = min(wv + NW * m, npairs - 1);
+            hm[m] = a.hamax[(size_t)(p + (p / k) * a.S) * tiles + min(lane, tiles - 1)];
+        }
+    }
     // pair p = t*k + r lives at h row t*(k+S) + r = p + (p / k) * S; walk it without dividing
     float2 hv[MAXP];
     if (loader) {
@@ -1026,7 +1035,17 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         if (tid < npairs) s_h[tid] = a.hs[s_pair[tid]];
         __syncthreads();
     } else {
-    requant_scales(a.hamax, tiles, s_pair, npairs, s_h);
+    for (int m = 0; m < 4 && wv + NW * m < npairs; ++m) {  // uniform per wave
+        const float mx = max64(lane < tiles ? hm[m] : 0.0f);
+        if (lane == 0) s_h[wv + NW * m] = mx > 0.0f ? mx / 448.0f : 1.0f;
+    }
+    for (int p = wv + 4 * NW; p < npairs; p += NW) {  // more pairs than 4 per wave (small grids)
+        float v = 0.0f;
+        for (int tl = lane; tl < tiles; tl += 64) v = fmaxf(v, a.hamax[(size_t)s_pair[p] * tiles + tl]);
+        const float mx = max64(v);
+        if (lane == 0) s_h[p] = mx > 0.0f ? mx / 448.0f : 1.0f;
+    }
+    __syncthreads();
     if (loader) {
 #pragma unroll
         for (int m = 0; m < MAXP; ++m) {
