@@ -40,7 +40,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
     ap.add_argument("--variant", choices=("persistent", "three_kernels"), default="three_kernels",
-                    help="kernel set: one persistent kernel per pass (default) or three kernels per layer")
+                    help="kernel set: three kernels per layer (default, the faster one) or one persistent kernel per pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
@@ -84,8 +84,8 @@ def main():
             "w2": torch.empty((n, H, I // 2), **u8), "w2_s": torch.empty((n, H, I // 32), **u8)}
 
     t0 = time.time()
-    vflags = moe.F_THREE_KERNELS if args.variant == "three_kernels" else 0
-    persistent = vflags == 0
+    vflags = moe.F_PERSISTENT if args.variant == "persistent" else 0
+    persistent = vflags != 0
     h = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, L,
                               moe.F_RMSNORM_INPUT | vflags)
     for l in range(L):

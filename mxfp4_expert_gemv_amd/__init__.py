@@ -20,7 +20,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
 F_RMSNORM_INPUT = 0x1
 F_DIRECT_LAUNCH = 0x2
-F_THREE_KERNELS = 0x4
+F_PERSISTENT = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
@@ -60,8 +60,8 @@ class Info(ctypes.Structure):
                 ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
 
 
-# kernel classes of the timing record: three kernels per layer (MOE_F_THREE_KERNELS), or the one
-# whole-pass kernel in class 0 (default)
+# kernel classes of the timing record: three kernels per layer (default), or the one whole-pass
+# kernel in class 0 (MOE_F_PERSISTENT)
 TIMING_CLASSES = ("router", "gateup", "down")
 
 

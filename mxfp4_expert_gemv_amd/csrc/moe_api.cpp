@@ -35,7 +35,7 @@ struct moe_decode_handle {
     moe_decode_config cfg;
     Shape sh;
     int device;
-    // persistent whole-stack kernel (default) or three kernels per layer (MOE_F_THREE_KERNELS)
+    // three kernels per layer (default) or one persistent whole-stack kernel (MOE_F_PERSISTENT)
     bool persistent;
     int grid_n = 0, rmax = 0;
     long long timeout_ticks = 0;
@@ -113,7 +113,7 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->inter % moe::kBlock || !moe::shape_supported(sh))
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
                     c->hidden, c->inter);
-    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_THREE_KERNELS))
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_PERSISTENT))
         return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
@@ -223,7 +223,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->xn = (uint16_t*)(h->ws + o_xn);
     h->hq = h->ws + o_hq;
     h->hs = (float*)(h->ws + o_hs);
-    h->persistent = (cfg->flags & MOE_F_THREE_KERNELS) == 0;
+    h->persistent = (cfg->flags & MOE_F_PERSISTENT) != 0;
     if (h->persistent) {
         int cus = 0, clock_khz = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||

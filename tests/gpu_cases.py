@@ -64,9 +64,10 @@ class DeviceLayer:
         return {e: synth.expert(self.shape, self.seed, self.layer, e) for e in used}
 
 
-# kernel variants of the library: the persistent whole-pass kernel (default) and three kernels per
-# layer; the parity tests run on both
-VARIANTS = {"persistent": 0, "three_kernels": moe.F_THREE_KERNELS}
+# kernel variants of the library: three kernels per layer (default) and the persistent whole-pass
+# kernel; the parity tests run on both
+VARIANTS = {"persistent": moe.F_PERSISTENT, "three_kernels": 0}
+DEFAULT_VARIANT = "three_kernels"
 _variant = {"flags": 0}
 
 

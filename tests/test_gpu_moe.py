@@ -11,7 +11,7 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import (MANIFEST, VARIANTS, DeviceLayer, check_layer, create, margin_attempt, normwise_err,
+from gpu_cases import (DEFAULT_VARIANT, MANIFEST, VARIANTS, DeviceLayer, check_layer, create, margin_attempt, normwise_err,
                        run_layer, set_variant, to_dev_u16)
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ def variant(request):
     print(f"variant {request.param}", flush=True)
     set_variant(request.param)
     yield request.param
-    set_variant("persistent")
+    set_variant(DEFAULT_VARIANT)
 
 
 def _layer_case(shape, seed, x, layer_obj=None, handle=None):

@@ -10,7 +10,7 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import MANIFEST, VARIANTS, DeviceLayer, Y_TOL, create, normwise_err, run_layer, set_variant
+from gpu_cases import DEFAULT_VARIANT, MANIFEST, VARIANTS, DeviceLayer, Y_TOL, create, normwise_err, run_layer, set_variant
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def stack(request):
         torch.cuda.synchronize()
         layers.append((lay.router_host, st["seed"], l))
         del lay
-    set_variant("persistent")
+    set_variant(DEFAULT_VARIANT)
     yield shape, h, layers, st
     moe.moe_decode_destroy(h)
 
