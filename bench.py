@@ -326,7 +326,7 @@ def kernel_names(variant, T):
     gu, dn = variant.split("-")[2:4]
     bpl = int(gu[2:].split("x")[1])
     ksub, iters = (int(v) for v in dn[2:].split("x"))
-    spw = 1 if T == 1 else 2 if T == 2 else 3
+    spw = 1 if T == 1 else 2 if T == 2 else 4
     return {"router": f"void moe::k1_router_shared<{T}, {bpl}>(moe::K1Args)",
             "gateup": f"void moe::k2_gateup<{T}, {bpl}, {ksub}, {iters}>(moe::K2Args)",
             "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}

@@ -571,13 +571,16 @@ struct K0Args {
     int H, normalize;
 };
 
-template <int T>
+// One workgroup per token (H/4 <= 1024 quads: one load per thread).
 __global__ __launch_bounds__(1024) void k0_input(K0Args a) {
     extern __shared__ uint4 smem0[];
-    __shared__ double redd[16 * T];
-    __shared__ float redf[16 * T];
-    norm_quant<T>(a.x, a.H, a.normalize != 0, (uint16_t*)smem0, a.xn, a.xq, a.xs, a.trace, a.x_scale, a.x_codes,
-                  redd, redf);
+    __shared__ double redd[16];
+    __shared__ float redf[16];
+    const int t = blockIdx.x;
+    const size_t o = (size_t)t * a.H;
+    norm_quant<1>(a.x + o, a.H, a.normalize != 0, (uint16_t*)smem0, a.xn + o, a.xq + o, a.xs + t,
+                  a.trace ? a.trace + o : nullptr, a.x_scale ? a.x_scale + t : nullptr,
+                  a.x_codes ? a.x_codes + o : nullptr, redd, redf);
 }
 
 struct KQArgs {
@@ -1174,7 +1177,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     constexpr bool CENTRAL = T >= 3;  // input and h requantisation once per layer (k0, kq)
     if (CENTRAL) {
         K0Args a0{P.x, P.xn, P.xq, P.xs, P.trace, P.x_scale, P.x_codes, sh.H, normalize ? 1 : 0};
-        k0_input<T><<<1, 1024, (size_t)T * sh.H * 2, stream>>>(a0);
+        k0_input<<<T, 1024, (size_t)sh.H * 2, stream>>>(a0);
     }
     const int n_router_wg = (sh.E + GW - 1) / GW;
     K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.xn, P.trace, P.logits,
