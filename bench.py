@@ -311,9 +311,9 @@ def kernel_bytes(shape, T, distinct):
     w13 = shape.w13_bytes + shape.w13s_bytes
     w2 = shape.w2_bytes + shape.w2s_bytes
     x = T * shape.hidden * 2
-    return {"router": shape.num_experts * shape.hidden * 2 + shape.num_shared * w13 + x,
-            "gateup": distinct * w13 + shape.num_shared * w2,
-            "down": distinct * w2 + 2 * x}
+    return {"router": shape.num_experts * shape.hidden * 2 + x,
+            "gateup": (distinct + shape.num_shared) * w13,
+            "down": (distinct + shape.num_shared) * w2 + 2 * x}
 
 
 def kernel_names(variant, T):
@@ -327,8 +327,8 @@ def kernel_names(variant, T):
     bpl = int(gu[2:].split("x")[1])
     ksub, iters = (int(v) for v in dn[2:].split("x"))
     spw = 1 if T == 1 else 2 if T == 2 else 4
-    return {"router": f"void moe::k1_router_shared<{T}, {bpl}>(moe::K1Args)",
-            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {ksub}, {iters}>(moe::K2Args)",
+    return {"router": f"void moe::k1_router<{T}, {bpl}>(moe::K1Args)",
+            "gateup": f"void moe::k2_gateup<{T}, {bpl}>(moe::K2Args)",
             "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}
 
 

@@ -90,7 +90,7 @@ typedef struct fp8_head_handle fp8_head_handle;
 typedef struct {
     uint32_t struct_size; /* sizeof(moe_decode_config) */
     int32_t hidden;       /* H: multiple of 256, 256..2560 (the library checks that it has a kernel) */
-    int32_t num_experts;  /* E routed experts: 1..512 */
+    int32_t num_experts;  /* E routed experts: a multiple of 8 up to 512 */
     int32_t top_k;        /* k: 1..8, <= E */
     int32_t num_shared;   /* S: 0 or 1; the shared expert is stored at expert index E */
     int32_t inter;        /* I: SwiGLU width: 64, 128, 256 or 768 */

@@ -55,7 +55,6 @@ struct moe_decode_handle {
     moe::SlotTable* slots;
     float* h;
     float* hamax;
-    float* dshared;
     uint16_t* xn;
     uint8_t* hq;
     float* hs;
@@ -106,7 +105,8 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->num_shared > 1) return fail(MOE_ERR_UNSUPPORTED, "num_shared %d (0 or 1 supported)", c->num_shared);
     if (c->hidden % 256 || c->hidden > 2560)
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", c->hidden);
-    if (c->num_experts > 512) return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > 512", c->num_experts);
+    if (c->num_experts > 512 || c->num_experts % 8)
+        return fail(MOE_ERR_UNSUPPORTED, "num_experts %d (multiple of 8 up to 512 supported)", c->num_experts);
     if (c->top_k > moe::kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k %d > 8", c->top_k);
     if (c->max_tokens > moe::kMaxTokens) return fail(MOE_ERR_UNSUPPORTED, "max_tokens %d > 4", c->max_tokens);
     const moe::Shape sh{c->hidden, c->num_experts, c->top_k, c->num_shared, c->inter};
@@ -184,7 +184,6 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     const uint64_t o_slot = o; o += align256(sizeof(moe::SlotTable));
     const uint64_t o_h = o; o += align256((uint64_t)sh.pairs(T) * sh.I * 4);
     const uint64_t o_ham = o; o += align256((uint64_t)sh.pairs(T) * sh.gu_tiles() * 4);
-    const uint64_t o_ds = o; o += align256((uint64_t)T * sh.H * 4);
     const uint64_t o_xn = o; o += align256((uint64_t)T * sh.H * 2);
     const uint64_t o_hq = o; o += align256((uint64_t)sh.pairs(T) * sh.I);
     const uint64_t o_hs = o; o += align256((uint64_t)sh.pairs(T) * 4);
@@ -219,7 +218,6 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->slots = (moe::SlotTable*)(h->ws + o_slot);
     h->h = (float*)(h->ws + o_h);
     h->hamax = (float*)(h->ws + o_ham);
-    h->dshared = (float*)(h->ws + o_ds);
     h->xn = (uint16_t*)(h->ws + o_xn);
     h->hq = h->ws + o_hq;
     h->hs = (float*)(h->ws + o_hs);
@@ -350,7 +348,6 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
         p.slots = h->slots;
         p.h = h->h;
         p.hamax = h->hamax;
-        p.dshared = h->dshared;
         p.xn = h->xn;
         p.hq = h->hq;
         p.hs = h->hs;

@@ -1,18 +1,25 @@
 // moe_kernels.hip -- gfx950 kernels of the W4A8 sparse-MoE decode step.
 //
-// One layer is three launches (replayed from a HIP graph by the library):
-//   k1_router_shared  router GEMV, one wave per expert row (bf16 x bf16 products, fp32 FMA), and the
-//                     shared expert's gate/up tiles (it needs no routing decision).
-//   k2_gateup         every workgroup redoes the top-k from the logits (one wave per token, lower
-//                     index first on ties), builds the list of distinct routed experts, then streams
-//                     its 32-row MXFP4 gate/up tile: E2M1 pairs are converted to f16 in VGPRs and
-//                     dot2-multiplied with the FP8-quantised activation held in LDS; writes
-//                     h = SiLU(gate) * up and the tile's max |h|.  Extra workgroups compute the
-//                     shared expert's down projection.
-//   k3_down           one workgroup per 8-row output tile and every routed expert: requantises each
-//                     (token, expert) h vector to FP8 in LDS, streams the MXFP4 down rows and sums
-//                     the routing-weighted results and the shared expert's in a fixed order (no
-//                     float atomics); writes y and the bf16 residual.
+// One layer is three launches (replayed from a HIP graph by the library), plus two small ones at
+// 3-4 tokens:
+//   k0_input          (3-4 tokens) one workgroup per token: RMSNorm of the residual and the FP8
+//                     quantisation of the MoE input, once per layer.
+//   k1_router         router GEMV, one wave per expert row (bf16 x bf16 products, fp32 FMA).  At
+//                     1-2 tokens every workgroup also normalises the input itself and stores the
+//                     FP8 codes of its share of it; at 3-4 tokens the last router workgroup to
+//                     finish takes the top-k once (arrival ticket), and extra workgroups compute
+//                     the shared expert's gate/up tiles.
+//   k2_gateup         the routed gate/up tiles (and at 1-2 tokens the shared expert's): at 1-2
+//                     tokens every routed workgroup redoes the top-k from the logits (one wave per
+//                     token, lower index first on ties) and builds the list of distinct routed
+//                     experts; each workgroup streams its 32-row MXFP4 gate/up tile: E2M1 pairs are
+//                     converted to f16 in VGPRs and dot2-multiplied with the FP8 activation codes
+//                     (as f16) held in LDS; writes h = SiLU(gate) * up and the tile's max |h|.
+//   kq_requant        (3-4 tokens) the FP8 requantisation of every h vector, once per layer.
+//   k3_down           one workgroup per 8-row output tile, over every routed expert and the shared
+//                     one: requantises each (token, expert) h vector to FP8 in LDS (or decodes its
+//                     codes), streams the MXFP4 down rows and sums the routing-weighted results in
+//                     a fixed order (no float atomics); writes y and the bf16 residual.
 //
 // What is computed follows the MoE decode step described on the pages (tanhow.com, "NVIDIA 在单台
 // DGX Spark 上叠加三项优化..." sections "Ling 3.0 是什么" (8 of 512 routed experts + 1 shared) and
@@ -23,6 +30,8 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -44,15 +53,6 @@ struct ScaleBytes<4> {
     __device__ void load(const uint8_t* p) { v = __builtin_nontemporal_load((const uint32_t*)p); }
     __device__ uint32_t get(int i) const { return (v >> (8 * i)) & 0xffu; }
 };
-
-template <int T>
-__device__ __forceinline__ float pick(const float (&v)[T], int t) {
-    float r = v[0];
-#pragma unroll
-    for (int i = 1; i < T; ++i)
-        if (t == i) r = v[i];
-    return r;
-}
 
 // ------------------------------------------------------------------------------------------------
 // repack kernels (canonical row-major -> lane tiles; pure permutations of 16-byte units / bytes)
@@ -135,37 +135,51 @@ __global__ void repack_w2s(const uint8_t* __restrict__ src, uint8_t* __restrict_
 // shared pieces: MoE input, FP8 quantisation of the input, gate/up tile
 // ------------------------------------------------------------------------------------------------
 
-// x_in = x, or bf16(fl32(x * r)) with r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64; stored as
-// bf16 bits in LDS xb[T][H].  One 16-byte load per thread and token (H/8 <= threads), all issued
-// before any use.
+// The MoE input of T tokens in one workgroup: x_in = x, or bf16(fl32(x * r)) with
+// r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64 (sum of squares in fp64), staged in LDS
+// xb[T][H]; and its per-token FP8 scale s = max|x_in| / 448 (1 when x_in = 0), returned in sx.
+// The maximum of |x_in| is bf16(max|x| * r) because rounding is monotonic, so both reductions
+// share one barrier.  red_d, red_m: LDS [waves][T].  Ends with a barrier.
 template <int T>
-__device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize, uint16_t* xb, double* red_d) {
+__device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize, uint16_t* xb, double* red_d,
+                          float* red_m, float (&sx)[T]) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
     const bool has = tid < NC;
     uint4 v[T];
 #pragma unroll
     for (int t = 0; t < T; ++t)
         if (has) v[t] = *(const uint4*)(x + (size_t)t * H + tid * 8);
-    if (normalize) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            double ss = 0.0;
-            if (has) {
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        float m = 0.0f;
+        if (has) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const double a = (double)bf16_to_f32(comp(v[t], q)), b = (double)bf16_to_f32(comp(v[t], q) >> 16);
-                    ss += a * a + b * b;
-                }
+            for (int q = 0; q < 4; ++q) {
+                const float a = bf16_to_f32(comp(v[t], q)), b = bf16_to_f32(comp(v[t], q) >> 16);
+                ss += (double)a * (double)a + (double)b * (double)b;
+                m = fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
             }
-            ss = sum64(ss);
-            if (lane == 0) red_d[wv * T + t] = ss;
         }
-        __syncthreads();
+        if (normalize) ss = sum64(ss);
+        m = max64(m);
+        if (lane == 0) {
+            red_d[wv * T + t] = ss;
+            red_m[wv * T + t] = m;
+        }
+    }
+    __syncthreads();
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            double ss = 0.0;
-            for (int w = 0; w < NW; ++w) ss += red_d[w * T + t];
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        float m = 0.0f;
+        for (int w = 0; w < NW; ++w) {
+            ss += red_d[w * T + t];
+            m = fmaxf(m, red_m[w * T + t]);
+        }
+        if (normalize) {
             const double r = 1.0 / sqrt(ss / (double)H + 1e-6);
+            m = bf16_to_f32(f32_to_bf16((float)((double)m * r)));
             if (has) {
                 uint32_t o[4];
 #pragma unroll
@@ -178,6 +192,7 @@ __device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize,
                 v[t] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
+        sx[t] = m > 0.0f ? m / 448.0f : 1.0f;
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -185,75 +200,42 @@ __device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize,
     __syncthreads();
 }
 
-// Per-token FP8 quantisation of the bf16 input xb[T][H] (LDS): s = max|x| / 448 (1 when x = 0),
-// codes = RNE(x / s).  The exact f16 values of the codes go to xh[T][H/2] (LDS); when codes_out is
-// set the codes and scales are also stored to global memory.
+// FP8 codes RNE(x_in / s) of this workgroup's share of the 8-element units of xb[T][H] (LDS,
+// complete): every workgroup of the grid stores its own share (workgroup 0 also the scales), so
+// the work on each workgroup's path is one division per element of its share.  codes_dbg /
+// scale_dbg: optional copies.
 template <int T>
-__device__ void quantize_input(const uint16_t* xb, int H, half2_t* xh, float* wmax, float* sx_lds,
-                               uint8_t* codes_out, float* scale_out, uint8_t* codes_dbg = nullptr,
-                               float* scale_dbg = nullptr) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
-    const bool has = tid < NC;
-    uint4 v[T];
+__device__ void quantize_slice(const uint16_t* xb, int H, const float (&sx)[T], uint8_t* codes, float* scales,
+                               uint8_t* codes_dbg, float* scale_dbg) {
+    const int tid = threadIdx.x, NC = H / 8;
+    const int per = (NC + (int)gridDim.x - 1) / (int)gridDim.x, u = (int)blockIdx.x * per + tid;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        float m = 0.0f;
-        if (has) {
-            v[t] = *(const uint4*)(xb + t * H + tid * 8);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(comp(v[t], q))), fabsf(bf16_to_f32(comp(v[t], q) >> 16))));
+        if (blockIdx.x == 0 && tid == 0) {
+            scales[t] = sx[t];
+            if (scale_dbg) scale_dbg[t] = sx[t];
         }
-        m = max64(m);
-        if (lane == 0) wmax[wv * T + t] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float m = 0.0f;
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, wmax[w * T + t]);
-        const float sx = m > 0.0f ? m / 448.0f : 1.0f;
-        if (tid == 0) {
-            sx_lds[t] = sx;
-            if (scale_out) scale_out[t] = sx;
-            if (scale_dbg) scale_dbg[t] = sx;
-        }
-        if (has) {
+        if (tid < per && u < NC) {
+            const uint4 v = *(const uint4*)(xb + t * H + u * 8);
             uint32_t c[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t d = comp(v[t], q);
-                c[q] = e4m3_pack2(bf16_to_f32(d) / sx, bf16_to_f32(d >> 16) / sx);
-                xh[t * (H / 2) + tid * 4 + q] = e4m3x2_to_f16x2(c[q]);
+                const uint32_t d = comp(v, q);
+                c[q] = e4m3_pack2(bf16_to_f32(d) / sx[t], bf16_to_f32(d >> 16) / sx[t]);
             }
             const uint2 cw = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
-            if (codes_out) *(uint2*)(codes_out + (size_t)t * H + tid * 8) = cw;
-            if (codes_dbg) *(uint2*)(codes_dbg + (size_t)t * H + tid * 8) = cw;
+            *(uint2*)(codes + (size_t)t * H + u * 8) = cw;
+            if (codes_dbg) *(uint2*)(codes_dbg + (size_t)t * H + u * 8) = cw;
         }
     }
-    __syncthreads();
 }
 
-__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent32(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The MoE input of one layer, computed once per layer by one workgroup: x_in = x, or
-// bf16(fl32(x * r)) with r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64 (sum of squares in
-// fp64); its per-token FP8 quantisation s = max|x_in| / 448 (1 when x_in = 0), codes = RNE(x_in / s).
-// The maximum of |x_in| is bf16(max|x| * r) because rounding is monotonic.  x is read with
-// device-scope loads (other workgroups of the same kernel may have just written it), staged in
-// LDS xb[T][H].  Writes x_in (bf16) to xn, the codes to xq, the scales to xs, and the optional
-// per-layer copies (trace: x itself; x_scale; x_codes).
+// The MoE input of T tokens, computed by one workgroup: x_in = x, or bf16(fl32(x * r)) with
+// r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64 (sum of squares in fp64); its per-token FP8
+// quantisation s = max|x_in| / 448 (1 when x_in = 0), codes = RNE(x_in / s).  The maximum of
+// |x_in| is bf16(max|x| * r) because rounding is monotonic.  x is staged in LDS xb[T][H].  Writes
+// x_in (bf16) to xn, the codes to xq, the scales to xs, and the optional per-layer copies (trace:
+// x itself; x_scale; x_codes).
 template <int T>
 __device__ void norm_quant(const uint16_t* x, int H, bool normalize, uint16_t* xb, uint16_t* xn, uint8_t* xq,
                            float* xs, uint16_t* trace, float* x_scale, uint8_t* x_codes, double* redd, float* redf) {
@@ -270,7 +252,7 @@ __device__ void norm_quant(const uint16_t* x, int H, bool normalize, uint16_t* x
         int t = 0;
 #pragma unroll
         for (int tt = 1; tt < T; ++tt) t += i >= tt * NQ ? 1 : 0;
-        const uint64_t v = ld_agent64((const uint64_t*)x + i);
+        const uint64_t v = ((const uint64_t*)x)[i];
         ((uint64_t*)xb)[i] = v;
         if (trace) ((uint64_t*)trace)[i] = v;
         double d = 0.0;
@@ -434,54 +416,60 @@ __device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, con
     }
 }
 
-// FP8 requantisation scale of each listed h vector: s_h = max|h| / 448 (1 when h = 0), from the
-// per-tile maxima hamax[pair][tiles] (tiles <= 64).  One wave per vector, lanes over tiles, up to 4
-// vectors per wave and batch; pairs[i] < 0 gives 1.  out: LDS.  Ends with a barrier.
-__device__ void requant_scales(const float* hamax, int tiles, const int* pairs, int n, float* out) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
-    for (int base = wv; base < n; base += 4 * NW) {  // uniform per wave
-        int pr[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) pr[m] = base + NW * m < n ? pairs[base + NW * m] : -1;
-        float v[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) v[m] = hamax[(size_t)max(pr[m], 0) * tiles + min(lane, tiles - 1)];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            if (pr[m] < 0 || lane >= tiles) v[m] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int i = base + NW * m;
-            if (i < n) {
-                const float mx = max64(v[m]);
-                if (lane == 0) out[i] = mx > 0.0f ? mx / 448.0f : 1.0f;
-            }
-        }
-    }
-    __syncthreads();
+// Top-k of every token, one wave per token.  Lane l holds experts 8l..8l+7 and sorts them by
+// (logit descending, index ascending) with 64-bit keys; then each of the k rounds takes the
+// wave-wide maximum of the lanes' head logits (32-bit order-preserving codes) through lane
+// exchanges, the lowest lane holding it wins (lower lanes hold lower experts, so ties go to the
+// lower index) and pops its head.  Lane r keeps the winner of round r, so the softmax over the
+// selected logits runs across lanes 0..k-1.  (A six-level bitonic merge tree across lanes, and
+// 64-bit keys in the rounds, measured slower: a single wave is bound by its instruction count.)
+// Then the list of distinct routed experts; everything lands in LDS.
+//
+// route_issue loads the logits of this wave's first token (token = wave index, if below T) so
+// that the caller can overlap other work with their latency; route_finish completes the
+// selection (further tokens of this wave, on small workgroups, are loaded there).
+// The 8 logits of this lane, experts 8 lane .. 8 lane + 7 (E is a multiple of 8; lanes beyond E
+// reload the last 8): two 16-byte loads.
+__device__ __forceinline__ void load_logits8(const float* row, int E, float (&v)[8]) {
+    const float4* p = (const float4*)(row + min((int)(threadIdx.x & 63) * 8, E - 8));
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Top-k of every token, one wave per token: each lane sorts its 8 keys (experts lane + 64j) in
-// descending order; each of the k rounds takes the wave-wide maximum of the lanes' heads through
-// lane exchanges and the winning lane pops its head.  Lane r keeps the winner of round r, so the
-// softmax over the selected logits runs across lanes 0..k-1.  (A six-level bitonic merge tree
-// across lanes measured slower: a single wave is bound by its instruction count.)  Then the
-// list of distinct routed experts; everything lands in LDS.
-template <int T>
-__device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids, float* wts) {
+// The same from logits that other workgroups of the running kernel stored with device-scope stores.
+__device__ __forceinline__ void load_logits8_agent(const float* row, int E, float (&v)[8]) {
+    const float* p = row + min((int)(threadIdx.x & 63) * 8, E - 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wave loads (waves beyond the last token repeat it), so that the number of loads in flight
+// is the same on every path and later waits stay exact.
+__device__ __forceinline__ void route_issue(const float* logits, int E, int T, float (&lgv)[8]) {
+    load_logits8(logits + min((int)(threadIdx.x >> 6), T - 1) * E, E, lgv);
+}
+
+template <int T, bool AGENT = false>
+__device__ void route_finish(const float (&lgv0)[8], const float* logits, int E, int k, SlotTable* st, int* ids,
+                             float* wts) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
     for (int t = wv; t < T; t += NW) {
-        // all 8 loads unconditional (clamped index) so they are issued back to back
         float lgv[8];
+        if (t == wv) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            lgv[j] = __hip_atomic_load(logits + t * E + min(lane + 64 * j, E - 1), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        uint64_t key[8];
+            for (int j = 0; j < 8; ++j) lgv[j] = lgv0[j];
+        } else if (AGENT) {
+            load_logits8_agent(logits + t * E, E, lgv);
+        } else {
+            load_logits8(logits + t * E, E, lgv);
+        }
+        uint64_t key[8];  // order code of the logit above, 7 - j below; 0 = no expert
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int e = lane + 64 * j;
-            key[j] = e < E ? topk_key(lgv[j], e) : 0ull;
+            const uint32_t u = __float_as_uint(lgv[j] + 0.0f);  // -0 -> +0
+            const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            key[j] = lane * 8 + j < E ? ((uint64_t)o << 32) | (uint32_t)(7 - j) : 0ull;
         }
         cx_desc(key[0], key[1]); cx_desc(key[2], key[3]); cx_desc(key[4], key[5]); cx_desc(key[6], key[7]);
         cx_desc(key[0], key[2]); cx_desc(key[1], key[3]); cx_desc(key[4], key[6]); cx_desc(key[5], key[7]);
@@ -489,30 +477,41 @@ __device__ void route(const float* logits, int E, int k, SlotTable* st, int* ids
         cx_desc(key[0], key[4]); cx_desc(key[1], key[5]); cx_desc(key[2], key[6]); cx_desc(key[3], key[7]);
         cx_desc(key[2], key[4]); cx_desc(key[3], key[5]);
         cx_desc(key[1], key[2]); cx_desc(key[3], key[4]); cx_desc(key[5], key[6]);
-        uint64_t mine = 0ull;
-        for (int r = 0; r < k; ++r) {
-            uint64_t best = key[0];
-            best = max64u(best, xchg<0>(best));
-            best = max64u(best, xchg<1>(best));
-            best = max64u(best, xchg<2>(best));
-            best = max64u(best, xchg<3>(best));
-            best = max64u(best, xchg<4>(best));
-            best = max64u(best, xchg<5>(best));
-            const bool win = key[0] == best;  // keys are unique: exactly one lane pops
+        uint32_t hv[8], hj = 0;  // head codes; the lane-local positions 7 - j, 4 bits each
 #pragma unroll
-            for (int j = 0; j < 7; ++j) key[j] = win ? key[j + 1] : key[j];
-            key[7] = win ? 0ull : key[7];
-            mine = lane == r ? best : mine;
+        for (int i = 0; i < 8; ++i) {
+            hv[i] = (uint32_t)(key[i] >> 32);
+            hj |= ((uint32_t)key[i] & 7u) << (4 * i);
         }
-        const uint32_t o = (uint32_t)(mine >> 32);
-        const float lg = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+        int my_id = 0;
+        uint32_t my_code = 0;
+        for (int r = 0; r < k; ++r) {
+            uint32_t m = hv[0];
+            m = max(m, xchg<0>(m));
+            m = max(m, xchg<1>(m));
+            m = max(m, xchg<2>(m));
+            m = max(m, xchg<3>(m));
+            m = max(m, xchg<4>(m));
+            m = max(m, xchg<5>(m));
+            const int w = (int)__builtin_ctzll(__ballot(hv[0] == m));  // lowest lane with the maximum
+            const int id = w * 8 + 7 - (int)(__builtin_amdgcn_readlane(hj, w) & 7u);
+            my_id = lane == r ? id : my_id;
+            my_code = lane == r ? m : my_code;
+            if (lane == w) {
+#pragma unroll
+                for (int i = 0; i < 7; ++i) hv[i] = hv[i + 1];
+                hv[7] = 0u;
+                hj >>= 4;
+            }
+        }
+        const float lg = __uint_as_float((my_code & 0x80000000u) ? (my_code & 0x7fffffffu) : ~my_code);
         const float l0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg)));  // the maximum
         const float z = lane < k ? expf(lg - l0) : 0.0f;
         float zs = z + xchg<0>(z);
         zs += xchg<1>(zs);
         zs += xchg<2>(zs);  // lanes 0..7 now all hold the sum over lanes 0..7 (k <= 8)
         if (lane < k) {
-            ids[t * k + lane] = (int)(0xffffffffu - (uint32_t)mine);
+            ids[t * k + lane] = my_id;
             wts[t * k + lane] = z / zs;
         }
     }
@@ -588,14 +587,14 @@ struct KQArgs {
     const float* hamax;  // [pairs][I/16]
     uint8_t* hq;         // [pairs][I] FP8 codes
     float* hs;           // [pairs] scales
-    int I, k, S;
+    int I;
 };
 
-// One workgroup per routed (token, rank) pair p = t*k + r (h row t*(k+S) + r): s_h = max|h| / 448
+// One workgroup per h row (token, rank r <= k; r = k is the shared expert): s_h = max|h| / 448
 // (1 when h = 0) from the tile maxima, codes = RNE(h / s_h).
 __global__ __launch_bounds__(256) void kq_requant(KQArgs a) {
     __shared__ float s;
-    const int p = blockIdx.x, t = p / a.k, row = p + t * a.S, tid = threadIdx.x, lane = tid & 63;
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int I = a.I, tiles = I / kGuOut, Ih = I / 2;
     float2 v[2];
 #pragma unroll
@@ -626,102 +625,139 @@ __global__ __launch_bounds__(256) void kq_requant(KQArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// k1: router rows + shared expert gate/up tiles (+ the FP8 codes of the input, stored once)
+// k1: router rows (+ the layer's MoE input, stored once for the gate/up kernel)
 // ------------------------------------------------------------------------------------------------
 
 struct K1Args {
     const uint16_t* router;  // [E][H]
-    const uint4* w13;        // repacked codes (expert E = shared)
-    const uint8_t* w13s;
     const uint16_t* x;       // [T][H] residual x_l (or the MoE input)
-    const uint16_t* xn;      // [T][H] MoE input computed by the input kernel (3-4 tokens), else unused
-    uint16_t* trace;         // [T][H] copy of x, or null (workgroup 0)
+    const uint16_t* xn;      // 3-4 tokens: [T][H] MoE input from the input kernel
+    uint8_t* xq;             // 1-2 tokens: [T][H] FP8 codes of the MoE input (stored here, shared out)
+    float* xs;               // 1-2 tokens: [T] their scales
+    uint16_t* trace;         // 1-2 tokens: [T][H] copy of x, or null (workgroup 0)
+    float* x_scale;          // 1-2 tokens: [T] or null
+    uint8_t* x_codes;        // 1-2 tokens: [T][H] or null
     float* logits;           // [T][E]
-    uint8_t* xq;             // [T][H] FP8 codes of the MoE input (one workgroup stores them)
-    float* xs;               // [T] their scales
-    float* x_scale_out;      // [T] or null
-    uint8_t* x_codes_out;    // [T][H] or null
-    float* h;                // [pairs][I]
-    float* hamax;            // [pairs][I/16]
+    // 3-4 tokens: the last router workgroup to finish takes the top-k once for the layer
     unsigned* ticket;        // arrivals of router workgroups; zero between layers
-    SlotTable* slots_out;    // routed experts of this layer (written by the last router workgroup)
+    SlotTable* slots_out;    // routed experts of this layer
     int32_t* ids_out;        // [T][k] or null
     float* w_out;            // [T][k] or null
+    // 3-4 tokens: workgroups from n_router_wg on compute the shared expert's gate/up tiles (CUs the
+    // router leaves idle), which keeps the gate/up kernel within one workgroup round
+    const uint4* w13;
+    const uint8_t* w13s;
+    float* h;                // [pairs][I]
+    float* hamax;            // [pairs][I/16]
     int H, E, k, S, I, normalize, n_router_wg;
-    int ntok;                // = T, passed at run time so the shared tile's token loop stays a loop
+    int ntok;                // = T, at run time (keeps the shared expert's token loop a loop)
 };
 
+// One expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row; bf16 x bf16
+// products in fp32 FMA, one logit per wave and token.  At 1-2 tokens every workgroup also
+// normalises the input and stores the FP8 codes of its share of it.
 template <int T, int BPL>
-__global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
+__global__ __launch_bounds__(320) void k1_router(K1Args a) {
     extern __shared__ uint4 smem1[];
-    uint16_t* xb = (uint16_t*)smem1;                      // [T][H] bf16 MoE input
-    half2_t* xh = (half2_t*)(xb + T * a.H);               // [T][H/2]
+    uint16_t* xb = (uint16_t*)smem1;  // [T][H] bf16 MoE input
     __shared__ double red_d[kMaxWaves * T];
     __shared__ float wmax[kMaxWaves * T];
-    __shared__ float red[kMaxWaves * T * kGuRows];
-    __shared__ float sx[T];
     __shared__ SlotTable st;
     __shared__ int ids[T * kMaxTopK];
     __shared__ float wts[T * kMaxTopK];
     __shared__ int is_last;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    const int H = a.H;
-    const bool is_router = (int)blockIdx.x < a.n_router_wg;
-    // the workgroup that publishes the input's FP8 codes: shared tile 0, or router 0 without a shared expert
-    const bool publish = a.S ? (int)blockIdx.x == a.n_router_wg : blockIdx.x == 0;
-    // 3-4 tokens: the MoE input and its codes come from the input kernel (once per layer) instead of
-    // being recomputed by every workgroup (its fp64 work grows with the token count)
+    const int H = a.H, NU = H / 8;
+    // 3-4 tokens: the MoE input comes from the input kernel (once per layer) instead of being
+    // recomputed by every workgroup (its fp64 work grows with the token count)
     constexpr bool CENTRAL = T >= 3;
-
-    if (is_router) {
-        // one expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row
-        const int e = blockIdx.x * NW + wv;
-        const int NU = H / 8;
-        uint4 wr[kMaxWaves];
-        {
-            const uint4* p = (const uint4*)(a.router + (size_t)min(e, a.E - 1) * H);
+    if constexpr (CENTRAL) {
+        if ((int)blockIdx.x >= a.n_router_wg) {  // the shared expert's gate/up tile, every token
+            __shared__ float red[kMaxWaves * T * kGuRows];
+            __shared__ float sx[T];
+            half2_t* xh = (half2_t*)smem1;  // [T][H/2] f16 values of the input's FP8 codes
+            const int tiles = a.I / kGuOut, tile = blockIdx.x - a.n_router_wg, NC = H / 8;
+            uint2 xc[T];
+            const int xi = min(tid, NC - 1) * 8;
 #pragma unroll
-            for (int j = 0; j < kMaxWaves; ++j) wr[j] = ld_nt(p + min(lane + 64 * j, NU - 1));
-        }
-        if constexpr (CENTRAL) {
-            for (int i = tid; i < T * NU; i += blockDim.x) ((uint4*)xb)[i] = ((const uint4*)a.xn)[i];
-            __syncthreads();
-        } else {
-            moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
-            if (blockIdx.x == 0 && a.trace) {
-                for (int i = tid; i < T * H / 8; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
-            }
-            if (publish) quantize_input<T>(xb, H, xh, wmax, sx, a.xq, a.xs, a.x_codes_out, a.x_scale_out);
-        }
-        if (e < a.E) {
-            float acc[T];
-#pragma unroll
-            for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kMaxWaves; ++j) {
-                const int u = lane + 64 * j;
-                if (u < NU) {
-#pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        const uint4 xv = *(const uint4*)(xb + t * H + u * 8);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint32_t d = comp(wr[j], q), xx = comp(xv, q);
-                            acc[t] = fmaf(__uint_as_float(d << 16), __uint_as_float(xx << 16), acc[t]);
-                            acc[t] = fmaf(__uint_as_float(d & 0xffff0000u), __uint_as_float(xx & 0xffff0000u), acc[t]);
-                        }
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the LDS reads of later units from being hoisted
-            }
+            for (int t = 0; t < T; ++t) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + xi);
+            const float sxv = a.xs[tid < T ? tid : 0];
+            GuLoads<BPL> L;
+            L.issue(a.w13, a.w13s, a.E, tile, tiles, NW);
+            if (tid < T) sx[tid] = sxv;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float v = sum64(acc[t]);
-                // write-through store: the last router workgroup reads it without any cache flush
-                if (lane == 0) __hip_atomic_store(a.logits + t * a.E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (tid < NC) {
+                    half2_t* o = xh + t * (H / 2) + tid * 4;
+                    o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
+                    o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
+                    o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
+                    o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
+                }
+            }
+            __syncthreads();
+            int tok[T], pair[T];
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+                tok[j] = j;
+                pair[j] = j * (a.k + a.S) + a.k;
+            }
+            gateup_tile<T, BPL>(L, xh, H, sx, a.ntok, tok, pair, tile, a.I, a.h, a.hamax, red);
+            return;
+        }
+    }
+    const int e = blockIdx.x * NW + wv;
+    uint4 wr[kMaxWaves];
+    {
+        const uint4* p = (const uint4*)(a.router + (size_t)min(e, a.E - 1) * H);
+#pragma unroll
+        for (int j = 0; j < kMaxWaves; ++j) wr[j] = ld_nt(p + min(lane + 64 * j, NU - 1));
+    }
+    if constexpr (CENTRAL) {
+        for (int i = tid; i < T * NU; i += blockDim.x) ((uint4*)xb)[i] = ((const uint4*)a.xn)[i];
+        __syncthreads();
+    } else {
+        float sx[T];
+        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d, wmax, sx);
+        if (blockIdx.x == 0 && a.trace)
+            for (int i = tid; i < T * NU; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
+        quantize_slice<T>(xb, H, sx, a.xq, a.xs, a.x_codes, a.x_scale);
+    }
+    if (e < a.E) {
+        float acc[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxWaves; ++j) {
+            const int u = lane + 64 * j;
+            if (u < NU) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const uint4 xv = *(const uint4*)(xb + t * H + u * 8);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t d = comp(wr[j], q), xx = comp(xv, q);
+                        acc[t] = fmaf(__uint_as_float(d << 16), __uint_as_float(xx << 16), acc[t]);
+                        acc[t] = fmaf(__uint_as_float(d & 0xffff0000u), __uint_as_float(xx & 0xffff0000u), acc[t]);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the LDS reads of later units from being hoisted
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float v = sum64(acc[t]);
+            if (lane == 0) {
+                if constexpr (CENTRAL)  // write-through: the last workgroup reads it without a cache flush
+                    __hip_atomic_store(a.logits + t * a.E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    a.logits[t * a.E + e] = v;
             }
         }
-        // the last router workgroup to arrive takes the top-k of every token for the whole layer
+    }
+    if constexpr (CENTRAL) {
+        // 3-4 tokens: the last router workgroup to arrive takes the top-k of every token (the gate/up
+        // workgroups would otherwise each redo it for all tokens)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's logit stores have completed
         __syncthreads();
         if (tid == 0)
@@ -729,7 +765,9 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
                       (unsigned)(a.n_router_wg - 1);
         __syncthreads();
         if (is_last) {
-            route<T>(a.logits, a.E, a.k, &st, ids, wts);
+            float lgv[8];
+            load_logits8_agent(a.logits + min(wv, T - 1) * a.E, a.E, lgv);
+            route_finish<T, true>(lgv, a.logits, a.E, a.k, &st, ids, wts);
             for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
                 ((int*)a.slots_out)[i] = ((const int*)&st)[i];
             for (int i = tid; i < T * a.k; i += blockDim.x) {
@@ -738,180 +776,114 @@ __global__ __launch_bounds__(320) void k1_router_shared(K1Args a) {
             }
             if (tid == 0) *a.ticket = 0u;  // read again only by the next layer's router, after this kernel
         }
-    } else {
-        // shared expert (index E), gate/up tile, every token
-        const int tile = blockIdx.x - a.n_router_wg, tiles = a.I / kGuOut;
-        GuLoads<BPL> L;
-        L.issue(a.w13, a.w13s, a.E, tile, tiles, NW);
-        if constexpr (CENTRAL) {
-            if (tid < T) sx[tid] = a.xs[tid];
-            for (int i = tid; i < T * H / 8; i += blockDim.x) {
-                const uint2 c = *(const uint2*)(a.xq + (size_t)i * 8);
-                half2_t* o = xh + i * 4;
-                o[0] = e4m3x2_to_f16x2(c.x & 0xffffu);
-                o[1] = e4m3x2_to_f16x2(c.x >> 16);
-                o[2] = e4m3x2_to_f16x2(c.y & 0xffffu);
-                o[3] = e4m3x2_to_f16x2(c.y >> 16);
-            }
-            __syncthreads();
-        } else {
-            moe_input<T>(a.x, H, a.normalize != 0, xb, red_d);
-            quantize_input<T>(xb, H, xh, wmax, sx, publish ? a.xq : nullptr, publish ? a.xs : nullptr,
-                              publish ? a.x_codes_out : nullptr, publish ? a.x_scale_out : nullptr);
-        }
-        int tok[T], pair[T];
-#pragma unroll
-        for (int j = 0; j < T; ++j) {
-            tok[j] = j;
-            pair[j] = j * (a.k + a.S) + a.k;
-        }
-        gateup_tile<T, BPL>(L, xh, H, sx, a.ntok, tok, pair, tile, a.I, a.h, a.hamax, red);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// k2: top-k + routed gate/up tiles + shared expert down rows
+// k2: top-k (redone by every routed workgroup) + gate/up tiles of the routed and shared experts
 // ------------------------------------------------------------------------------------------------
 
 struct K2Args {
-    const SlotTable* slots;  // routed experts of this layer
+    const float* logits;     // [T][E]
     const uint8_t* xq;       // [T][H] FP8 codes of the MoE input
     const float* xs;         // [T] their scales
     const uint4* w13;
     const uint8_t* w13s;
-    const uint4* w2;
-    const uint8_t* w2s;
     float* h;                // [pairs][I]
     float* hamax;            // [pairs][I/16]
-    float* dshared;          // [T][H]
-    int H, E, k, S, I, n_gu_wg;
+    SlotTable* slots;        // routed experts of this layer: stored here for the down kernel (1-2
+                             // tokens) or read (3-4 tokens, from the router kernel)
+    int32_t* ids_out;        // [T][k] or null
+    float* w_out;            // [T][k] or null
+    int H, E, k, S, I, n_sh_wg;
     int ntok;                // = T, at run time (keeps the shared expert's token loop a loop)
 };
 
-template <int T, int BPL, int KSUB, int ITERS>
+// Workgroups [0, n_sh_wg): the shared expert's gate/up tiles for every token (no routing needed).
+// The others: workgroup (slot, tile) takes the top-k of every token from the logits (one wave per
+// token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
+// tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
+// the weights.
+template <int T, int BPL>
 __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     extern __shared__ uint4 smem2[];
-    half2_t* xh = (half2_t*)smem2;                          // [T][H/2]
+    half2_t* xh = (half2_t*)smem2;  // [T][H/2] f16 values of the input's FP8 codes
     __shared__ float red[kMaxWaves * T * kGuRows];
     __shared__ float sx[T];
-    __shared__ float sh[T];
-    __shared__ int shp[T];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    __shared__ SlotTable st;
+    __shared__ int ids[T * kMaxTopK];
+    __shared__ float wts[T * kMaxTopK];
+    const int tid = threadIdx.x, NW = blockDim.x >> 6;
     const int H = a.H, I = a.I, k = a.k, tiles = I / kGuOut, NC = H / 8;
+    const bool is_shared = (int)blockIdx.x < a.n_sh_wg;
 
-    if ((int)blockIdx.x < a.n_gu_wg) {
-        // FP8 codes of the input: one 8-byte load per thread and token, issued first
-        uint2 xc[T];
+    // the input's FP8 codes, loaded first (one 8-byte load per thread and token), then the logits
+    uint2 xc[T];
+    const int xi = min(tid, NC - 1) * 8;  // loads unconditional (clamped), stores guarded
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            if (tid < NC) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + tid * 8);
-        const float sxv = a.xs[tid < T ? tid : 0];
-        const int slot = blockIdx.x / tiles, tile = blockIdx.x - slot * tiles;
-        // this workgroup's routed expert and its tokens (uniform loads)
-        const int n = a.slots->n, expert = a.slots->expert[slot < kMaxSlots ? slot : 0];
-        const int nt = a.slots->ntok[slot < kMaxSlots ? slot : 0];
-        int tok[T], pair[T];
+    for (int t = 0; t < T; ++t) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + xi);
+    const float sxv = a.xs[tid < T ? tid : 0];
+    // 1-2 tokens: every routed workgroup takes the top-k itself; 3-4 tokens: the router kernel did
+    constexpr bool ROUTE = T <= 2;
+    float lgv[8];
+    if constexpr (ROUTE) route_issue(a.logits, a.E, T, lgv);  // shared workgroups load them too: exact waits below
+
+    // f16 values of the codes into LDS while the logits are in flight
+    if (tid < T) sx[tid] = sxv;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (tid < NC) {
+            half2_t* o = xh + t * (H / 2) + tid * 4;
+            o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
+            o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
+            o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
+            o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
+        }
+    }
+
+    GuLoads<BPL> L;
+    int tok[T], pair[T], nt, tile;
+    if (is_shared) {
+        tile = blockIdx.x;
+        L.issue(a.w13, a.w13s, a.E, blockIdx.x, tiles, NW);
+        nt = a.ntok;
 #pragma unroll
         for (int j = 0; j < T; ++j) {
-            tok[j] = a.slots->tok[slot][j];
-            pair[j] = tok[j] * (k + a.S) + a.slots->rank[slot][j];
+            tok[j] = j;
+            pair[j] = j * (k + a.S) + k;
         }
-        if (slot >= n) return;
-        GuLoads<BPL> L;
-        L.issue(a.w13, a.w13s, expert, tile, tiles, NW);
-        if (tid < T) sx[tid] = sxv;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (tid < NC) {
-                half2_t* o = xh + t * (H / 2) + tid * 4;
-                o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
-                o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
-                o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
-                o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < T; ++j)
-            if (j >= nt) tok[j] = pair[j] = 0;
-        gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
     } else {
-        // shared expert down: each wave one R-row tile, every token
-        constexpr int R = kWave / KSUB;
-        const int rt = (blockIdx.x - a.n_gu_wg) * NW + wv, rtiles = H / R;
-        const int Ih = I / 2, ks = lane % KSUB;
-        uint4 wr[ITERS];
-        uint32_t sb[ITERS];
-        if (rt < rtiles) {
-            const size_t base = (((size_t)a.E * rtiles + rt) * ITERS) * kWave + lane;
-#pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                wr[it] = ld_nt(a.w2 + base + (size_t)it * kWave);
-                sb[it] = __builtin_nontemporal_load(a.w2s + base + (size_t)it * kWave);
-            }
-        }
-        // the shared expert's h of every token, loaded up front: thread -> column pairs q0, q0 + threads
-        const int nth = blockDim.x;
-        float2 hv[2][T];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int q = tid + c * nth;
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-                if (q < Ih && t < a.ntok) hv[c][t] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
-        }
-        // requantisation scales s_h = max|h| / 448
-        if (tid < T) shp[tid] = tid < a.ntok ? tid * (k + a.S) + k : -1;
-        __syncthreads();
-        requant_scales(a.hamax, tiles, shp, T, sh);
-        half2_t* hh = xh;  // [T][I/2]
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int q = tid + c * nth;
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-                if (q < Ih && t < a.ntok)
-                    hh[t * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(hv[c][t].x / sh[t], hv[c][t].y / sh[t]));
-        }
-        for (int q = tid + 2 * nth; q < Ih; q += nth) {  // more than two columns per thread (small H only)
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if (t < a.ntok) {
-                    const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + k) * I + 2 * q);
-                    hh[t * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / sh[t], v.y / sh[t]));
+        const int b = blockIdx.x - a.n_sh_wg, slot = b / tiles;
+        tile = b - slot * tiles;
+        if constexpr (ROUTE) {
+            route_finish<T>(lgv, a.logits, a.E, k, &st, ids, wts);
+            if (b == 0) {  // the first routed workgroup publishes the routing of the layer
+                for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
+                    ((int*)a.slots)[i] = ((const int*)&st)[i];
+                for (int i = tid; i < T * k; i += blockDim.x) {
+                    if (a.ids_out) a.ids_out[i] = ids[i];
+                    if (a.w_out) a.w_out[i] = wts[i];
                 }
             }
         }
-        __syncthreads();
-        if (rt < rtiles) {
-            float p[T];
+        // the slot's entries: from LDS (routed here) or straight from the stored list (uniform loads)
+        const SlotTable& sl = ROUTE ? st : *a.slots;
+        if (slot >= sl.n) return;
+        L.issue(a.w13, a.w13s, sl.expert[slot], tile, tiles, NW);
+        nt = sl.ntok[slot];
 #pragma unroll
-            for (int t = 0; t < T; ++t) p[t] = 0.0f;
-#pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                const float scale = e8m0_to_f32(sb[it]);
-                const int pbase = (it * KSUB + ks) * (kBlock / 2);
-                const half2_t* xp[T];
-#pragma unroll
-                for (int t = 0; t < T; ++t) xp[t] = hh + t * Ih + pbase;
-                float q[T];
-#pragma unroll
-                for (int t = 0; t < T; ++t) q[t] = 0.0f;
-                block_dot<T>(wr[it], xp, q, a.ntok);
-#pragma unroll
-                for (int t = 0; t < T; ++t) p[t] = fmaf(q[t], scale, p[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                p[t] = sum_ksub<KSUB>(p[t]);
-                if (ks == 0) a.dshared[(size_t)t * H + rt * R + lane / KSUB] = sh[t] * p[t];
-            }
+        for (int j = 0; j < T; ++j) {
+            const bool on = j < nt;
+            tok[j] = on ? sl.tok[slot][j] : 0;
+            pair[j] = on ? sl.tok[slot][j] * (k + a.S) + sl.rank[slot][j] : 0;
         }
     }
+    __syncthreads();
+    gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
 }
 
 // ------------------------------------------------------------------------------------------------
-// k3: routed down rows + combine + residual
+// k3: routed + shared down rows, combine, residual
 // ------------------------------------------------------------------------------------------------
 
 struct K3Args {
@@ -922,89 +894,61 @@ struct K3Args {
     const float* hamax;      // [pairs][I/16]
     const uint8_t* hq;       // [pairs][I] FP8 codes of h (3-4 tokens: from the requantisation kernel)
     const float* hs;         // [pairs] their scales
-    const float* dshared;    // [T][H] or null (no shared expert)
     const uint16_t* xres;    // [T][H] residual x_l, or null
     uint16_t* xnext;         // [T][H] bf16(x_l + y), or null
     float* y;                // [T][H] or null
-    int H, k, S, I;
+    int H, E, k, S, I;
 };
 
+// One workgroup per R-row output tile.  Work items ("slots") are the distinct routed experts of the
+// layer followed by the shared expert once per token (weight 1; one token per slot keeps the waves'
+// work even); wave w takes slots w, w + waves, ... (SPW at most).  h vectors are indexed by their
+// row t*(k+S) + r (r = k: shared expert).
 template <int KSUB, int ITERS, int T, int SPW>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     constexpr int R = kWave / KSUB;
     constexpr bool CODES = T >= 3;  // FP8 h codes from the requantisation kernel
-    constexpr int MAXP = CODES ? 1 : T == 1 ? 8 : 16;  // h columns (pairs) per thread, loaded up front
+    constexpr int MAXP = CODES ? 1 : T == 1 ? 9 : 18;  // h columns (rows of h) per thread, loaded up front
     extern __shared__ uint4 smem3[];
-    half2_t* hh = (half2_t*)smem3;  // [T*k][I/2], routed pair t*k + r
-    __shared__ float s_h[kMaxTokens * kMaxTopK];
-    __shared__ int s_pair[kMaxTokens * kMaxTopK];
-    __shared__ int s_expert[kMaxSlots], s_ntok[kMaxSlots], s_tok[kMaxSlots][kMaxTokens], s_rank[kMaxSlots][kMaxTokens];
-    __shared__ float s_w[kMaxSlots][kMaxTokens];
-    __shared__ int s_n;
+    half2_t* hh = (half2_t*)smem3;  // [T*(k+S)][I/2] f16 values of the FP8 codes of each h row
+    __shared__ float s_h[kMaxPairs];
+    __shared__ SlotTable s_st;  // copy of the routed slots; slot n (= s_st.n) is the shared expert
     __shared__ float red[16][T][R];
     const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6;
     const int H = a.H, I = a.I, k = a.k, Ih = I / 2, tiles = I / kGuOut, rtiles = H / R;
     const int tile = blockIdx.x, ks = lane % KSUB;
-    const int npairs = T * k;
-    // epilogue operands of this thread's output element (shared expert output, residual), loaded first
+    const int nrows = T * (k + a.S);
+    // epilogue operand of this thread's output element (residual), loaded first
     const int oe = tid < R * T ? tid : 0;
     const size_t oo = (size_t)(oe / R) * H + (size_t)tile * R + oe % R;
-    const float ds_pre = a.dshared ? a.dshared[oo] : 0.0f;
     const uint16_t xr_pre = a.xnext ? a.xres[oo] : (uint16_t)0;
-    // thread -> (column pair q, pair group g); G groups cover the pairs g, g + G, ...
+    // thread -> (column pair q, row group g); G groups cover the rows g, g + G, ...
     const int G = nth / Ih, q0 = tid % Ih, g0 = tid / Ih;
     const bool loader = !CODES && G > 0 && g0 < G;
 
-    // 1. independent loads: slot list, h of every routed pair (first MAXV * nth values)
-    const SlotTable* st = a.slots;
-    {
-        const int sl = tid & (kMaxSlots - 1);  // every thread loads (no branch), the first kMaxSlots store
-        const int nn = st->n, ex = st->expert[sl], nt = st->ntok[sl];
-        int tk[kMaxTokens], rk[kMaxTokens];
-        float ww[kMaxTokens];
-#pragma unroll
-        for (int j = 0; j < kMaxTokens; ++j) {
-            tk[j] = st->tok[sl][j];
-            rk[j] = st->rank[sl][j];
-            ww[j] = st->w[sl][j];
-        }
-        if (tid == 0) s_n = nn;
-        if (tid < kMaxSlots) {
-            s_expert[tid] = ex;
-            s_ntok[tid] = nt;
-#pragma unroll
-            for (int j = 0; j < kMaxTokens; ++j) {
-                s_tok[tid][j] = tk[j];
-                s_rank[tid][j] = rk[j];
-                s_w[tid][j] = ww[j];
-            }
-        }
-    }
-    if (tid < npairs) s_pair[tid] = (tid / k) * (k + a.S) + tid % k;
-    // tile maxima of this wave's pairs (p = wave + m * waves), loaded with everything else up front
+    // 1. independent loads, all issued before any is used: slot list, tile maxima of this wave's
+    // rows (row = wave + m * waves), h of every row (first MAXP * G rows).  Indices are clamped
+    // instead of branched on, so that the waits below stay exact.
+    constexpr int NSU = (int)(sizeof(SlotTable) / 16);  // 16-byte units of the slot list
+    static_assert(sizeof(SlotTable) % 16 == 0 && NSU <= 128, "slot list: one unit per thread of two waves");
+    const uint4 stu = ((const uint4*)a.slots)[min(tid, NSU - 1)];
     float hm[4];
     if constexpr (!CODES) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int p = min(wv + NW * m, npairs - 1);
-            hm[m] = a.hamax[(size_t)(p + (p / k) * a.S) * tiles + min(lane, tiles - 1)];
+            const int p = min(wv + NW * m, nrows - 1);
+            hm[m] = a.hamax[(size_t)p * tiles + min(lane, tiles - 1)];
         }
     }
-    // pair p = t*k + r lives at h row t*(k+S) + r = p + (p / k) * S; walk it without dividing
     float2 hv[MAXP];
-    if (loader) {
-        int p = g0, t = 0, r = g0;
-        while (r >= k) { r -= k; ++t; }
+    if constexpr (!CODES) {
+        const int qc = min(q0, Ih - 1);
 #pragma unroll
-        for (int m = 0; m < MAXP; ++m) {
-            if (p < npairs) hv[m] = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q0);
-            p += G;
-            r += G;
-            while (r >= k) { r -= k; ++t; }
-        }
+        for (int m = 0; m < MAXP; ++m) hv[m] = *(const float2*)(a.h + (size_t)min(g0 + m * G, nrows - 1) * I + 2 * qc);
     }
+    if (tid < NSU) ((uint4*)&s_st)[tid] = stu;
     __syncthreads();
-    const int n = s_n;
+    const int n = s_st.n, nall = n + a.S * T;  // routed slots, then the shared expert once per token
 
     // 2. down weight loads of this wave's slots
     uint4 wr[SPW][ITERS];
@@ -1012,8 +956,9 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
         const int s = wv + NW * m;
-        if (s < n) {
-            const size_t base = (((size_t)s_expert[s] * rtiles + tile) * ITERS) * kWave + lane;
+        if (s < nall) {
+            const int ex = s < n ? s_st.expert[s] : a.E;
+            const size_t base = (((size_t)ex * rtiles + tile) * ITERS) * kWave + lane;
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
                 wr[m][it] = ld_nt(a.w2 + base + (size_t)it * kWave);
@@ -1022,12 +967,12 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         }
     }
 
-    // 3. FP8 requantisation of every routed (token, rank) h vector into LDS (or its codes)
+    // 3. FP8 requantisation of every h row into LDS (or the decode of its codes)
     if constexpr (CODES) {
         const int I16 = I / 16;
-        for (int i = tid; i < npairs * I16; i += nth) {
+        for (int i = tid; i < nrows * I16; i += nth) {
             const int p = (unsigned)i / (unsigned)I16, c = i - p * I16;
-            const uint4 cw = *(const uint4*)(a.hq + (size_t)(p + (p / k) * a.S) * I + c * 16);
+            const uint4 cw = *(const uint4*)(a.hq + (size_t)p * I + c * 16);
             half2_t* o = hh + p * Ih + c * 8;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1035,35 +980,35 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
                 o[2 * q + 1] = e4m3x2_to_f16x2(comp(cw, q) >> 16);
             }
         }
-        if (tid < npairs) s_h[tid] = a.hs[s_pair[tid]];
+        if (tid < nrows) s_h[tid] = a.hs[tid];
         __syncthreads();
     } else {
-    for (int m = 0; m < 4 && wv + NW * m < npairs; ++m) {  // uniform per wave
-        const float mx = max64(lane < tiles ? hm[m] : 0.0f);
-        if (lane == 0) s_h[wv + NW * m] = mx > 0.0f ? mx / 448.0f : 1.0f;
-    }
-    for (int p = wv + 4 * NW; p < npairs; p += NW) {  // more pairs than 4 per wave (small grids)
-        float v = 0.0f;
-        for (int tl = lane; tl < tiles; tl += 64) v = fmaxf(v, a.hamax[(size_t)s_pair[p] * tiles + tl]);
-        const float mx = max64(v);
-        if (lane == 0) s_h[p] = mx > 0.0f ? mx / 448.0f : 1.0f;
-    }
-    __syncthreads();
-    if (loader) {
-#pragma unroll
-        for (int m = 0; m < MAXP; ++m) {
-            const int p = g0 + m * G;
-            if (p < npairs) hh[p * Ih + q0] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / s_h[p], hv[m].y / s_h[p]));
+        for (int m = 0; m < 4 && wv + NW * m < nrows; ++m) {  // uniform per wave
+            const float mx = max64(lane < tiles ? hm[m] : 0.0f);
+            if (lane == 0) s_h[wv + NW * m] = mx > 0.0f ? mx / 448.0f : 1.0f;
         }
-    }
-    // pairs beyond the up-front batch, or every pair when there are fewer threads than columns
-    const int p0 = G > 0 ? (G * MAXP < npairs ? G * MAXP : npairs) : 0;
-    for (int i = tid; i < (npairs - p0) * Ih; i += nth) {
-        const int p = p0 + i / Ih, q = i % Ih, t = p / k, r = p - t * k;
-        const float2 v = *(const float2*)(a.h + (size_t)(t * (k + a.S) + r) * I + 2 * q);
-        hh[p * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / s_h[p], v.y / s_h[p]));
-    }
-    __syncthreads();
+        for (int p = wv + 4 * NW; p < nrows; p += NW) {  // more rows than 4 per wave (small grids)
+            float v = 0.0f;
+            for (int tl = lane; tl < tiles; tl += 64) v = fmaxf(v, a.hamax[(size_t)p * tiles + tl]);
+            const float mx = max64(v);
+            if (lane == 0) s_h[p] = mx > 0.0f ? mx / 448.0f : 1.0f;
+        }
+        __syncthreads();
+        if (loader) {
+#pragma unroll
+            for (int m = 0; m < MAXP; ++m) {
+                const int p = g0 + m * G;
+                if (p < nrows) hh[p * Ih + q0] = e4m3x2_to_f16x2(e4m3_pack2(hv[m].x / s_h[p], hv[m].y / s_h[p]));
+            }
+        }
+        // rows beyond the up-front batch, or every row when there are fewer threads than columns
+        const int p0 = G > 0 ? (G * MAXP < nrows ? G * MAXP : nrows) : 0;
+        for (int i = tid; i < (nrows - p0) * Ih; i += nth) {
+            const int p = p0 + i / Ih, q = i % Ih;
+            const float2 v = *(const float2*)(a.h + (size_t)p * I + 2 * q);
+            hh[p * Ih + q] = e4m3x2_to_f16x2(e4m3_pack2(v.x / s_h[p], v.y / s_h[p]));
+        }
+        __syncthreads();
     }
 
     // 4. block dot products, routing-weighted into per-token accumulators
@@ -1073,11 +1018,14 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
         const int s = wv + NW * m;
-        if (s < n) {
-            const int nt = s_ntok[s];
+        if (s < nall) {
+            const bool shs = s >= n;  // the shared expert for token s - n: rank k, weight 1
+            const int si = min(s, kMaxSlots - 1), ts = s - n;
+            const int nt = shs ? 1 : s_st.ntok[si];
             int pp[T];
 #pragma unroll
-            for (int j = 0; j < T; ++j) pp[j] = j < nt ? s_tok[s][j] * k + s_rank[s][j] : 0;
+            for (int j = 0; j < T; ++j)
+                pp[j] = j < nt ? (shs ? ts * (k + a.S) + k : s_st.tok[si][j] * (k + a.S) + s_st.rank[si][j]) : 0;
             float pj[T];
 #pragma unroll
             for (int j = 0; j < T; ++j) pj[j] = 0.0f;
@@ -1099,8 +1047,8 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
 #pragma unroll
             for (int j = 0; j < T; ++j) {
                 if (j < nt) {
-                    const int tk = s_tok[s][j];
-                    const float cf = s_w[s][j] * s_h[pp[j]];
+                    const int tk = shs ? ts : s_st.tok[si][j];
+                    const float cf = (shs ? 1.0f : s_st.w[si][j]) * s_h[pp[j]];
 #pragma unroll
                     for (int t = 0; t < T; ++t)
                         if (t == tk) acc[t] = fmaf(cf, pj[j], acc[t]);
@@ -1109,7 +1057,7 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         }
     }
 
-    // 5. reduce over the KSUB lanes of a row, then over waves in wave order; add the shared expert
+    // 5. reduce over the KSUB lanes of a row, then over waves in wave order
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = sum_ksub<KSUB>(acc[t]);
     if (ks == 0) {
@@ -1122,7 +1070,6 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         float ysum = 0.0f;
         for (int w = 0; w < NW; ++w) ysum += red[w][t][r];
         const size_t o = (size_t)t * H + (size_t)tile * R + r;
-        ysum += idx == tid ? ds_pre : (a.dshared ? a.dshared[o] : 0.0f);
         if (a.y) a.y[o] = ysum;
         if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(idx == tid ? xr_pre : a.xres[o]) + ysum);
     }
@@ -1180,27 +1127,29 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
         k0_input<<<T, 1024, (size_t)sh.H * 2, stream>>>(a0);
     }
     const int n_router_wg = (sh.E + GW - 1) / GW;
-    K1Args a1{(const uint16_t*)L.router, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.x, P.xn, P.trace, P.logits,
-              P.xq, P.xs, P.x_scale, P.x_codes, P.h, P.hamax, P.ticket, P.slots, P.ids, P.w, sh.H, sh.E, sh.k,
-              sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
-    launch(k1_router_shared<T, BPL>, n_router_wg + sh.S * tiles, 64 * GW, (size_t)T * sh.H * 4, stream, ev, a1);
+    const int n_sh1 = CENTRAL ? sh.S * tiles : 0;  // shared gate/up tiles in the router kernel
+    K1Args a1{(const uint16_t*)L.router, P.x, P.xn, P.xq, P.xs, CENTRAL ? nullptr : P.trace,
+              CENTRAL ? nullptr : P.x_scale, CENTRAL ? nullptr : P.x_codes, P.logits, P.ticket, P.slots,
+              CENTRAL ? P.ids : nullptr, CENTRAL ? P.w : nullptr, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h,
+              P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
+    launch(k1_router<T, BPL>, n_router_wg + n_sh1, 64 * GW, (size_t)T * sh.H * 2, stream, ev, a1);
 
+    const int n_sh_wg = CENTRAL ? 0 : sh.S * tiles;  // 1-2 tokens: shared gate/up tiles here
     const int n_gu_wg = routed_slots_max(sh, T) * tiles;
-    const int n_sd_wg = sh.S ? (rtiles + GW - 1) / GW : 0;
-    K2Args a2{P.slots, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, (const uint4*)L.w2,
-              (const uint8_t*)L.w2s, P.h, P.hamax, P.dshared, sh.H, sh.E, sh.k, sh.S, sh.I, n_gu_wg, T};
+    K2Args a2{P.logits, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h, P.hamax, P.slots,
+              CENTRAL ? nullptr : P.ids, CENTRAL ? nullptr : P.w, sh.H, sh.E, sh.k, sh.S, sh.I, n_sh_wg, T};
     const size_t lds2 = (size_t)T * sh.H * 2;
-    launch(k2_gateup<T, BPL, KSUB, ITERS>, n_gu_wg + n_sd_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
+    launch(k2_gateup<T, BPL>, n_sh_wg + n_gu_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
 
     if (CENTRAL) {
-        KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I, sh.k, sh.S};
-        kq_requant<<<T * sh.k, 256, 0, stream>>>(aq);
+        KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
+        kq_requant<<<sh.pairs(T), 256, 0, stream>>>(aq);
     }
-    constexpr int SPW = T == 1 ? 1 : T == 2 ? 2 : 4;  // 3-4 tokens: 8 waves, two workgroups per CU
-    const int nw = (routed_slots_max(sh, T) + SPW - 1) / SPW;
-    K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, P.hq, P.hs, sh.S ? P.dshared : nullptr,
-              P.xnext ? P.x : nullptr, P.xnext, P.y, sh.H, sh.k, sh.S, sh.I};
-    const size_t lds3 = (size_t)T * sh.k * sh.I * 2;
+    constexpr int SPW = T == 1 ? 1 : T == 2 ? 3 : 5;  // slots per wave: at most 8 waves per workgroup
+    const int nw = std::max((routed_slots_max(sh, T) + sh.S * T + SPW - 1) / SPW, 2);  // >= 2: slot list copy
+    K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, P.hq, P.hs, P.xnext ? P.x : nullptr,
+              P.xnext, P.y, sh.H, sh.E, sh.k, sh.S, sh.I};
+    const size_t lds3 = (size_t)sh.pairs(T) * sh.I * 2;
     launch(k3_down<KSUB, ITERS, T, SPW>, rtiles, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
     return hipGetLastError();
 }

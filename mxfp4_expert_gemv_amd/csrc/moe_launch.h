@@ -22,16 +22,15 @@ struct RunPtrs {
     float* x_scale;     // [T] or null
     uint8_t* x_codes;   // [T][H] or null
     // workspace
-    uint8_t* xq;        // [T][H] FP8 codes of the MoE input
-    float* xs;          // [T] their scales
+    uint8_t* xq;        // 3-4 tokens: [T][H] FP8 codes of the MoE input
+    float* xs;          // 3-4 tokens: [T] their scales
     float* logits;      // [T][E]
-    unsigned* ticket;   // router arrivals (zero between layers)
+    unsigned* ticket;   // 3-4 tokens: router arrivals (zero between layers)
     SlotTable* slots;
     float* h;           // [T*(k+S)][I]
     float* hamax;       // [T*(k+S)][I/16]
-    float* dshared;     // [T][H] shared expert output
-    // 3-4 tokens: the layer's MoE input and the routed h codes, computed once per layer
     uint16_t* xn;       // [T][H] MoE input (bf16)
+    // 3-4 tokens: the FP8 codes of every h row, computed once per layer
     uint8_t* hq;        // [T*(k+S)][I] FP8 codes of h
     float* hs;          // [T*(k+S)] their scales
 };

@@ -41,7 +41,7 @@ def _status(cfg_kwargs):
 
 @pytest.mark.parametrize("bad,status", [
     ({"struct_size": 4}, -1), ({"hidden": 0}, -1), ({"top_k": 9, "num_experts": 8}, -1),
-    ({"hidden": 2500}, -2), ({"hidden": 4096}, -2), ({"num_experts": 1024}, -2), ({"top_k": 9}, -2),
+    ({"hidden": 2500}, -2), ({"hidden": 4096}, -2), ({"num_experts": 1024}, -2), ({"num_experts": 12, "top_k": 2}, -2), ({"top_k": 9}, -2),
     ({"num_shared": 2}, -2), ({"inter": 96}, -2), ({"inter": 1024}, -2), ({"max_tokens": 5}, -2),
     ({"flags": 0x80}, -1),
 ])
