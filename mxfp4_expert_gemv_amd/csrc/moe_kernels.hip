@@ -898,29 +898,33 @@ struct K3Args {
     uint16_t* xnext;         // [T][H] bf16(x_l + y), or null
     float* y;                // [T][H] or null
     int H, E, k, S, I;
+    int rows;                // output rows per workgroup (H / grid)
+    int units_max;           // (slot, row) units of the largest layer: (routed slots + S T) * rows
 };
 
-// One workgroup per R-row output tile.  Work items ("slots") are the distinct routed experts of the
-// layer followed by the shared expert once per token (weight 1; one token per slot keeps the waves'
-// work even); wave w takes slots w, w + waves, ... (SPW at most).  h vectors are indexed by their
-// row t*(k+S) + r (r = k: shared expert).
-template <int KSUB, int ITERS, int T, int SPW>
+// One workgroup per `rows` consecutive output rows (H / rows = one workgroup per CU, so no CU holds
+// two while others hold one).  Work items ("slots") are the distinct routed experts of the layer
+// followed by the shared expert once per token (weight 1).  The (slot, row) units are spread over
+// the waves, R = 64 / KSUB units per wave and group, KSUB lanes per unit (ITERS blocks of 32 each),
+// UPW groups per wave.  Each unit's routing-weighted result goes to LDS and the epilogue sums a
+// row's units in slot order.  h vectors are indexed by their row t*(k+S) + r (r = k: shared).
+template <int KSUB, int ITERS, int T, int UPW>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
-    constexpr int R = kWave / KSUB;
-    constexpr bool CODES = T >= 3;  // FP8 h codes from the requantisation kernel
-    constexpr int MAXP = CODES ? 1 : T == 1 ? 9 : 18;  // h columns (rows of h) per thread, loaded up front
+    constexpr int R = kWave / KSUB;  // units per wave and group; rows per repacked tile
+    constexpr bool CODES = T >= 3;   // FP8 h codes from the requantisation kernel
+    constexpr int MAXP = CODES ? 1 : T == 1 ? 5 : 9;  // h columns (rows of h) per thread, loaded up front
     extern __shared__ uint4 smem3[];
-    half2_t* hh = (half2_t*)smem3;  // [T*(k+S)][I/2] f16 values of the FP8 codes of each h row
-    __shared__ float s_h[kMaxPairs];
-    __shared__ SlotTable s_st;  // copy of the routed slots; slot n (= s_st.n) is the shared expert
-    __shared__ float red[16][T][R];
-    const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6;
     const int H = a.H, I = a.I, k = a.k, Ih = I / 2, tiles = I / kGuOut, rtiles = H / R;
-    const int tile = blockIdx.x, ks = lane % KSUB;
     const int nrows = T * (k + a.S);
-    // epilogue operand of this thread's output element (residual), loaded first
-    const int oe = tid < R * T ? tid : 0;
-    const size_t oo = (size_t)(oe / R) * H + (size_t)tile * R + oe % R;
+    half2_t* hh = (half2_t*)smem3;                     // [T*(k+S)][I/2] f16 values of h's FP8 codes
+    float* red = (float*)(hh + (size_t)nrows * Ih);    // [units][T] routing-weighted unit results
+    __shared__ float s_h[kMaxPairs];
+    __shared__ SlotTable s_st;  // copy of the routed slots
+    const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6;
+    const int RW = a.rows, row0 = blockIdx.x * RW, ks = lane % KSUB;
+    // epilogue operand of this thread's output element (row row0 + tid % RW, token tid / RW)
+    const int oe = tid < RW * T ? tid : 0;
+    const size_t oo = (size_t)(oe / RW) * H + row0 + oe % RW;
     const uint16_t xr_pre = a.xnext ? a.xres[oo] : (uint16_t)0;
     // thread -> (column pair q, row group g); G groups cover the rows g, g + G, ...
     const int G = nth / Ih, q0 = tid % Ih, g0 = tid / Ih;
@@ -948,22 +952,31 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     }
     if (tid < NSU) ((uint4*)&s_st)[tid] = stu;
     __syncthreads();
-    const int n = s_st.n, nall = n + a.S * T;  // routed slots, then the shared expert once per token
+    const int n = s_st.n, nall = n + a.S * T, nunits = nall * RW;  // routed slots, then shared per token
 
-    // 2. down weight loads of this wave's slots
-    uint4 wr[SPW][ITERS];
-    uint32_t sb[SPW][ITERS];
+    // 2. down weight loads of this wave's units: unit u = (wave + NW m) R + lane / KSUB is slot
+    // u / RW, row row0 + u % RW (units past the last repeat it; their results are not stored).
+    // With KSUB = 8 the unit's ITERS x 8 scale bytes come in as one dword per lane (lanes
+    // ks < 2 ITERS) and are handed to their lanes by ds_bpermute: one load instead of ITERS.
+    static_assert(KSUB != 8 || ITERS <= 4, "scale bytes of a unit: one dword per lane");
+    uint4 wr[UPW][ITERS];
+    uint32_t sw[UPW][KSUB == 8 ? 1 : ITERS];
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-        const int s = wv + NW * m;
-        if (s < nall) {
-            const int ex = s < n ? s_st.expert[s] : a.E;
-            const size_t base = (((size_t)ex * rtiles + tile) * ITERS) * kWave + lane;
+    for (int m = 0; m < UPW; ++m) {
+        const int u = min((wv + NW * m) * R + lane / KSUB, nunits - 1);
+        const int s = u / RW, r = row0 + (u - s * RW);
+        const int ex = s < n ? s_st.expert[s] : a.E;
+        const size_t tb = ((size_t)ex * rtiles + r / R) * ITERS;  // first 1 KiB unit of the row's tile
+        const int lo = (r % R) * KSUB + ks;
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                wr[m][it] = ld_nt(a.w2 + base + (size_t)it * kWave);
-                sb[m][it] = __builtin_nontemporal_load(a.w2s + base + (size_t)it * kWave);
-            }
+        for (int it = 0; it < ITERS; ++it) wr[m][it] = ld_nt(a.w2 + (tb + it) * kWave + lo);
+        if constexpr (KSUB == 8) {
+            const int j = ks % (2 * ITERS);  // dword j: iteration j / 2, half j % 2
+            sw[m][0] = __builtin_nontemporal_load(
+                (const uint32_t*)(a.w2s + (tb + j / 2) * kWave + (size_t)(r % R) * KSUB) + (j & 1));
+        } else {
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) sw[m][it] = __builtin_nontemporal_load(a.w2s + (tb + it) * kWave + lo);
         }
     }
 
@@ -1011,65 +1024,72 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         __syncthreads();
     }
 
-    // 4. block dot products, routing-weighted into per-token accumulators
-    float acc[T];
+    // 4. block dot products of each unit, routing-weighted per token, reduced over the unit's lanes
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+    for (int m = 0; m < UPW; ++m) {
+        const int u0 = (wv + NW * m) * R + lane / KSUB, u = min(u0, nunits - 1);
+        const int s = u / RW;
+        const bool shs = s >= n;  // the shared expert for token s - n: rank k, weight 1
+        const int si = min(s, kMaxSlots - 1), ts = s - n;
+        const int nt = shs ? 1 : s_st.ntok[si];
+        int pp[T];
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-        const int s = wv + NW * m;
-        if (s < nall) {
-            const bool shs = s >= n;  // the shared expert for token s - n: rank k, weight 1
-            const int si = min(s, kMaxSlots - 1), ts = s - n;
-            const int nt = shs ? 1 : s_st.ntok[si];
-            int pp[T];
+        for (int j = 0; j < T; ++j)
+            pp[j] = j < nt ? (shs ? ts * (k + a.S) + k : s_st.tok[si][j] * (k + a.S) + s_st.rank[si][j]) : 0;
+        float pj[T];
 #pragma unroll
-            for (int j = 0; j < T; ++j)
-                pp[j] = j < nt ? (shs ? ts * (k + a.S) + k : s_st.tok[si][j] * (k + a.S) + s_st.rank[si][j]) : 0;
-            float pj[T];
+        for (int j = 0; j < T; ++j) pj[j] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < T; ++j) pj[j] = 0.0f;
-#pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                const float scale = e8m0_to_f32(sb[m][it]);
-                const int pbase = (it * KSUB + ks) * (kBlock / 2);
-                const half2_t* xp[T];
-#pragma unroll
-                for (int j = 0; j < T; ++j) xp[j] = hh + pp[j] * Ih + pbase;
-                float q[T];
-#pragma unroll
-                for (int j = 0; j < T; ++j) q[j] = 0.0f;
-                block_dot<T>(wr[m][it], xp, q, nt);
-#pragma unroll
-                for (int j = 0; j < T; ++j) pj[j] = fmaf(q[j], scale, pj[j]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int it = 0; it < ITERS; ++it) {
+            uint32_t sbyte;
+            if constexpr (KSUB == 8) {
+                const uint32_t sd = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                    ((lane & ~7) + 2 * it + (ks >> 2)) * 4, (int)sw[m][0]);
+                sbyte = sd >> (8 * (ks & 3));
+            } else {
+                sbyte = sw[m][it];
             }
+            const float scale = e8m0_to_f32(sbyte & 0xffu);
+            const int pbase = (it * KSUB + ks) * (kBlock / 2);
+            const half2_t* xp[T];
 #pragma unroll
-            for (int j = 0; j < T; ++j) {
-                if (j < nt) {
-                    const int tk = shs ? ts : s_st.tok[si][j];
-                    const float cf = (shs ? 1.0f : s_st.w[si][j]) * s_h[pp[j]];
+            for (int j = 0; j < T; ++j) xp[j] = hh + pp[j] * Ih + pbase;
+            float q[T];
 #pragma unroll
-                    for (int t = 0; t < T; ++t)
-                        if (t == tk) acc[t] = fmaf(cf, pj[j], acc[t]);
-                }
+            for (int j = 0; j < T; ++j) q[j] = 0.0f;
+            block_dot<T>(wr[m][it], xp, q, nt);
+#pragma unroll
+            for (int j = 0; j < T; ++j) pj[j] = fmaf(q[j], scale, pj[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float v[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) v[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            if (j < nt) {
+                const int tk = shs ? ts : s_st.tok[si][j];
+                const float cf = (shs ? 1.0f : s_st.w[si][j]) * s_h[pp[j]];
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    if (t == tk) v[t] = fmaf(cf, pj[j], v[t]);
             }
         }
-    }
-
-    // 5. reduce over the KSUB lanes of a row, then over waves in wave order
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = sum_ksub<KSUB>(acc[t]);
-    if (ks == 0) {
+        for (int t = 0; t < T; ++t) v[t] = sum_ksub<KSUB>(v[t]);
+        if (ks == 0 && u0 < nunits) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) red[wv][t][lane / KSUB] = acc[t];
+            for (int t = 0; t < T; ++t) red[u0 * T + t] = v[t];
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < R * T; idx += nth) {  // one pass: R * T <= threads
-        const int t = idx / R, r = idx - t * R;
+
+    // 5. each output row: its units summed in slot order (routed slots, then shared)
+    for (int idx = tid; idx < RW * T; idx += nth) {
+        const int t = idx / RW, r = idx - t * RW;
         float ysum = 0.0f;
-        for (int w = 0; w < NW; ++w) ysum += red[w][t][r];
-        const size_t o = (size_t)t * H + (size_t)tile * R + r;
+        for (int s = 0; s < nall; ++s) ysum += red[(s * RW + r) * T + t];
+        const size_t o = (size_t)t * H + row0 + r;
         if (a.y) a.y[o] = ysum;
         if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(idx == tid ? xr_pre : a.xres[o]) + ysum);
     }
@@ -1120,7 +1140,7 @@ static void launch(Kern kern, unsigned grid, unsigned block, size_t lds, hipStre
 template <int T, int BPL, int KSUB, int ITERS>
 static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev) {
-    const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows(), rtiles = sh.H / R;
+    const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows();
     constexpr bool CENTRAL = T >= 3;  // input and h requantisation once per layer (k0, kq)
     if (CENTRAL) {
         K0Args a0{P.x, P.xn, P.xq, P.xs, P.trace, P.x_scale, P.x_codes, sh.H, normalize ? 1 : 0};
@@ -1145,12 +1165,17 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
         KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
         kq_requant<<<sh.pairs(T), 256, 0, stream>>>(aq);
     }
-    constexpr int SPW = T == 1 ? 1 : T == 2 ? 3 : 5;  // slots per wave: at most 8 waves per workgroup
-    const int nw = std::max((routed_slots_max(sh, T) + sh.S * T + SPW - 1) / SPW, 2);  // >= 2: slot list copy
+    // down: one workgroup per CU-sized share of the rows; (slot, row) units spread over up to 12
+    // waves, UPW groups of 64 / KSUB units per wave
+    constexpr int UPW = T;
+    const int rows = sh.H / kDownGrid;
+    const int units_max = (routed_slots_max(sh, T) + sh.S * T) * rows, groups = (units_max + R - 1) / R;
+    const int nw = std::max(std::min(groups, 12), 2);  // >= 2: slot list copy
+    if (nw * UPW < groups) return hipErrorInvalidValue;
     K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, P.hq, P.hs, P.xnext ? P.x : nullptr,
-              P.xnext, P.y, sh.H, sh.E, sh.k, sh.S, sh.I};
-    const size_t lds3 = (size_t)sh.pairs(T) * sh.I * 2;
-    launch(k3_down<KSUB, ITERS, T, SPW>, rtiles, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
+              P.xnext, P.y, sh.H, sh.E, sh.k, sh.S, sh.I, rows, units_max};
+    const size_t lds3 = (size_t)sh.pairs(T) * sh.I * 2 + (size_t)units_max * T * 4;
+    launch(k3_down<KSUB, ITERS, T, UPW>, kDownGrid, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
     return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
 constexpr int kGuRows = 32;         // rows per gate/up tile: 16 gate + 16 up
 constexpr int kGuOut = 16;          // h outputs per gate/up tile
 constexpr int kMaxWaves = 5;        // waves per workgroup of the router / gate/up kernels
+constexpr int kDownGrid = 256;      // workgroups of the down kernel: one per compute unit (H % 256 == 0)
 
 // Work list of the routed experts of one call, built identically by every workgroup of the
 // gate/up kernel from the router logits (workgroup 0 also stores it for the down kernel).
