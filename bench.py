@@ -39,6 +39,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
+    ap.add_argument("--no-head", action="store_true", help="skip the FP8 LM-head measurement")
     ap.add_argument("--variant", choices=("persistent", "three_kernels"), default="three_kernels",
                     help="kernel set: three kernels per layer (default, the faster one) or one persistent kernel per pass")
     ap.add_argument("--copy-probe", action="store_true",
@@ -197,6 +198,8 @@ def main():
                 "bytes_per_launch": kb[dom], "us_per_launch": round(kt1[dom], 3), "all_kernels_t1": per_kernel}
     log(f"roofline: dominant {names[dom]} {kt1[dom]:.2f} us/launch, {achieved:.0f} GB/s; {per_kernel}")
 
+    head = None if args.no_head else time_head(moe, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, st, x4_host[:1], expert_bytes, router_bytes)
@@ -210,7 +213,8 @@ def main():
            "us_per_layer": round(r1["us_per_layer"], 3), "tokens_per_s": round(r1["tokens_per_s"], 1),
            "pct_of_hbm_peak": round(r1["pct_of_hbm_peak"], 2), "kernel_us_t1": r1["kernel_us"],
            "stack_t4": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[4].items()},
-           "single_layer": single, "variant": info["variant"], "roofline": roofline, "cpu_baseline": cpu}
+           "single_layer": single, "lm_head": head, "variant": info["variant"], "roofline": roofline,
+           "cpu_baseline": cpu}
     moe.moe_decode_destroy(h)
     print(json.dumps(out), flush=True)
 
@@ -330,6 +334,41 @@ def kernel_names(variant, T):
     return {"router": f"void moe::k1_router<{T}, {bpl}>(moe::K1Args)",
             "gateup": f"void moe::k2_gateup<{T}, {bpl}>(moe::K2Args)",
             "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}
+
+
+def time_head(moe, dev, stream, steps=50, warmup=5):
+    """The FP8 LM head (vocab 157,184 x hidden 2,560, E4M3 rows with fp32 row scales, argmax only)
+    at 1 and 4 tokens, back to back (its 403 MB exceed the 256 MB last-level cache).  Random codes
+    (no NaN pattern) and scales: the timing does not depend on the values."""
+    import torch
+
+    V, H = 157184, 2560
+    w = torch.randint(0, 0x7E, (V, H), dtype=torch.uint8, device=dev)
+    w |= torch.randint(0, 2, (V, H), dtype=torch.uint8, device=dev) << 7
+    scale = torch.full((V,), 1e-3, dtype=torch.float32, device=dev)
+    hd = moe.fp8_head_create(w, scale)
+    torch.cuda.synchronize()
+    del w
+    x = torch.randn((4, H), device=dev).to(torch.bfloat16)
+    am = torch.empty((4,), dtype=torch.int32, device=dev)
+    nbytes = V * H + V * 4
+    out = {"vocab": V, "hidden": H, "bytes_per_call": nbytes}
+    for T in (1, 4):
+        for _ in range(warmup):
+            moe.fp8_head_run(hd, x[:T], am[:T])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            moe.fp8_head_run(hd, x[:T], am[:T])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[f"t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        log(f"LM head T={T}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    moe.fp8_head_destroy(hd)
+    return out
 
 
 def cpu_baseline(shape, st, x_host, expert_bytes, router_bytes, budget_s=12.0):

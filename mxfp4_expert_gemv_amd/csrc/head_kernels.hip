@@ -129,23 +129,25 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
             if (a.logits) a.logits[(size_t)t * a.V + row] = v;
         }
         for (int off = 32; off > 0; off >>= 1) better(v, idx, __shfl_xor(v, off, 64), __shfl_xor(idx, off, 64));
-        if (lane == 0) {
-            a.pval[(size_t)vt * T + t] = v;
-            a.pidx[(size_t)vt * T + t] = idx;
+        if (lane == 0) {  // write-through: the last workgroup reads them without any cache flush
+            __hip_atomic_store(a.pval + (size_t)vt * T + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.pidx + (size_t)vt * T + t, idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __threadfence();
+    // the last workgroup to arrive reduces the per-tile maxima.  No fence: the partials were written
+    // through to the device-coherent level, and vmcnt(0) waits for those stores to complete.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (tid == 0) is_last = atomicAdd(a.ticket, 1u) == (unsigned)(VT - 1);
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
     for (int t = wv; t < T; t += NW) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         for (int i = lane; i < VT; i += kWave)
-            better(bv, bi, __builtin_nontemporal_load(a.pval + (size_t)i * T + t),
-                   __builtin_nontemporal_load(a.pidx + (size_t)i * T + t));
+            better(bv, bi, __hip_atomic_load(a.pval + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                   __hip_atomic_load(a.pidx + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         for (int off = 32; off > 0; off >>= 1) better(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
         if (lane == 0) a.argmax[t] = bi;
     }

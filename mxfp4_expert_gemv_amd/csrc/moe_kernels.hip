@@ -950,6 +950,16 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
 #pragma unroll
         for (int m = 0; m < MAXP; ++m) hv[m] = *(const float2*)(a.h + (size_t)min(g0 + m * G, nrows - 1) * I + 2 * qc);
     }
+    // 3-4 tokens: the h codes (16 per unit) and scales
+    constexpr int HQ = CODES ? 3 : 1;  // code units per thread loaded up front
+    const int nq = nrows * (I / 16);
+    uint4 hqv[HQ];
+    float hsv = 0.0f;
+    if constexpr (CODES) {
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) hqv[m] = *(const uint4*)(a.hq + (size_t)min(tid + m * nth, nq - 1) * 16);
+        hsv = a.hs[min(tid, nrows - 1)];
+    }
     if (tid < NSU) ((uint4*)&s_st)[tid] = stu;
     __syncthreads();
     const int n = s_st.n, nall = n + a.S * T, nunits = nall * RW;  // routed slots, then shared per token
@@ -982,18 +992,29 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
 
     // 3. FP8 requantisation of every h row into LDS (or the decode of its codes)
     if constexpr (CODES) {
-        const int I16 = I / 16;
-        for (int i = tid; i < nrows * I16; i += nth) {
-            const int p = (unsigned)i / (unsigned)I16, c = i - p * I16;
-            const uint4 cw = *(const uint4*)(a.hq + (size_t)p * I + c * 16);
-            half2_t* o = hh + p * Ih + c * 8;
+        // unit i of h's codes (16 codes) -> 8 f16 pairs at hh + 8 i (rows of I/16 units are contiguous)
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) {
+            const int i = tid + m * nth;
+            if (i < nq) {
+                half2_t* o = hh + (size_t)i * 8;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    o[2 * q] = e4m3x2_to_f16x2(comp(hqv[m], q) & 0xffffu);
+                    o[2 * q + 1] = e4m3x2_to_f16x2(comp(hqv[m], q) >> 16);
+                }
+            }
+        }
+        for (int i = tid + HQ * nth; i < nq; i += nth) {  // more units than threads can preload
+            const uint4 cw = *(const uint4*)(a.hq + (size_t)i * 16);
+            half2_t* o = hh + (size_t)i * 8;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 o[2 * q] = e4m3x2_to_f16x2(comp(cw, q) & 0xffffu);
                 o[2 * q + 1] = e4m3x2_to_f16x2(comp(cw, q) >> 16);
             }
         }
-        if (tid < nrows) s_h[tid] = a.hs[tid];
+        if (tid < nrows) s_h[tid] = hsv;
         __syncthreads();
     } else {
         for (int m = 0; m < 4 && wv + NW * m < nrows; ++m) {  // uniform per wave
