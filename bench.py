@@ -332,7 +332,7 @@ def kernel_names(variant, T):
     ksub, iters = (int(v) for v in dn[2:].split("x"))
     spw = 1 if T == 1 else 2 if T == 2 else 4
     return {"router": f"void moe::k1_router<{T}, {bpl}>(moe::K1Args)",
-            "gateup": f"void moe::k2_gateup<{T}, {bpl}>(moe::K2Args)",
+            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {4 if T == 1 else 2 if T == 2 else 1}>(moe::K2Args)",
             "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}
 
 

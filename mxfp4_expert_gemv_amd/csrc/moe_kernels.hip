@@ -416,25 +416,38 @@ __device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, con
     }
 }
 
-// Top-k of every token, one wave per token.  Lane l holds experts 8l..8l+7 and sorts them by
-// (logit descending, index ascending) with 64-bit keys; then each of the k rounds takes the
-// wave-wide maximum of the lanes' head logits (32-bit order-preserving codes) through lane
-// exchanges, the lowest lane holding it wins (lower lanes hold lower experts, so ties go to the
-// lower index) and pops its head.  Lane r keeps the winner of round r, so the softmax over the
-// selected logits runs across lanes 0..k-1.  (A six-level bitonic merge tree across lanes, and
-// 64-bit keys in the rounds, measured slower: a single wave is bound by its instruction count.)
-// Then the list of distinct routed experts; everything lands in LDS.
+// Top-k.  One wave takes the top-k of a run of 64 P consecutive experts: lane l holds experts
+// base + P l .. base + P l + P - 1 and sorts them by (logit descending, index ascending) with
+// 64-bit keys; then each of the k rounds takes the wave-wide maximum of the lanes' head logits
+// (32-bit order-preserving codes) through lane exchanges, the lowest lane holding it wins (lower
+// lanes hold lower experts, so ties go to the lower index) and pops its head.  Lane r keeps the
+// winner of round r.  With one wave per token (P = 8) that is the answer; with W waves per token
+// (P = 8 / W) the first wave of the token merges the W candidate lists the same way, one
+// candidate per lane in (wave, rank) order, which again sends ties to the lower index.  The
+// softmax over the selected logits runs across lanes 0..k-1.  (A six-level bitonic merge tree
+// across lanes, and 64-bit keys in the rounds, measured slower: a single wave is bound by its
+// instruction count.)  Then the list of distinct routed experts; everything lands in LDS.
 //
-// route_issue loads the logits of this wave's first token (token = wave index, if below T) so
-// that the caller can overlap other work with their latency; route_finish completes the
-// selection (further tokens of this wave, on small workgroups, are loaded there).
-// The 8 logits of this lane, experts 8 lane .. 8 lane + 7 (E is a multiple of 8; lanes beyond E
-// reload the last 8): two 16-byte loads.
-__device__ __forceinline__ void load_logits8(const float* row, int E, float (&v)[8]) {
-    const float4* p = (const float4*)(row + min((int)(threadIdx.x & 63) * 8, E - 8));
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+// route_issue loads the logits so that the caller can overlap other work with their latency;
+// route_finish completes the selection (on small workgroups, tokens beyond the waves are loaded
+// there).
+
+// P logits of this lane from row[base + P lane ..] (E a multiple of 8; lanes past E reload the
+// last P, their keys are dropped).
+template <int P>
+__device__ __forceinline__ void load_logits(const float* row, int base, int E, float (&v)[P]) {
+    const float* p = row + min(base + (int)(threadIdx.x & 63) * P, E - P);
+    if constexpr (P == 8) {
+        const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else if constexpr (P == 4) {
+        const float4 a = *(const float4*)p;
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    } else {
+        const float2 a = *(const float2*)p;
+        v[0] = a.x; v[1] = a.y;
+    }
 }
 
 // The same from logits that other workgroups of the running kernel stored with device-scope stores.
@@ -444,79 +457,96 @@ __device__ __forceinline__ void load_logits8_agent(const float* row, int E, floa
     for (int j = 0; j < 8; ++j) v[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every wave loads (waves beyond the last token repeat it), so that the number of loads in flight
-// is the same on every path and later waits stay exact.
-__device__ __forceinline__ void route_issue(const float* logits, int E, int T, float (&lgv)[8]) {
-    load_logits8(logits + min((int)(threadIdx.x >> 6), T - 1) * E, E, lgv);
+// W waves per token: wave v takes token v / W, experts (v % W) 64 P ...  Every wave loads (waves
+// past the last token repeat it), so that the number of loads in flight is the same on every path
+// and later waits stay exact.
+template <int T, int W>
+__device__ __forceinline__ void route_issue(const float* logits, int E, float (&lgv)[8 / W]) {
+    constexpr int P = 8 / W;
+    const int wv = threadIdx.x >> 6, t = min(wv / W, T - 1);
+    load_logits<P>(logits + t * E, (wv % W) * 64 * P, E, lgv);
 }
 
-template <int T, bool AGENT = false>
-__device__ void route_finish(const float (&lgv0)[8], const float* logits, int E, int k, SlotTable* st, int* ids,
-                             float* wts) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    for (int t = wv; t < T; t += NW) {
-        float lgv[8];
-        if (t == wv) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+    m = max(m, xchg<0>(m));
+    m = max(m, xchg<1>(m));
+    m = max(m, xchg<2>(m));
+    m = max(m, xchg<3>(m));
+    m = max(m, xchg<4>(m));
+    return max(m, xchg<5>(m));
+}
+
+// One wave's top-k of its P logits per lane (experts base + P lane + j): lane r < k returns the
+// order code and expert of rank r.
+template <int P>
+__device__ __forceinline__ void wave_topk(const float (&lgv)[P], int base, int E, int k, uint32_t& my_code,
+                                          int& my_id) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[P];  // order code of the logit above, 7 - j below; 0 = no expert
 #pragma unroll
-            for (int j = 0; j < 8; ++j) lgv[j] = lgv0[j];
-        } else if (AGENT) {
-            load_logits8_agent(logits + t * E, E, lgv);
-        } else {
-            load_logits8(logits + t * E, E, lgv);
-        }
-        uint64_t key[8];  // order code of the logit above, 7 - j below; 0 = no expert
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t u = __float_as_uint(lgv[j] + 0.0f);  // -0 -> +0
-            const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-            key[j] = lane * 8 + j < E ? ((uint64_t)o << 32) | (uint32_t)(7 - j) : 0ull;
-        }
+    for (int j = 0; j < P; ++j) {
+        const uint32_t u = __float_as_uint(lgv[j] + 0.0f);  // -0 -> +0
+        const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        key[j] = base + lane * P + j < E ? ((uint64_t)o << 32) | (uint32_t)(7 - j) : 0ull;
+    }
+    if constexpr (P == 8) {
         cx_desc(key[0], key[1]); cx_desc(key[2], key[3]); cx_desc(key[4], key[5]); cx_desc(key[6], key[7]);
         cx_desc(key[0], key[2]); cx_desc(key[1], key[3]); cx_desc(key[4], key[6]); cx_desc(key[5], key[7]);
         cx_desc(key[1], key[2]); cx_desc(key[5], key[6]);
         cx_desc(key[0], key[4]); cx_desc(key[1], key[5]); cx_desc(key[2], key[6]); cx_desc(key[3], key[7]);
         cx_desc(key[2], key[4]); cx_desc(key[3], key[5]);
         cx_desc(key[1], key[2]); cx_desc(key[3], key[4]); cx_desc(key[5], key[6]);
-        uint32_t hv[8], hj = 0;  // head codes; the lane-local positions 7 - j, 4 bits each
+    } else if constexpr (P == 4) {
+        cx_desc(key[0], key[1]); cx_desc(key[2], key[3]);
+        cx_desc(key[0], key[2]); cx_desc(key[1], key[3]);
+        cx_desc(key[1], key[2]);
+    } else {
+        cx_desc(key[0], key[1]);
+    }
+    uint32_t hv[P], hj = 0;  // head codes; the lane-local positions 7 - j, 4 bits each
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            hv[i] = (uint32_t)(key[i] >> 32);
-            hj |= ((uint32_t)key[i] & 7u) << (4 * i);
-        }
-        int my_id = 0;
-        uint32_t my_code = 0;
-        for (int r = 0; r < k; ++r) {
-            uint32_t m = hv[0];
-            m = max(m, xchg<0>(m));
-            m = max(m, xchg<1>(m));
-            m = max(m, xchg<2>(m));
-            m = max(m, xchg<3>(m));
-            m = max(m, xchg<4>(m));
-            m = max(m, xchg<5>(m));
-            const int w = (int)__builtin_ctzll(__ballot(hv[0] == m));  // lowest lane with the maximum
-            const int id = w * 8 + 7 - (int)(__builtin_amdgcn_readlane(hj, w) & 7u);
-            my_id = lane == r ? id : my_id;
-            my_code = lane == r ? m : my_code;
-            if (lane == w) {
+    for (int i = 0; i < P; ++i) {
+        hv[i] = (uint32_t)(key[i] >> 32);
+        hj |= ((uint32_t)key[i] & 7u) << (4 * i);
+    }
+    my_id = 0;
+    my_code = 0;
+    for (int r = 0; r < k; ++r) {
+        const uint32_t m = wave_max_u32(hv[0]);
+        const int w = (int)__builtin_ctzll(__ballot(hv[0] == m));  // lowest lane with the maximum
+        const int id = base + w * P + 7 - (int)(__builtin_amdgcn_readlane(hj, w) & 7u);
+        my_id = lane == r ? id : my_id;
+        my_code = lane == r ? m : my_code;
+        if (lane == w) {
 #pragma unroll
-                for (int i = 0; i < 7; ++i) hv[i] = hv[i + 1];
-                hv[7] = 0u;
-                hj >>= 4;
-            }
-        }
-        const float lg = __uint_as_float((my_code & 0x80000000u) ? (my_code & 0x7fffffffu) : ~my_code);
-        const float l0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg)));  // the maximum
-        const float z = lane < k ? expf(lg - l0) : 0.0f;
-        float zs = z + xchg<0>(z);
-        zs += xchg<1>(zs);
-        zs += xchg<2>(zs);  // lanes 0..7 now all hold the sum over lanes 0..7 (k <= 8)
-        if (lane < k) {
-            ids[t * k + lane] = my_id;
-            wts[t * k + lane] = z / zs;
+            for (int i = 0; i < P - 1; ++i) hv[i] = hv[i + 1];
+            hv[P - 1] = 0u;
+            hj >>= 4;
         }
     }
+}
+
+// Softmax of the selected logits (lanes 0..k-1 hold rank r's code and expert) into ids / wts.
+__device__ __forceinline__ void topk_softmax(uint32_t my_code, int my_id, int k, int* ids, float* wts) {
+    const int lane = threadIdx.x & 63;
+    const float lg = __uint_as_float((my_code & 0x80000000u) ? (my_code & 0x7fffffffu) : ~my_code);
+    const float l0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg)));  // the maximum
+    const float z = lane < k ? expf(lg - l0) : 0.0f;
+    float zs = z + xchg<0>(z);
+    zs += xchg<1>(zs);
+    zs += xchg<2>(zs);  // lanes 0..7 now all hold the sum over lanes 0..7 (k <= 8)
+    if (lane < k) {
+        ids[lane] = my_id;
+        wts[lane] = z / zs;
+    }
+}
+
+// Distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair.
+// Starts and ends with a barrier.
+template <int T>
+__device__ void build_slots(int k, SlotTable* st, const int* ids, const float* wts) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     __syncthreads();
-    // distinct experts in order of first appearance (token, then rank); one lane per (t, r) pair
     if (T == 1) {  // one token: its k experts are distinct, slot r is rank r
         if (tid < k) {
             st->expert[tid] = ids[tid];
@@ -552,6 +582,65 @@ __device__ void route_finish(const float (&lgv0)[8], const float* logits, int E,
         if (lane == 0) st->n = __popcll(firsts);
     }
     __syncthreads();
+}
+
+// One wave per token (waves past the last token loop, on small workgroups).
+template <int T, bool AGENT = false>
+__device__ void route_finish(const float (&lgv0)[8], const float* logits, int E, int k, SlotTable* st, int* ids,
+                             float* wts) {
+    const int wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    for (int t = wv; t < T; t += NW) {
+        float lgv[8];
+        if (t == wv) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lgv[j] = lgv0[j];
+        } else if (AGENT) {
+            load_logits8_agent(logits + t * E, E, lgv);
+        } else {
+            load_logits<8>(logits + t * E, 0, E, lgv);
+        }
+        uint32_t my_code;
+        int my_id;
+        wave_topk<8>(lgv, 0, E, k, my_code, my_id);
+        topk_softmax(my_code, my_id, k, ids + t * k, wts + t * k);
+    }
+    build_slots<T>(k, st, ids, wts);
+}
+
+// W > 1 waves per token (the workgroup has at least T W waves): each takes the top-k of its
+// 64 P experts, then the token's first wave merges the W lists.
+template <int T, int W>
+__device__ void route_split(const float (&lgv)[8 / W], int E, int k, SlotTable* st, int* ids, float* wts) {
+    constexpr int P = 8 / W;
+    __shared__ uint32_t cc[T][W * kMaxTopK];  // candidates: order codes (0 = none) and experts
+    __shared__ int ci[T][W * kMaxTopK];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, t = wv / W, w = wv % W;
+    if (t < T) {
+        uint32_t my_code;
+        int my_id;
+        wave_topk<P>(lgv, w * 64 * P, E, k, my_code, my_id);
+        if (lane < kMaxTopK) {
+            cc[t][w * kMaxTopK + lane] = lane < k ? my_code : 0u;
+            ci[t][w * kMaxTopK + lane] = my_id;
+        }
+    }
+    __syncthreads();
+    if (t < T && w == 0) {
+        uint32_t code = lane < W * kMaxTopK ? cc[t][lane] : 0u;
+        const int cid = lane < W * kMaxTopK ? ci[t][lane] : 0;
+        int my_id = 0;
+        uint32_t my_code = 0;
+        for (int r = 0; r < k; ++r) {
+            const uint32_t m = wave_max_u32(code);
+            const int win = (int)__builtin_ctzll(__ballot(code == m));  // lowest (wave, rank) with it
+            const int id = __builtin_amdgcn_readlane(cid, win);
+            my_id = lane == r ? id : my_id;
+            my_code = lane == r ? m : my_code;
+            if (lane == win) code = 0u;
+        }
+        topk_softmax(my_code, my_id, k, ids + t * k, wts + t * k);
+    }
+    build_slots<T>(k, st, ids, wts);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -804,7 +893,7 @@ struct K2Args {
 // token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
 // tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
 // the weights.
-template <int T, int BPL>
+template <int T, int BPL, int W>
 __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     extern __shared__ uint4 smem2[];
     half2_t* xh = (half2_t*)smem2;  // [T][H/2] f16 values of the input's FP8 codes
@@ -825,8 +914,9 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     const float sxv = a.xs[tid < T ? tid : 0];
     // 1-2 tokens: every routed workgroup takes the top-k itself; 3-4 tokens: the router kernel did
     constexpr bool ROUTE = T <= 2;
-    float lgv[8];
-    if constexpr (ROUTE) route_issue(a.logits, a.E, T, lgv);  // shared workgroups load them too: exact waits below
+    // W waves per token take the top-k together (W = 1: one wave per token)
+    float lgv[8 / W];
+    if constexpr (ROUTE) route_issue<T, W>(a.logits, a.E, lgv);  // shared workgroups load them too: exact waits below
 
     // f16 values of the codes into LDS while the logits are in flight
     if (tid < T) sx[tid] = sxv;
@@ -856,7 +946,10 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
         const int b = blockIdx.x - a.n_sh_wg, slot = b / tiles;
         tile = b - slot * tiles;
         if constexpr (ROUTE) {
-            route_finish<T>(lgv, a.logits, a.E, k, &st, ids, wts);
+            if constexpr (W > 1)
+                route_split<T, W>(lgv, a.E, k, &st, ids, wts);
+            else
+                route_finish<T>(lgv, a.logits, a.E, k, &st, ids, wts);
             if (b == 0) {  // the first routed workgroup publishes the routing of the layer
                 for (int i = tid; i < (int)(sizeof(SlotTable) / 4); i += blockDim.x)
                     ((int*)a.slots)[i] = ((const int*)&st)[i];
@@ -1180,7 +1273,12 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     K2Args a2{P.logits, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h, P.hamax, P.slots,
               CENTRAL ? nullptr : P.ids, CENTRAL ? nullptr : P.w, sh.H, sh.E, sh.k, sh.S, sh.I, n_sh_wg, T};
     const size_t lds2 = (size_t)T * sh.H * 2;
-    launch(k2_gateup<T, BPL>, n_sh_wg + n_gu_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
+    // top-k waves per token in the gate/up workgroups (1-2 tokens; workgroups of 4+ waves)
+    constexpr int WT = T == 1 ? 4 : T == 2 ? 2 : 1;
+    if (GW >= T * WT)
+        launch(k2_gateup<T, BPL, WT>, n_sh_wg + n_gu_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
+    else
+        launch(k2_gateup<T, BPL, 1>, n_sh_wg + n_gu_wg, 64 * GW, lds2, stream, ev ? ev + 2 : nullptr, a2);
 
     if (CENTRAL) {
         KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
