@@ -84,6 +84,23 @@ __device__ __forceinline__ void block_dot(const uint4& w, const half2_t* const (
     }
 }
 
+// The same for nt tokens of at most NT: a work item with one token (every shared-expert item, and
+// every routed expert when the tokens' top-k sets are disjoint) takes the one-token form, without
+// the per-token guards that the NT form carries through each dword.
+template <int NT>
+__device__ __forceinline__ void block_dot_nt(const uint4& w, const half2_t* const (&xp)[NT], float (&p)[NT], int nt) {
+    if constexpr (NT > 1) {
+        if (nt == 1) {
+            const half2_t* const x1[1] = {xp[0]};
+            float p1[1] = {p[0]};
+            block_dot<1>(w, x1, p1, 1);
+            p[0] = p1[0];
+            return;
+        }
+    }
+    block_dot<NT>(w, xp, p, nt);
+}
+
 // Lane exchange without LDS: stage S pairs every lane with one partner (0: lane^1, 1: lane^2,
 // 2: mirror within 8 lanes, 3: mirror within 16 lanes, 4: lane^16, 5: lane^32).  Applying an
 // associative, commutative op with stages 0..n-1 reduces over groups of 2^n lanes.

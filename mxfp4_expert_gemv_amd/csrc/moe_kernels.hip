@@ -374,7 +374,7 @@ __device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, con
         float p[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) p[j] = 0.0f;
-        block_dot<T>(L.w[i], xp, p, nt);
+        block_dot_nt<T>(L.w[i], xp, p, nt);
 #pragma unroll
         for (int j = 0; j < T; ++j) acc[j] = fmaf(p[j], scale, acc[j]);
         __builtin_amdgcn_sched_barrier(0);  // bound the live activation registers to one block
@@ -450,11 +450,16 @@ __device__ __forceinline__ void load_logits(const float* row, int base, int E, f
     }
 }
 
-// The same from logits that other workgroups of the running kernel stored with device-scope stores.
+// The same from logits that other workgroups of the running kernel stored with device-scope stores
+// (64-bit device-scope loads: the logits are 8-byte aligned).
 __device__ __forceinline__ void load_logits8_agent(const float* row, int E, float (&v)[8]) {
-    const float* p = row + min((int)(threadIdx.x & 63) * 8, E - 8);
+    const uint64_t* p = (const uint64_t*)(row + min((int)(threadIdx.x & 63) * 8, E - 8));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t u = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[2 * j] = __uint_as_float((uint32_t)u);
+        v[2 * j + 1] = __uint_as_float((uint32_t)(u >> 32));
+    }
 }
 
 // W waves per token: wave v takes token v / W, experts (v % W) 64 P ...  Every wave loads (waves
@@ -561,8 +566,8 @@ __device__ void build_slots(int k, SlotTable* st, const int* ids, const float* w
         const bool valid = p < np;
         const int e = valid ? ids[p] : -1;
         int first = p, j = 0, c = 0;  // first pair with this expert, position among them, count
-        for (int q = 0; q < np; ++q) {
-            const bool same = ids[q] == e;
+        for (int q = 0; q < np; ++q) {  // pair q's expert, broadcast from lane q
+            const bool same = __builtin_amdgcn_readlane(e, q) == e;
             if (same && q < first) first = q;
             if (same && q < p) ++j;
             if (same) ++c;
@@ -1171,7 +1176,7 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
             float q[T];
 #pragma unroll
             for (int j = 0; j < T; ++j) q[j] = 0.0f;
-            block_dot<T>(wr[m][it], xp, q, nt);
+            block_dot_nt<T>(wr[m][it], xp, q, nt);
 #pragma unroll
             for (int j = 0; j < T; ++j) pj[j] = fmaf(q[j], scale, pj[j]);
             __builtin_amdgcn_sched_barrier(0);
@@ -1284,17 +1289,22 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
         KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
         kq_requant<<<sh.pairs(T), 256, 0, stream>>>(aq);
     }
-    // down: one workgroup per CU-sized share of the rows; (slot, row) units spread over up to 12
-    // waves, UPW groups of 64 / KSUB units per wave
-    constexpr int UPW = T;
-    const int rows = sh.H / kDownGrid;
+    // down: one workgroup per CU-sized share of the rows (3-4 tokens: two per CU, so that each SIMD
+    // holds twice the waves to hide the LDS latency of the dot phase); (slot, row) units spread
+    // over up to 12 waves, UPW groups of 64 / KSUB units per wave
+    const bool two_per_cu = CENTRAL && sh.H % (2 * kDownGrid) == 0;
+    const int dgrid = two_per_cu ? 2 * kDownGrid : kDownGrid, upw = two_per_cu ? 2 : T;
+    const int rows = sh.H / dgrid;
     const int units_max = (routed_slots_max(sh, T) + sh.S * T) * rows, groups = (units_max + R - 1) / R;
     const int nw = std::max(std::min(groups, 12), 2);  // >= 2: slot list copy
-    if (nw * UPW < groups) return hipErrorInvalidValue;
+    if (nw * upw < groups) return hipErrorInvalidValue;
     K3Args a3{P.slots, (const uint4*)L.w2, (const uint8_t*)L.w2s, P.h, P.hamax, P.hq, P.hs, P.xnext ? P.x : nullptr,
               P.xnext, P.y, sh.H, sh.E, sh.k, sh.S, sh.I, rows, units_max};
     const size_t lds3 = (size_t)sh.pairs(T) * sh.I * 2 + (size_t)units_max * T * 4;
-    launch(k3_down<KSUB, ITERS, T, UPW>, kDownGrid, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
+    if (two_per_cu)
+        launch(k3_down<KSUB, ITERS, T, 2>, dgrid, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
+    else
+        launch(k3_down<KSUB, ITERS, T, T>, dgrid, 64 * nw, lds3, stream, ev ? ev + 4 : nullptr, a3);
     return hipGetLastError();
 }
 
