@@ -156,13 +156,23 @@ def main():
     single = {}
     if not args.no_single:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for name, key, T in (("layer_t1", "layer_t1", 1), ("layer_t4", "layer_t4", 4)):
+        # layer_t4_overlap: a verify step whose 4 tokens share routed experts (correlated tokens,
+        # rho 0.9); its bytes are counted from the distinct experts the run returns
+        for name, key, T in (("layer_t1", "layer_t1", 1), ("layer_t4", "layer_t4", 4),
+                             ("layer_t4_overlap", "layer_t4", 4)):
             m = man[key]
             h1 = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, 1, vflags)
             layer_tensors(m["seed"], 0, 0, bufs)
             moe.moe_decode_set_layer(h1, 0, bufs["router"], bufs["w13"], bufs["w13_s"], bufs["w2"], bufs["w2_s"])
-            xs = torch.from_numpy(synth.tokens(H, m["seed"], T, m["x_attempt"]).view(np.int16)).to(dev)
-            xs = xs.view(torch.bfloat16)
+            if name == "layer_t4_overlap":
+                xh = synth.tokens_correlated(H, m["seed"], T, 0.9, 0)
+            else:
+                xh = synth.tokens(H, m["seed"], T, m["x_attempt"])
+            xs = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
+            ids1 = torch.empty((1, T, shape.top_k), dtype=torch.int32, device=dev)
+            moe.moe_decode_run(h1, xs, T, topk_ids=ids1)
+            torch.cuda.synchronize()
+            distinct = len(set(ids1.cpu().numpy().reshape(-1).tolist()))
             y = torch.empty((T, H), dtype=torch.float32, device=dev)
             times = []
             for i in range(args.warmup + args.steps):
@@ -174,13 +184,14 @@ def main():
                 e1.synchronize()
                 if i >= args.warmup:
                     times.append(e0.elapsed_time(e1) * 1e3)
-            distinct = len(set(sum(m["ids"], [])))
             nbytes = router_bytes + (distinct + shape.num_shared) * expert_bytes
             med = float(np.median(times))
-            single[name] = {"tokens": T, "us_median": med, "us_p10": float(np.percentile(times, 10)),
+            single[name] = {"tokens": T, "distinct_routed_experts": distinct, "us_median": med,
+                            "us_p10": float(np.percentile(times, 10)),
                             "us_p90": float(np.percentile(times, 90)), "bytes": nbytes,
                             "gb_s": nbytes / (med * 1e-6) / 1e9}
-            log(f"single layer T={T} (cache flushed): median {med:.1f} us, {single[name]['gb_s']:.0f} GB/s")
+            log(f"single layer {name} ({distinct} routed experts, cache flushed): median {med:.1f} us, "
+                f"{single[name]['gb_s']:.0f} GB/s")
             moe.moe_decode_destroy(h1)
         del flush
 

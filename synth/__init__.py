@@ -145,6 +145,20 @@ def tokens(hidden: int, seed: int, T: int, attempt: int = 0, layer: int = 0) -> 
     return out
 
 
+def tokens_correlated(hidden: int, seed: int, T: int, rho: float, attempt: int = 0, layer: int = 0) -> np.ndarray:
+    """bf16 bits [T][H] of T tokens with a common component: token 0 is z_0 and token t >= 1 is
+    rho z_0 + sqrt(1 - rho^2) z_t, with z_t ~ N(0, 1) in fp32 drawn as in tokens() and the mix
+    rounded once to bf16 (nearest, ties to even).  Their router scores are correlated, so their
+    top-k sets overlap, as for the positions of one speculative verify step."""
+    z = [normal_f32(hidden, key(seed, layer, TENSOR_X, t, attempt), X_SIGMA).astype(np.float64) for t in range(T)]
+    mix = np.empty((T, hidden), dtype=np.float32)
+    mix[0] = z[0]
+    for t in range(1, T):
+        mix[t] = rho * z[0] + np.sqrt(1.0 - rho * rho) * z[t]
+    u = mix.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def expert(shape: Shape, seed: int, layer: int, e: int) -> dict:
     """Canonical MXFP4 tensors of expert e (index num_experts is the shared expert).
 

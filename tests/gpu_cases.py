@@ -126,14 +126,20 @@ def check_layer(shape, gpu: dict, ref_y: np.ndarray, ref_tr: dict, layer: int = 
     return err
 
 
-def margin_attempt(shape, router_host, seed, T, start=0, need_disjoint=False):
-    """First x attempt >= start whose routing is well posed under fp32 evaluation."""
+def margin_attempt(shape, router_host, seed, T, start=0, need_disjoint=False, rho=None):
+    """First x attempt >= start whose routing is well posed under fp32 evaluation.  With rho, the
+    tokens are correlated (synth.tokens_correlated) and the attempt must share at least one routed
+    expert between tokens."""
     for a in range(start, start + 10000):
-        x = synth.tokens(shape.hidden, seed, T, a)
+        x = synth.tokens(shape.hidden, seed, T, a) if rho is None else synth.tokens_correlated(shape.hidden, seed, T,
+                                                                                                rho, a)
         ro = oracle.route(shape, router_host, x)
         ok = all(oracle.topk_margin_ok(ro["logits"][t], ro["bounds"][t], shape.top_k) for t in range(T))
+        distinct = len(set(ro["ids"].reshape(-1).tolist()))
         if ok and need_disjoint:
-            ok = len(set(ro["ids"].reshape(-1).tolist())) == ro["ids"].size
+            ok = distinct == ro["ids"].size
+        if ok and rho is not None:
+            ok = distinct < ro["ids"].size
         if ok:
             return a, x
     raise RuntimeError("no attempt with a routing margin")

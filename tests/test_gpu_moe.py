@@ -131,6 +131,20 @@ def test_flash_layer_t4_disjoint():
     moe.moe_decode_destroy(h)
 
 
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_flash_layer_overlapping_routing(flash_t1, T):
+    """Verify step whose tokens share routed experts (correlated tokens): every distinct expert is
+    read once for all of its tokens, and each token's combine still matches the oracle."""
+    shape, lay, h, m = flash_t1
+    a, x = margin_attempt(shape, lay.router_host, 11, T, rho=0.9)
+    gpu = run_layer(h, shape, x)
+    ro = oracle.route(shape, lay.router_host, x)
+    ref_y, ref_tr = oracle.moe_layer(shape, lay.router_host, lay.oracle_experts(ro["ids"]), x)
+    distinct = len(set(ro["ids"].reshape(-1).tolist()))
+    err = check_layer(shape, gpu, ref_y, ref_tr)
+    print(f"flash T={T} overlapping routing: attempt {a}, {distinct} distinct routed experts, normwise y error {err}")
+
+
 def test_flash_token_independence(flash_t1):
     shape, lay, h, m = flash_t1
     a, x = margin_attempt(shape, lay.router_host, m["seed"], 4, start=500)

@@ -55,3 +55,18 @@ def test_expert_shapes():
     assert t["w2"].shape == (2560, 384) and t["w2_s"].shape == (2560, 24)
     per_expert = sum(v.nbytes for v in t.values())
     assert per_expert == 3_133_440
+
+
+def test_tokens_correlated_mix_and_rounding():
+    """Correlated verify tokens: token 0 is bit-equal to tokens()'s token 0 (the same normal draw and
+    the same round-to-nearest-even bf16 rounding, done here in numpy and in C there); token t >= 1 has
+    correlation rho with token 0 and rho^2 with the other mixed tokens."""
+    H, rho = 2560, 0.9
+    x = synth.tokens_correlated(H, 5, 3, rho, 0)
+    assert x.shape == (3, H) and x.dtype == np.uint16
+    assert (x[0] == synth.tokens(H, 5, 1, 0)[0]).all()
+    f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = np.corrcoef(f)
+    assert abs(c[0, 1] - rho) < 0.02 and abs(c[0, 2] - rho) < 0.02
+    assert abs(c[1, 2] - rho * rho) < 0.03
+    assert (synth.tokens_correlated(H, 5, 3, rho, 0) == x).all()
