@@ -379,6 +379,23 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
         out[f"t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
         log(f"LM head T={T}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     moe.fp8_head_destroy(hd)
+    # the load-time quantisation of the head (fp32 rows in, E4M3 codes and row scales out)
+    wf = torch.randn((V, H), device=dev) * 0.02
+    codes = torch.empty((V, H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((V,), dtype=torch.float32, device=dev)
+    moe.fp8_head_quantize(wf, codes, sc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        moe.fp8_head_quantize(wf, codes, sc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 10
+    qbytes = V * H * 4 + V * H + V * 4
+    out["quantize_fp32"] = {"us": round(us, 1), "bytes": qbytes, "gb_s": round(qbytes / (us * 1e-6) / 1e9, 1)}
+    log(f"LM head quantisation (fp32 in): {us:.1f} us, {qbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    del wf, codes, sc
     return out
 
 

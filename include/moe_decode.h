@@ -178,6 +178,19 @@ moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, f
                         void* stream);
 moe_status fp8_head_destroy(fp8_head_handle* h);
 
+/* Per-row FP8 quantisation of an LM-head weight matrix at load time, the step that makes the FP8
+ * head (tanhow.com, section "三项优化是什么", item 2: the head is kept in FP8 instead of BF16 so that
+ * each decode step reads half the bytes; devotd.net, "dgx-spark-moe-inference-optimizations",
+ * section 2).  For every row r of W (BF16 or FP32 [rows][cols], row-major, tag checked):
+ *   scales[r]   = fl32(max_c |W[r][c]| / 448), or 1 for an all-zero row;
+ *   codes[r][c] = OCP E4M3 round-to-nearest-even of fl32(W[r][c] / scales[r]).
+ * The outputs (E4M3 [rows][cols] and FP32 [rows], caller-owned device buffers, 8- and 4-byte
+ * aligned) are the inputs fp8_head_create takes.  cols: a multiple of 256 up to 2560.  Only
+ * enqueues work on `stream`; W may be freed after the stream has synchronised.  Errors:
+ * MOE_ERR_INVALID_ARG (sizes, NULL or misaligned pointers), MOE_ERR_UNSUPPORTED (cols),
+ * MOE_ERR_DTYPE (tag), MOE_ERR_NO_DEVICE, MOE_ERR_HIP (launch). */
+moe_status fp8_head_quantize(int32_t rows, int32_t cols, moe_tensor w, void* codes, float* scales, void* stream);
+
 /* Kernel timing instrumentation.  moe_decode_timing_enable(h, max_runs) makes the next up to
  * max_runs calls of moe_decode_run launch their kernels one by one on the caller's stream (no
  * graph), each with a start and a stop HIP event that the runtime stamps with that kernel's own

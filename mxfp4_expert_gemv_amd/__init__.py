@@ -24,7 +24,7 @@ F_PERSISTENT = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
-           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy",
+           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize",
            "moe_status_string", "moe_last_error")
 
 
@@ -93,6 +93,7 @@ def lib():
             "fp8_head_create": [i32, i32, Tensor, Tensor, vp, ctypes.POINTER(vp)],
             "fp8_head_run": [vp, vp, i32, vp, vp, vp],
             "fp8_head_destroy": [vp],
+            "fp8_head_quantize": [i32, i32, Tensor, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -201,3 +202,12 @@ def fp8_head_run(handle, x, argmax, logits=None, num_tokens: int | None = None, 
 
 def fp8_head_destroy(handle) -> None:
     _check(lib().fp8_head_destroy(handle))
+
+
+def fp8_head_quantize(w, codes, scales, stream=None) -> None:
+    """Per-row E4M3 quantisation of w (torch bf16 or float32 [rows][cols], device) into codes
+    (uint8 [rows][cols]) and scales (float32 [rows]); enqueues only."""
+    import torch
+    rows, cols = w.shape
+    dt = DT_BF16 if w.dtype == torch.bfloat16 else DT_FP32 if w.dtype == torch.float32 else -1
+    _check(lib().fp8_head_quantize(rows, cols, _tensor(w, dt), _ptr(codes), _ptr(scales), _stream(stream)))

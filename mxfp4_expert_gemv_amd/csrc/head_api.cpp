@@ -8,6 +8,8 @@
 
 namespace head {
 hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream);
+hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* codes, float* scales,
+                                hipStream_t stream);
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
                        float* pval, int32_t* pidx, unsigned* ticket, int V, int H, hipStream_t stream);
 }
@@ -80,6 +82,28 @@ extern "C" moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t T,
     hipError_t e = head::launch_head(h->w, h->scale, (const uint16_t*)x, T, logits, argmax, h->pval, h->pidx, h->ticket,
                                      h->V, h->H, (hipStream_t)stream);
     if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_quantize(int32_t rows, int32_t cols, moe_tensor w, void* codes, float* scales,
+                                        void* stream) {
+    if (rows <= 0 || cols <= 0) return moe_fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
+    if (cols % 256 || cols > 2560)
+        return moe_fail(MOE_ERR_UNSUPPORTED, "cols %d (multiple of 256 up to 2560 supported)", cols);
+    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
+    if (w.dtype != MOE_DT_BF16 && w.dtype != MOE_DT_FP32)
+        return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected BF16 (%d) or FP32 (%d)", w.dtype, MOE_DT_BF16,
+                        MOE_DT_FP32);
+    if (!codes || (uintptr_t)codes % 8) return moe_fail(MOE_ERR_INVALID_ARG, "codes is NULL or not 8-byte aligned");
+    if (!scales || (uintptr_t)scales % 4) return moe_fail(MOE_ERR_INVALID_ARG, "scales is NULL or not 4-byte aligned");
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    hipError_t e = head::launch_quantize_rows(w.ptr, w.dtype == MOE_DT_BF16, rows, cols, codes, scales,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head quantisation launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 

@@ -154,6 +154,66 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     if (tid == 0) *a.ticket = 0u;
 }
 
+// Per-row FP8 quantisation of the head at load time (the step the pages put before the FP8 head):
+// s_r = fl32(max_c |W[r][c]| / 448), 1 for an all-zero row, and code[r][c] = E4M3 round-to-nearest-
+// even of fl32(W[r][c] / s_r) (both divisions correctly rounded; |W / s| <= 448 up to the rounding
+// of s, inside the E4M3 range).  One wave per row: lane l holds the 8-element chunks l, l + 64, ...
+// of the row (H / 8 <= 320 chunks, so at most 5 per lane), one wave-wide maximum, then the codes.
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_rows(const void* __restrict__ w, int V, int H,
+                                                     uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    constexpr int kChunks = 5;
+    const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + (threadIdx.x >> 6), NC = H / 8;
+    if (row >= V) return;  // the whole wave
+    float v[kChunks][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const int c = lane + 64 * j;
+        if (c < NC) {
+            if constexpr (BF16) {
+                const uint4 u = ((const uint4*)w)[(size_t)row * NC + c];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[j][2 * q] = __uint_as_float(comp(u, q) << 16);
+                    v[j][2 * q + 1] = __uint_as_float(comp(u, q) & 0xffff0000u);
+                }
+            } else {
+                const float4 a = ((const float4*)w)[((size_t)row * NC + c) * 2];
+                const float4 b = ((const float4*)w)[((size_t)row * NC + c) * 2 + 1];
+                v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+                v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float s = m > 0.0f ? m / 448.0f : 1.0f;
+    if (lane == 0) scales[row] = s;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const int c = lane + 64 * j;
+        if (c < NC) {
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                d[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[j][2 * q] / s, v[j][2 * q + 1] / s, 0, false) & 0xffffu;
+            ((uint2*)codes)[(size_t)row * NC + c] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+        }
+    }
+}
+
+hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* codes, float* scales,
+                                hipStream_t stream) {
+    const unsigned grid = (unsigned)((V + 3) / 4);
+    if (bf16)
+        quantize_rows<true><<<grid, 256, 0, stream>>>(w, V, H, (uint8_t*)codes, scales);
+    else
+        quantize_rows<false><<<grid, 256, 0, stream>>>(w, V, H, (uint8_t*)codes, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream) {
     const int VT = (V + kWave - 1) / kWave;
     uint64_t total = (uint64_t)VT * (H / kUnit) * kWave;

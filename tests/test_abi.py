@@ -85,3 +85,16 @@ def test_head_dtype_tags_checked_before_device():
                              ctypes.byref(h)) == -3
     assert L.fp8_head_create(100, 2000, moe.Tensor(addr, moe.DT_E4M3), moe.Tensor(addr, moe.DT_FP32), None,
                              ctypes.byref(h)) == -2
+
+
+def test_head_quantize_arguments_checked_before_device():
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(64)
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    ok = moe.Tensor(addr, moe.DT_FP32)
+    assert L.fp8_head_quantize(0, 2560, ok, addr, addr, None) == -1
+    assert L.fp8_head_quantize(8, 2000, ok, addr, addr, None) == -2
+    # E4M3-tagged input: only BF16 or FP32 weights are quantised
+    assert L.fp8_head_quantize(8, 2560, moe.Tensor(addr, moe.DT_E4M3), addr, addr, None) == -3
+    assert L.fp8_head_quantize(8, 2560, ok, None, addr, None) == -1
+    assert L.fp8_head_quantize(8, 2560, ok, addr, None, None) == -1

@@ -78,3 +78,74 @@ def test_full_head_argmax(T):
     rows = np.unique(np.concatenate([np.arange(0, V, 997), np.array(m["argmax"][:T]), [V - 1]]))
     lg_o, bd_o, _ = oracle.head_logits(Wq[rows], s[rows], x)
     assert (np.abs(lg[:, rows] - lg_o) <= bd_o).all()
+
+
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _gpu_quantize(w: torch.Tensor):
+    V, H = w.shape
+    codes = torch.empty((V, H), dtype=torch.uint8, device=dev())
+    scales = torch.empty((V,), dtype=torch.float32, device=dev())
+    moe.fp8_head_quantize(w, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def _crafted_rows(H):
+    """Rows that exercise the rounding rules: an all-zero row (scale 1); a row whose maximum is 448
+    (scale exactly 1) holding values halfway between E4M3 neighbours (ties go to the even code),
+    subnormal-range values and their ties; a single nonzero element; a row of equal magnitudes."""
+    rows = np.zeros((4, H), dtype=np.float32)
+    ties = [448.0, 1.0625, 1.1875, -1.0625, -1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 2.0 ** -11,
+            0.3, -0.3, 13.0, 17.0, 240.0, 432.0, 440.0]
+    rows[1, :len(ties)] = ties
+    rows[2, H // 3] = -0.037
+    rows[3, :] = 0.5
+    rows[3, 1::2] = -0.5
+    return rows
+
+
+@pytest.mark.parametrize("V,H", [(4099, 2560), (37, 256), (130, 1024)])
+def test_quantize_rows_bit_exact_fp32_and_bf16(V, H):
+    W = np.concatenate([_crafted_rows(H), synth.head_weights(V, H, 21)[: V - 4]])
+    codes, scales = _gpu_quantize(torch.from_numpy(W).to(dev()))
+    Wq_o, s_o = oracle.head_quantize(W)
+    assert (scales.view(np.uint32) == s_o.view(np.uint32)).all()
+    bad = np.argwhere(codes != Wq_o)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:5].tolist()}"
+    # the same rows in bf16: the device reads bf16, the oracle its exact fp32 value
+    Wb = _bf16_bits(W)
+    codes, scales = _gpu_quantize(torch.from_numpy(Wb.view(np.int16)).to(dev()).view(torch.bfloat16))
+    Wq_o, s_o = oracle.head_quantize((Wb.astype(np.uint32) << 16).view(np.float32))
+    assert (scales.view(np.uint32) == s_o.view(np.uint32)).all()
+    assert (codes == Wq_o).all()
+
+
+def test_full_head_quantised_on_device():
+    """The full 157,184 x 2,560 head quantised on the device at load (fp32 in), bit-equal to the
+    oracle's quantisation, then used by the FP8 head: the argmax is the oracle's."""
+    m = MANIFEST["head"]
+    V, H = m["vocab"], m["hidden"]
+    codes = torch.empty((V, H), dtype=torch.uint8, device=dev())
+    scales = torch.empty((V,), dtype=torch.float32, device=dev())
+    step = 16384
+    for r0 in range(0, V, step):
+        n = min(step, V - r0)
+        w = torch.from_numpy(synth.head_weights(V, H, m["seed"], r0, n)).to(dev())
+        moe.fp8_head_quantize(w, codes[r0:r0 + n], scales[r0:r0 + n])
+        torch.cuda.synchronize()
+        del w
+    Wq_o, s_o = _quantised(V, H, m["seed"])
+    assert (scales.cpu().numpy().view(np.uint32) == s_o.view(np.uint32)).all()
+    assert bool((codes == torch.from_numpy(Wq_o).to(dev())).all())
+    h = moe.fp8_head_create(codes, scales)
+    x = synth.tokens(H, m["seed"], 4, m["x_attempt"])
+    am = torch.full((4,), -1, dtype=torch.int32, device=dev())
+    moe.fp8_head_run(h, to_dev_u16(x), am)
+    torch.cuda.synchronize()
+    moe.fp8_head_destroy(h)
+    assert am.cpu().numpy().tolist() == m["argmax"]
