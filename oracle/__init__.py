@@ -31,6 +31,7 @@ PINS = {
     "rmsnorm_bf16": "constant-vector closed form; power-of-two scale invariance",
     "residual_bf16": "bf16 round trip vs torch",
     "head": "argmax brute force; duplicate-row tie; BLAS GEMV special case",
+    "head_bf16": "BLAS GEMV special case; equals the FP8 head exactly on rows that are E4M3 values times a power of two",
 }
 
 
@@ -91,6 +92,9 @@ def _load(path):
     L.oracle_head_quantize.restype = None
     L.oracle_head_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p]
+    L.oracle_head_logits_bf16.restype = None
+    L.oracle_head_logits_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.oracle_head_logits.restype = None
     L.oracle_head_logits.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -267,6 +271,19 @@ def head_logits(Wq, scale, x, want_logits: bool = True, want_bounds: bool = True
     bd = np.empty((T, V)) if want_bounds else None
     am = np.empty(T, dtype=np.int32)
     lib().oracle_head_logits(_p(Wq), _p(scale), V, H, _p(x), T, _p(lg), _p(bd), _p(am))
+    return lg, bd, am
+
+
+def head_logits_bf16(W, x, want_logits: bool = True, want_bounds: bool = True):
+    """The unquantised BF16 head (W bf16 bits [V][H]): fp64 logits, fp32 error bounds, argmax."""
+    W = _c(W, np.uint16)
+    x = _c(x, np.uint16)
+    V, H = W.shape
+    T = x.shape[0]
+    lg = np.empty((T, V)) if want_logits else None
+    bd = np.empty((T, V)) if want_bounds else None
+    am = np.empty(T, dtype=np.int32)
+    lib().oracle_head_logits_bf16(_p(W), V, H, _p(x), T, _p(lg), _p(bd), _p(am))
     return lg, bd, am
 
 

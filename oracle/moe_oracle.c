@@ -427,3 +427,33 @@ void oracle_head_logits(const uint8_t* Wq, const float* scale, int32_t V, int32_
     }
     free(xf);
 }
+
+/* The BF16 head that the FP8 head replaces: logits[t][r] = sum_c W[r][c] * x[t][c] in fp64 (W and x
+ * bf16, so every product is exact); argmax = lowest index among the maxima.  bounds (optional) =
+ * gamma_(H-1) * sum |W x|: the largest error of an fp32 dot product in any order. */
+void oracle_head_logits_bf16(const uint16_t* W, int32_t V, int32_t H, const uint16_t* x, int32_t T, double* logits,
+                             double* bounds, int32_t* argmax) {
+    const double nu = (double)(H - 1) * 0x1p-24;
+    const double gamma = nu / (1.0 - nu);
+    double* xf = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < H; ++c) xf[c] = (double)oracle_bf16_decode(x[(size_t)t * H + c]);
+        int best = 0;
+        double bestv = -INFINITY;
+        for (int r = 0; r < V; ++r) {
+            const uint16_t* row = W + (size_t)r * H;
+            double acc = 0.0, mag = 0.0;
+            for (int c = 0; c < H; ++c) {
+                double p = (double)oracle_bf16_decode(row[c]) * xf[c];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (logits) logits[(size_t)t * V + r] = acc;
+            if (bounds) bounds[(size_t)t * V + r] = gamma * mag;
+            if (acc > bestv) { bestv = acc; best = r; }
+        }
+        if (argmax) argmax[t] = best;
+    }
+    free(xf);
+}
+

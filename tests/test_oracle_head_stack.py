@@ -68,6 +68,38 @@ def test_head_duplicate_row_keeps_lowest_index():
     assert am3[0] == 0 or r == 0
 
 
+def _bf16_bits(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_bf16_head_matches_blas_and_argmax_brute_force():
+    V, H = 2000, 2560
+    Wb = _bf16_bits(synth.head_weights(V, H, seed=6, rows=V))
+    x = synth.tokens(H, 6, 3)
+    lg, bd, am = oracle.head_logits_bf16(Wb, x)
+    dense = oracle.bf16_decode(Wb).astype(np.float64) @ oracle.bf16_decode(x).astype(np.float64).T
+    np.testing.assert_allclose(lg, dense.T, rtol=1e-12, atol=1e-12)
+    for t in range(3):
+        assert am[t] == np.flatnonzero(lg[t] == lg[t].max())[0]
+        assert (bd[t] > 0).all()
+
+
+def test_bf16_head_equals_fp8_head_on_power_of_two_scales():
+    """Rows that are E4M3 values times a power of two are exact in bf16, and both heads then sum the
+    same exact products: the BF16 oracle must return the FP8 oracle's logits bit for bit."""
+    V, H = 700, 2560
+    Wq, s = oracle.head_quantize(synth.head_weights(V, H, seed=8, rows=V))
+    s2 = np.exp2(np.round(np.log2(s))).astype(np.float32)  # a power of two near each row scale
+    vals = torch.from_numpy(Wq).view(torch.float8_e4m3fn).to(torch.float32).numpy() * s2[:, None]
+    Wb = _bf16_bits(vals)
+    assert ((Wb.astype(np.uint32) << 16).view(np.float32) == vals).all()  # exact in bf16
+    x = synth.tokens(H, 8, 2)
+    lg8, _, am8 = oracle.head_logits(Wq, s2, x)
+    lgb, _, amb = oracle.head_logits_bf16(Wb, x)
+    assert (lg8 == lgb).all() and (am8 == amb).all()
+
+
 def test_fp8_head_halves_bf16_reads():
     V, H = synth.HEAD_VOCAB, 2560
     assert V * H == 402_391_040 and 2 * V * H == 804_782_080
