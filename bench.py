@@ -379,6 +379,28 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
         out[f"t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
         log(f"LM head T={T}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     moe.fp8_head_destroy(hd)
+    # the unquantised BF16 head it replaces (twice the bytes), for the comparison
+    wb = (torch.randn((V, H), device=dev) * 0.02).to(torch.bfloat16)
+    hb = moe.bf16_head_create(wb)
+    torch.cuda.synchronize()
+    del wb
+    bbytes = V * H * 2
+    for T in (1, 4):
+        for _ in range(warmup):
+            moe.fp8_head_run(hb, x[:T], am[:T])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            moe.fp8_head_run(hb, x[:T], am[:T])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = bbytes / (us * 1e-6) / 1e9
+        out[f"bf16_t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                             "fp8_speedup": round(us / out[f"t{T}"]["us"], 3)}
+        log(f"BF16 LM head T={T}: {us:.1f} us, {gbs:.0f} GB/s; FP8 head is {us / out[f't{T}']['us']:.2f}x faster")
+    moe.fp8_head_destroy(hb)
     # the load-time quantisation of the head (fp32 rows in, E4M3 codes and row scales out)
     wf = torch.randn((V, H), device=dev) * 0.02
     codes = torch.empty((V, H), dtype=torch.uint8, device=dev)

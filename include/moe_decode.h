@@ -173,6 +173,11 @@ moe_status moe_decode_destroy(moe_decode_handle* h);
  * lowest index among the maxima.  create copies W and s into handle-owned memory. */
 moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, void* stream,
                            fp8_head_handle** out);
+/* The unquantised head that the FP8 head replaces, for measuring what FP8 saves: W BF16 [V][H]
+ * (row-major; no scales), otherwise as fp8_head_create.  The handle is run and freed with
+ * fp8_head_run / fp8_head_destroy, which then compute logits[t][v] = sum_c W[v][c] x[t][c] (bf16
+ * products, exact in fp32; fp32 accumulation) and the lowest-index argmax. */
+moe_status bf16_head_create(int32_t vocab, int32_t hidden, moe_tensor w, void* stream, fp8_head_handle** out);
 /* logits (FP32 [T][V], device) may be NULL; argmax (INT32 [T], device) is required. */
 moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, float* logits, int32_t* argmax,
                         void* stream);

@@ -24,7 +24,7 @@ F_PERSISTENT = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
-           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize",
+           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize", "bf16_head_create",
            "moe_status_string", "moe_last_error")
 
 
@@ -94,6 +94,7 @@ def lib():
             "fp8_head_run": [vp, vp, i32, vp, vp, vp],
             "fp8_head_destroy": [vp],
             "fp8_head_quantize": [i32, i32, Tensor, vp, vp, vp],
+            "bf16_head_create": [i32, i32, Tensor, vp, ctypes.POINTER(vp)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -192,6 +193,15 @@ def fp8_head_create(w, row_scale, stream=None) -> ctypes.c_void_p:
     h = ctypes.c_void_p()
     _check(lib().fp8_head_create(vocab, hidden, _tensor(w, DT_E4M3), _tensor(row_scale, DT_FP32), _stream(stream),
                                  ctypes.byref(h)))
+    return h
+
+
+def bf16_head_create(w, stream=None) -> ctypes.c_void_p:
+    """The BF16 head (w torch bfloat16 [V][H], device); run and free it with fp8_head_run and
+    fp8_head_destroy."""
+    vocab, hidden = w.shape
+    h = ctypes.c_void_p()
+    _check(lib().bf16_head_create(vocab, hidden, _tensor(w, DT_BF16), _stream(stream), ctypes.byref(h)))
     return h
 
 

@@ -7,15 +7,17 @@
 #include "moe_launch.h"
 
 namespace head {
-hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream);
+hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, bool fp8,
+                              hipStream_t stream);
 hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* codes, float* scales,
                                 hipStream_t stream);
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
-                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, hipStream_t stream);
+                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, bool fp8, hipStream_t stream);
 }
 
 struct fp8_head_handle {
     int V, H, VT, device;
+    bool fp8;          // E4M3 rows with scales, or bf16 rows (bf16_head_create)
     uint8_t* mem;      // repacked weights | scales | per-tile partials | ticket
     void* w;
     float* scale;
@@ -26,18 +28,8 @@ struct fp8_head_handle {
 
 static uint64_t a256(uint64_t v) { return (v + 255) & ~(uint64_t)255; }
 
-extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, void* stream,
-                                      fp8_head_handle** out) {
-    if (!out) return moe_fail(MOE_ERR_INVALID_ARG, "out is NULL");
-    if (vocab <= 0 || hidden <= 0) return moe_fail(MOE_ERR_INVALID_ARG, "vocab and hidden must be positive");
-    if (hidden % 256 || hidden > 2560)
-        return moe_fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", hidden);
-    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
-    if (!row_scale.ptr || (uintptr_t)row_scale.ptr % 4)
-        return moe_fail(MOE_ERR_INVALID_ARG, "row_scale is NULL or not 4-byte aligned");
-    if (w.dtype != MOE_DT_E4M3) return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected E4M3 (%d)", w.dtype, MOE_DT_E4M3);
-    if (row_scale.dtype != MOE_DT_FP32)
-        return moe_fail(MOE_ERR_DTYPE, "row_scale: dtype tag %d, expected FP32 (%d)", row_scale.dtype, MOE_DT_FP32);
+static moe_status head_create(int32_t vocab, int32_t hidden, const void* w, const void* row_scale, bool fp8,
+                              void* stream, fp8_head_handle** out) {
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
         (void)hipGetLastError();
@@ -48,8 +40,9 @@ extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor 
     h->V = vocab;
     h->H = hidden;
     h->VT = (vocab + 63) / 64;
+    h->fp8 = fp8;
     (void)hipGetDevice(&h->device);
-    const uint64_t wb = a256((uint64_t)h->VT * 64 * hidden), sb = a256((uint64_t)h->VT * 64 * 4);
+    const uint64_t wb = a256((uint64_t)h->VT * 64 * hidden * (fp8 ? 1 : 2)), sb = a256((uint64_t)h->VT * 64 * 4);
     const uint64_t pb = a256((uint64_t)h->VT * 4 * 4);
     if (hipMalloc(&h->mem, wb + sb + 2 * pb + 256) != hipSuccess) {
         (void)hipGetLastError();
@@ -62,7 +55,8 @@ extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor 
     h->pidx = (int32_t*)(h->mem + wb + sb + pb);
     h->ticket = (unsigned*)(h->mem + wb + sb + 2 * pb);
     hipError_t e = hipMemsetAsync(h->ticket, 0, 256, (hipStream_t)stream);
-    if (e == hipSuccess) e = head::launch_repack_head(w.ptr, row_scale.ptr, h->w, h->scale, vocab, hidden, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = head::launch_repack_head(w, row_scale, h->w, h->scale, vocab, hidden, fp8, (hipStream_t)stream);
     if (e != hipSuccess) {
         (void)hipFree(h->mem);
         delete h;
@@ -70,6 +64,36 @@ extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor 
     }
     *out = h;
     return MOE_OK;
+}
+
+static moe_status head_shape_check(int32_t vocab, int32_t hidden, fp8_head_handle** out) {
+    if (!out) return moe_fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (vocab <= 0 || hidden <= 0) return moe_fail(MOE_ERR_INVALID_ARG, "vocab and hidden must be positive");
+    if (hidden % 256 || hidden > 2560)
+        return moe_fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", hidden);
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_create(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, void* stream,
+                                      fp8_head_handle** out) {
+    moe_status st = head_shape_check(vocab, hidden, out);
+    if (st != MOE_OK) return st;
+    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
+    if (!row_scale.ptr || (uintptr_t)row_scale.ptr % 4)
+        return moe_fail(MOE_ERR_INVALID_ARG, "row_scale is NULL or not 4-byte aligned");
+    if (w.dtype != MOE_DT_E4M3) return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected E4M3 (%d)", w.dtype, MOE_DT_E4M3);
+    if (row_scale.dtype != MOE_DT_FP32)
+        return moe_fail(MOE_ERR_DTYPE, "row_scale: dtype tag %d, expected FP32 (%d)", row_scale.dtype, MOE_DT_FP32);
+    return head_create(vocab, hidden, w.ptr, row_scale.ptr, true, stream, out);
+}
+
+extern "C" moe_status bf16_head_create(int32_t vocab, int32_t hidden, moe_tensor w, void* stream,
+                                       fp8_head_handle** out) {
+    moe_status st = head_shape_check(vocab, hidden, out);
+    if (st != MOE_OK) return st;
+    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
+    if (w.dtype != MOE_DT_BF16) return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected BF16 (%d)", w.dtype, MOE_DT_BF16);
+    return head_create(vocab, hidden, w.ptr, nullptr, false, stream, out);
 }
 
 extern "C" moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t T, float* logits, int32_t* argmax,
@@ -80,7 +104,7 @@ extern "C" moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t T,
     if (T < 1 || T > 4) return moe_fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [1, 4]", T);
     if (hipSetDevice(h->device) != hipSuccess) return moe_fail(MOE_ERR_HIP, "hipSetDevice failed");
     hipError_t e = head::launch_head(h->w, h->scale, (const uint16_t*)x, T, logits, argmax, h->pval, h->pidx, h->ticket,
-                                     h->V, h->H, (hipStream_t)stream);
+                                     h->V, h->H, h->fp8, (hipStream_t)stream);
     if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }

@@ -6,7 +6,9 @@
 // "dgx-spark-moe-inference-optimizations", section 2).  Weights are OCP E4M3 with one fp32 scale
 // per row; x stays bf16; logits are fp32; argmax takes the lowest index among equal maxima.
 //
-// Layout (repacked by fp8_head_create): [ceil(V/64) tiles][H/16 units][64 lanes][16 B], lane = row
+// The same kernel also runs the unquantised BF16 head (bf16_head_create), for comparison.
+//
+// Layout (repacked at create): [ceil(V/64) tiles][row bytes/16 units][64 lanes][16 B], lane = row
 // within the 64-row tile, so each wave-wide 16-byte load reads 1 KiB of contiguous HBM.  Each
 // workgroup owns one 64-row tile; its waves split the K range, E4M3 pairs are converted exactly to
 // bf16 pairs in VGPRs and multiplied with bf16 x pairs from LDS by v_dot2_f32_bf16 (exact products,
@@ -18,9 +20,7 @@
 namespace head {
 
 constexpr int kWave = 64;
-constexpr int kUnit = 16;           // E4M3 codes per 16-byte unit
-constexpr int kUnitsPerWave = 16;   // 256 K elements per wave
-constexpr int kSlice = kUnit * kUnitsPerWave;
+constexpr int kSlice = 256;  // K elements per wave: 16 units of 16 E4M3 codes, or 32 units of 8 bf16
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -34,9 +34,9 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// NU 16-byte units per row (H / 16 for E4M3 rows, H / 8 for bf16 rows); ssrc null: scales of 1.
 __global__ void repack_head(const uint4* __restrict__ src, const float* __restrict__ ssrc, uint4* __restrict__ dst,
-                            float* __restrict__ sdst, int V, int H, int VT) {
-    const int NU = H / kUnit;
+                            float* __restrict__ sdst, int V, int NU, int VT) {
     const uint64_t total = (uint64_t)VT * NU * kWave;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
          u += (uint64_t)gridDim.x * blockDim.x) {
@@ -46,7 +46,7 @@ __global__ void repack_head(const uint4* __restrict__ src, const float* __restri
         const uint64_t vt = r1 / NU;
         const uint64_t row = vt * kWave + lane;
         dst[u] = row < (uint64_t)V ? src[row * NU + unit] : make_uint4(0, 0, 0, 0);
-        if (unit == 0) sdst[row] = row < (uint64_t)V ? ssrc[row] : 0.0f;
+        if (unit == 0) sdst[row] = row < (uint64_t)V ? (ssrc ? ssrc[row] : 1.0f) : 0.0f;
     }
 }
 
@@ -69,8 +69,12 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
     }
 }
 
-template <int T>
+// FP8: rows of E4M3 codes (16 per 16-byte unit), converted exactly to bf16 pairs; otherwise rows of
+// bf16 (8 per unit), the unquantised head the FP8 one replaces (its scales are 1).
+template <int T, bool FP8>
 __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
+    constexpr int kUnit = FP8 ? 16 : 8;             // K elements per 16-byte unit
+    constexpr int kUnitsPerWave = kSlice / kUnit;
     extern __shared__ uint32_t xs[];  // [T][H/2] bf16 pairs
     __shared__ float red[10][T][kWave];
     __shared__ int is_last;
@@ -93,22 +97,36 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
 #pragma unroll
     for (int i = 0; i < kUnitsPerWave; ++i) {
         const int pbase = (wv * kUnitsPerWave + i) * (kUnit / 2);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        if constexpr (!FP8) {
             uint4 xv[T];
 #pragma unroll
-            for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase + 4 * h);
+            for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint32_t wd = comp(wr[i], 2 * h + q);
-                const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, false);
-                const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, true);
+            for (int q = 0; q < 4; ++q) {
+                const bf16x2_t wq = __builtin_bit_cast(bf16x2_t, comp(wr[i], q));
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q)),
-                                                            acc[t], false);
-                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q + 1)),
-                                                            acc[t], false);
+                for (int t = 0; t < T; ++t)
+                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wq, __builtin_bit_cast(bf16x2_t, comp(xv[t], q)), acc[t],
+                                                            false);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint4 xv[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase + 4 * h);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t wd = comp(wr[i], 2 * h + q);
+                    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, false);
+                    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, true);
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q)),
+                                                                acc[t], false);
+                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(
+                            hi, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q + 1)), acc[t], false);
+                    }
                 }
             }
         }
@@ -214,29 +232,37 @@ hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* co
     return hipGetLastError();
 }
 
-hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, hipStream_t stream) {
-    const int VT = (V + kWave - 1) / kWave;
-    uint64_t total = (uint64_t)VT * (H / kUnit) * kWave;
+// w: E4M3 [V][H] with scales s (fp8), or bf16 [V][H] (s ignored, scales of 1)
+hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, int V, int H, bool fp8,
+                              hipStream_t stream) {
+    const int VT = (V + kWave - 1) / kWave, NU = fp8 ? H / 16 : H / 8;
+    uint64_t total = (uint64_t)VT * NU * kWave;
     uint64_t g = (total + 255) / 256;
     if (g > 65536) g = 65536;
-    repack_head<<<(unsigned)g, 256, 0, stream>>>((const uint4*)w, (const float*)s, (uint4*)dw, (float*)ds, V, H, VT);
+    repack_head<<<(unsigned)g, 256, 0, stream>>>((const uint4*)w, fp8 ? (const float*)s : nullptr, (uint4*)dw,
+                                                 (float*)ds, V, NU, VT);
+    return hipGetLastError();
+}
+
+template <bool FP8>
+static hipError_t launch_head_t(const HeadArgs& a, int T, int VT, hipStream_t stream) {
+    const unsigned block = kWave * (a.H / kSlice);
+    const size_t lds = (size_t)T * a.H * 2;
+    switch (T) {
+        case 1: head_kernel<1, FP8><<<VT, block, lds, stream>>>(a); break;
+        case 2: head_kernel<2, FP8><<<VT, block, lds, stream>>>(a); break;
+        case 3: head_kernel<3, FP8><<<VT, block, lds, stream>>>(a); break;
+        case 4: head_kernel<4, FP8><<<VT, block, lds, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
-                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, hipStream_t stream) {
+                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, bool fp8, hipStream_t stream) {
     const int VT = (V + kWave - 1) / kWave;
     HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, V, H};
-    const unsigned block = kWave * (H / kSlice);
-    const size_t lds = (size_t)T * H * 2;
-    switch (T) {
-        case 1: head_kernel<1><<<VT, block, lds, stream>>>(a); break;
-        case 2: head_kernel<2><<<VT, block, lds, stream>>>(a); break;
-        case 3: head_kernel<3><<<VT, block, lds, stream>>>(a); break;
-        case 4: head_kernel<4><<<VT, block, lds, stream>>>(a); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return fp8 ? launch_head_t<true>(a, T, VT, stream) : launch_head_t<false>(a, T, VT, stream);
 }
 
 }  // namespace head

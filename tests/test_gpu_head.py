@@ -149,3 +149,43 @@ def test_full_head_quantised_on_device():
     torch.cuda.synchronize()
     moe.fp8_head_destroy(h)
     assert am.cpu().numpy().tolist() == m["argmax"]
+
+
+def _run_bf16(Wb, x):
+    h = moe.bf16_head_create(torch.from_numpy(Wb.view(np.int16)).to(dev()).view(torch.bfloat16))
+    T = x.shape[0]
+    am = torch.full((T,), -1, dtype=torch.int32, device=dev())
+    lg = torch.empty((T, Wb.shape[0]), dtype=torch.float32, device=dev())
+    moe.fp8_head_run(h, to_dev_u16(x), am, lg)
+    torch.cuda.synchronize()
+    moe.fp8_head_destroy(h)
+    return am.cpu().numpy(), lg.cpu().numpy()
+
+
+@pytest.mark.parametrize("V,T,H", [(3000, 4, 2560), (64 * 5 + 3, 1, 2560), (200, 3, 512)])
+def test_bf16_head_matches_oracle(V, T, H):
+    """The unquantised BF16 head (the comparison point of the FP8 head): logits within the fp32
+    evaluation bound of the oracle's fp64 logits, argmax exact where it is well posed."""
+    Wb = _bf16_bits(synth.head_weights(V, H, 17))
+    x = synth.tokens(H, 17, T)
+    lg_o, bd_o, am_o = oracle.head_logits_bf16(Wb, x)
+    am, lg = _run_bf16(Wb, x)
+    assert (np.abs(lg - lg_o) <= bd_o).all()
+    for t in range(T):
+        if oracle.argmax_margin_ok(lg_o[t], bd_o[t]):
+            assert am[t] == am_o[t]
+
+
+def test_full_bf16_head_argmax():
+    m = MANIFEST["head"]
+    V, H = m["vocab"], m["hidden"]
+    Wb = np.concatenate([_bf16_bits(synth.head_weights(V, H, m["seed"], r0, min(16384, V - r0)))
+                         for r0 in range(0, V, 16384)])
+    x = synth.tokens(H, m["seed"], 4, m["x_attempt"])[:2]
+    lg_o, bd_o, am_o = oracle.head_logits_bf16(Wb, x)
+    am, lg = _run_bf16(Wb, x)
+    for t in range(2):
+        assert oracle.argmax_margin_ok(lg_o[t], bd_o[t])
+        assert am[t] == am_o[t]
+    rows = np.arange(0, V, 613)
+    assert (np.abs(lg[:, rows] - lg_o[:, rows]) <= bd_o[:, rows]).all()
