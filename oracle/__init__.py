@@ -31,6 +31,7 @@ PINS = {
     "rmsnorm_bf16": "constant-vector closed form; power-of-two scale invariance",
     "residual_bf16": "bf16 round trip vs torch",
     "head": "argmax brute force; duplicate-row tie; BLAS GEMV special case",
+    "mtp_accept": "hand cases: all, none, first-mismatch positions, a match after a mismatch is not accepted",
     "head_bf16": "BLAS GEMV special case; equals the FP8 head exactly on rows that are E4M3 values times a power of two",
 }
 
@@ -285,6 +286,17 @@ def head_logits_bf16(W, x, want_logits: bool = True, want_bounds: bool = True):
     am = np.empty(T, dtype=np.int32)
     lib().oracle_head_logits_bf16(_p(W), V, H, _p(x), T, _p(lg), _p(bd), _p(am))
     return lg, bd, am
+
+
+def mtp_accept(argmax, draft) -> int:
+    """Greedy acceptance of a speculative verify step: position i's target token argmax[i] is the
+    model's next token after position i, and draft[i] the drafted token for position i + 1.  The
+    drafts are accepted while they equal the target's tokens; returns how many were accepted
+    (0 .. len(draft)); the step then emits those drafts plus argmax[accepted]."""
+    n = 0
+    while n < len(draft) and int(argmax[n]) == int(draft[n]):
+        n += 1
+    return n
 
 
 # ---- margins (well-posedness of integer results under fp32 evaluation) -----------------------

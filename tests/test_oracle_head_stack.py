@@ -140,3 +140,14 @@ def test_residual_matches_torch():
     ours = oracle.residual_bf16(x, y)
     ref = (torch.from_numpy(oracle.bf16_decode(x)) + torch.from_numpy(y)).to(torch.bfloat16)
     assert (ours == ref.view(torch.int16).numpy().view(np.uint16)).all()
+
+
+def test_mtp_accept_longest_matching_prefix():
+    # 4 verify positions, 3 drafts: the drafts are accepted up to the first mismatch only
+    assert oracle.mtp_accept([5, 7, 9, 11], [5, 7, 9]) == 3
+    assert oracle.mtp_accept([5, 7, 9, 11], [6, 7, 9]) == 0
+    assert oracle.mtp_accept([5, 7, 9, 11], [5, 8, 9]) == 1
+    assert oracle.mtp_accept([5, 7, 9, 11], [5, 7, 10]) == 2
+    assert oracle.mtp_accept([5, 7, 9, 11], [4, 7, 9]) == 0  # later matches do not count
+    assert oracle.mtp_accept([3, 1], [3]) == 1 and oracle.mtp_accept([3, 1], [2]) == 0
+    assert oracle.mtp_accept([3], []) == 0
