@@ -183,6 +183,17 @@ moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t num_tokens, f
                         void* stream);
 moe_status fp8_head_destroy(fp8_head_handle* h);
 
+/* The head of a speculative verify step with its greedy acceptance fused in (tanhow.com, section
+ * "三项优化是什么", item 3: one verify pass scores the current token and the drafted ones;
+ * devotd.net, "dgx-spark-moe-inference-optimizations", section 3).  x holds the T positions (BF16
+ * [T][H], 2 <= T <= 4): the current token, then the T-1 drafted ones; draft (INT32 [T-1], device)
+ * holds those drafted token ids.  Writes argmax[t] (INT32 [T]) as fp8_head_run does, and
+ * accept[0] = the number n of leading drafts that equal the target's tokens (draft[i] ==
+ * argmax[i] for every i < n, 0 <= n <= T-1); the step then emits draft[0 .. n-1] and argmax[n].
+ * All pointers are device pointers; only enqueues work on `stream`. */
+moe_status fp8_head_verify(fp8_head_handle* h, const void* x, int32_t num_tokens, const int32_t* draft,
+                           int32_t* argmax, int32_t* accept, void* stream);
+
 /* Per-row FP8 quantisation of an LM-head weight matrix at load time, the step that makes the FP8
  * head (tanhow.com, section "三项优化是什么", item 2: the head is kept in FP8 instead of BF16 so that
  * each decode step reads half the bytes; devotd.net, "dgx-spark-moe-inference-optimizations",

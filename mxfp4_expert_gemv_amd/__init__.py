@@ -24,7 +24,7 @@ F_PERSISTENT = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
-           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize", "bf16_head_create",
+           "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize", "bf16_head_create", "fp8_head_verify",
            "moe_status_string", "moe_last_error")
 
 
@@ -95,6 +95,7 @@ def lib():
             "fp8_head_destroy": [vp],
             "fp8_head_quantize": [i32, i32, Tensor, vp, vp, vp],
             "bf16_head_create": [i32, i32, Tensor, vp, ctypes.POINTER(vp)],
+            "fp8_head_verify": [vp, vp, i32, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -208,6 +209,13 @@ def bf16_head_create(w, stream=None) -> ctypes.c_void_p:
 def fp8_head_run(handle, x, argmax, logits=None, num_tokens: int | None = None, stream=None) -> None:
     T = x.shape[0] if num_tokens is None else num_tokens
     _check(lib().fp8_head_run(handle, _ptr(x), T, _ptr(logits), _ptr(argmax), _stream(stream)))
+
+
+def fp8_head_verify(handle, x, draft, argmax, accept, stream=None) -> None:
+    """Head of a verify step (x [T][H] bf16, draft int32 [T-1], argmax int32 [T], accept int32 [1],
+    all on the device): argmax and the number of accepted drafts; enqueues only."""
+    _check(lib().fp8_head_verify(handle, _ptr(x), x.shape[0], _ptr(draft), _ptr(argmax), _ptr(accept),
+                                 _stream(stream)))
 
 
 def fp8_head_destroy(handle) -> None:

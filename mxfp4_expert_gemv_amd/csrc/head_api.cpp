@@ -12,7 +12,8 @@ hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, 
 hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* codes, float* scales,
                                 hipStream_t stream);
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
-                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, bool fp8, hipStream_t stream);
+                       float* pval, int32_t* pidx, unsigned* ticket, const int32_t* draft, int32_t* accept, int V,
+                       int H, bool fp8, hipStream_t stream);
 }
 
 struct fp8_head_handle {
@@ -104,7 +105,20 @@ extern "C" moe_status fp8_head_run(fp8_head_handle* h, const void* x, int32_t T,
     if (T < 1 || T > 4) return moe_fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [1, 4]", T);
     if (hipSetDevice(h->device) != hipSuccess) return moe_fail(MOE_ERR_HIP, "hipSetDevice failed");
     hipError_t e = head::launch_head(h->w, h->scale, (const uint16_t*)x, T, logits, argmax, h->pval, h->pidx, h->ticket,
-                                     h->V, h->H, h->fp8, (hipStream_t)stream);
+                                     nullptr, nullptr, h->V, h->H, h->fp8, (hipStream_t)stream);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_verify(fp8_head_handle* h, const void* x, int32_t T, const int32_t* draft,
+                                      int32_t* argmax, int32_t* accept, void* stream) {
+    if (!h) return moe_fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!x || (uintptr_t)x % 16) return moe_fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+    if (!draft || !argmax || !accept) return moe_fail(MOE_ERR_INVALID_ARG, "draft, argmax and accept are required");
+    if (T < 2 || T > 4) return moe_fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [2, 4]", T);
+    if (hipSetDevice(h->device) != hipSuccess) return moe_fail(MOE_ERR_HIP, "hipSetDevice failed");
+    hipError_t e = head::launch_head(h->w, h->scale, (const uint16_t*)x, T, nullptr, argmax, h->pval, h->pidx, h->ticket,
+                                     draft, accept, h->V, h->H, h->fp8, (hipStream_t)stream);
     if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }

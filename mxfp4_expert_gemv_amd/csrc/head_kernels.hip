@@ -59,6 +59,8 @@ struct HeadArgs {
     float* pval;          // [VT][T] per-tile maxima
     int32_t* pidx;        // [VT][T]
     unsigned* ticket;
+    const int32_t* draft;  // [T-1] drafted tokens of positions 1 .. T-1, or null
+    int32_t* accept;       // [1] accepted drafts (with draft)
     int V, H;
 };
 
@@ -160,6 +162,7 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
         is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
     __syncthreads();
     if (!is_last) return;
+    __shared__ int32_t am_s[T];
     for (int t = wv; t < T; t += NW) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
@@ -167,7 +170,20 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
             better(bv, bi, __hip_atomic_load(a.pval + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                    __hip_atomic_load(a.pidx + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         for (int off = 32; off > 0; off >>= 1) better(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
-        if (lane == 0) a.argmax[t] = bi;
+        if (lane == 0) {
+            a.argmax[t] = bi;
+            am_s[t] = bi;
+        }
+    }
+    if (a.draft) {
+        // greedy acceptance of a speculative verify step: the drafts are kept while each equals the
+        // target's token of the position before it
+        __syncthreads();
+        if (tid == 0) {
+            int n = 0;
+            while (n < T - 1 && am_s[n] == a.draft[n]) ++n;
+            *a.accept = n;
+        }
     }
     if (tid == 0) *a.ticket = 0u;
 }
@@ -259,9 +275,10 @@ static hipError_t launch_head_t(const HeadArgs& a, int T, int VT, hipStream_t st
 }
 
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
-                       float* pval, int32_t* pidx, unsigned* ticket, int V, int H, bool fp8, hipStream_t stream) {
+                       float* pval, int32_t* pidx, unsigned* ticket, const int32_t* draft, int32_t* accept, int V,
+                       int H, bool fp8, hipStream_t stream) {
     const int VT = (V + kWave - 1) / kWave;
-    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, V, H};
+    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, draft, accept, V, H};
     return fp8 ? launch_head_t<true>(a, T, VT, stream) : launch_head_t<false>(a, T, VT, stream);
 }
 

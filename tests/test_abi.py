@@ -98,3 +98,8 @@ def test_head_quantize_arguments_checked_before_device():
     assert L.fp8_head_quantize(8, 2560, moe.Tensor(addr, moe.DT_E4M3), addr, addr, None) == -3
     assert L.fp8_head_quantize(8, 2560, ok, None, addr, None) == -1
     assert L.fp8_head_quantize(8, 2560, ok, addr, None, None) == -1
+
+
+def test_head_verify_arguments():
+    L = moe.lib()
+    assert L.fp8_head_verify(None, None, 4, None, None, None, None) == -1

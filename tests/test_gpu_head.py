@@ -189,3 +189,34 @@ def test_full_bf16_head_argmax():
         assert am[t] == am_o[t]
     rows = np.arange(0, V, 613)
     assert (np.abs(lg[:, rows] - lg_o[:, rows]) <= bd_o[:, rows]).all()
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_verify_accepts_longest_matching_prefix(T):
+    """Greedy acceptance fused after the argmax: drafts built from the oracle's target tokens so that
+    every accept count 0 .. T-1 occurs, plus a draft that matches only after a mismatch."""
+    V, H = 3000, 2560
+    Wq, s = _quantised(V, H, seed=13)
+    x = synth.tokens(H, 13, T)
+    lg_o, bd_o, am_o = oracle.head_logits(Wq, s, x)
+    assert all(oracle.argmax_margin_ok(lg_o[t], bd_o[t]) for t in range(T))
+    h = moe.fp8_head_create(torch.from_numpy(Wq).to(dev()), torch.from_numpy(s).to(dev()))
+    xd = to_dev_u16(x)
+    cases = []
+    for n in range(T):  # the first n drafts match, draft n (if any) does not
+        d = [int(am_o[i]) for i in range(T - 1)]
+        if n < T - 1:
+            d[n] = (d[n] + 1) % V
+        cases.append(d)
+    if T > 2:
+        d = [int(am_o[i]) for i in range(T - 1)]
+        d[0] = (d[0] + 7) % V
+        cases.append(d)
+    for d in cases:
+        am = torch.full((T,), -1, dtype=torch.int32, device=dev())
+        acc = torch.full((1,), -1, dtype=torch.int32, device=dev())
+        moe.fp8_head_verify(h, xd, torch.tensor(d, dtype=torch.int32, device=dev()), am, acc)
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == am_o.tolist()
+        assert int(acc.item()) == oracle.mtp_accept(am_o, d), (d, am_o.tolist())
+    moe.fp8_head_destroy(h)
