@@ -300,23 +300,25 @@ def summarize(dirs):
             a[1] += 1
         kib = {k: v[0] / v[1] for k, v in acc.items()}
         print()
-        print("| kernel | counter | KiB per dispatch | dispatches | scale (copy probe) | bytes per dispatch |")
+        print("| kernel | counter | mean per dispatch (KiB for FETCH_SIZE / WRITE_SIZE) | dispatches | "
+              "scale (copy probe) | bytes per dispatch |")
         print("|---|---|---:|---:|---:|---:|")
         rec = {"kernel_source_sha256_16": source_digest(), "copy_probe_bytes": COPY_PROBE_BYTES, "scale": scale,
                "kernels": {}}
         for (n, c), v in sorted(kib.items()):
             sc = scale.get(c)
             b = v * 1024 * sc if sc else None
-            print(f"| `{n}` | {c} | {v:.1f} | {acc[(n, c)][1]} | {sc if sc is None else round(sc, 4)} | "
+            print(f"| `{n}` | {c} | {v:.2f} | {acc[(n, c)][1]} | {'' if sc is None else round(sc, 4)} | "
                   f"{'' if b is None else int(b)} |")
             if b is not None:
                 k = rec["kernels"].setdefault(n, {"hbm_bytes_per_launch": 0})
                 k[c] = int(b)
                 k["hbm_bytes_per_launch"] += int(b)
-        print()
-        print("```json")
-        print(json.dumps(rec, indent=1))
-        print("```")
+        if rec["kernels"]:
+            print()
+            print("```json")
+            print(json.dumps(rec, indent=1))
+            print("```")
 
 
 def kernel_bytes(shape, T, distinct):
