@@ -40,8 +40,6 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 LM-head measurement")
-    ap.add_argument("--variant", choices=("persistent", "three_kernels"), default="three_kernels",
-                    help="kernel set: three kernels per layer (default, the faster one) or one persistent kernel per pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
@@ -85,10 +83,7 @@ def main():
             "w2": torch.empty((n, H, I // 2), **u8), "w2_s": torch.empty((n, H, I // 32), **u8)}
 
     t0 = time.time()
-    vflags = moe.F_PERSISTENT if args.variant == "persistent" else 0
-    persistent = vflags != 0
-    h = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, L,
-                              moe.F_RMSNORM_INPUT | vflags)
+    h = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, L, moe.F_RMSNORM_INPUT)
     for l in range(L):
         layer_tensors(st["seed"], l, st["router_attempts"][l], bufs)
         moe.moe_decode_set_layer(h, l, bufs["router"], bufs["w13"], bufs["w13_s"], bufs["w2"], bufs["w2_s"])
@@ -126,8 +121,6 @@ def main():
             moe.moe_decode_run(h, x4[:T], T, x_out=x_out[:T])
         t = moe.moe_decode_timing_read(h)
         moe.moe_decode_timing_enable(h, 0)
-        if persistent:  # one kernel per pass, in class 0
-            return {"stack": t["router"]["total_ms"] / max(t["router"]["launches"], 1) * 1e3}
         return {c: t[c]["total_ms"] / max(t[c]["launches"], 1) * 1e3 for c in moe.TIMING_CLASSES}  # us/launch
 
     if args.copy_probe:
@@ -143,7 +136,7 @@ def main():
     for T in (1, 4):
         nbytes, distinct = pass_bytes(T)
         ms = time_stack(T, args.steps, args.warmup)
-        moe.moe_decode_check(h)  # every timed pass completed (no expired wait)
+        moe.moe_decode_check(h)  # no asynchronous device error
         kt = kernel_times(T, min(args.steps, 50))
         gbs = nbytes / (ms * 1e-3) / 1e9
         results[T] = {"ms_per_pass": ms, "us_per_layer": ms * 1e3 / L, "tokens_per_s": T / (ms * 1e-3),
@@ -161,7 +154,7 @@ def main():
         for name, key, T in (("layer_t1", "layer_t1", 1), ("layer_t4", "layer_t4", 4),
                              ("layer_t4_overlap", "layer_t4", 4)):
             m = man[key]
-            h1 = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, 1, vflags)
+            h1 = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, 1)
             layer_tensors(m["seed"], 0, 0, bufs)
             moe.moe_decode_set_layer(h1, 0, bufs["router"], bufs["w13"], bufs["w13_s"], bufs["w2"], bufs["w2_s"])
             if name == "layer_t4_overlap":
@@ -198,7 +191,7 @@ def main():
     # roofline of the dominant kernel of a 1-token layer (the one with the largest kernel time)
     kt1 = results[1]["kernel_us"]
     names = kernel_names(info["variant"], 1)
-    kb = {"stack": results[1]["bytes_per_pass"]} if persistent else kernel_bytes(shape, 1, shape.top_k)
+    kb = kernel_bytes(shape, 1, shape.top_k)
     per_kernel = {c: {"kernel": names[c], "bytes_per_launch": kb[c], "us_per_launch": round(kt1[c], 3),
                       "gb_s": round(kb[c] / (kt1[c] * 1e-6) / 1e9, 1)} for c in kt1}
     dom = max(kt1, key=lambda c: kt1[c])
@@ -335,11 +328,7 @@ def kernel_bytes(shape, T, distinct):
 
 def kernel_names(variant, T):
     """Full names of the kernels as the profiler lists them, from the library's variant string
-    (gfx950-persistent-n<workgroups>-dn<ksub>x<iters>, or
-    gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-...)."""
-    if variant.startswith("gfx950-persistent"):
-        ksub, iters = (int(v) for v in variant.split("-")[3][2:].split("x"))
-        return {"stack": f"void moe::pk::stack_kernel<{T}, {ksub}, {iters}>(moe::pk::StackArgs)"}
+    (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-...)."""
     gu, dn = variant.split("-")[2:4]
     bpl = int(gu[2:].split("x")[1])
     ksub, iters = (int(v) for v in dn[2:].split("x"))

@@ -79,10 +79,6 @@ typedef enum {
 #define MOE_F_RMSNORM_INPUT 0x1u /* each layer's MoE input is RMSNorm(x), eps 1e-6, unweighted */
 #define MOE_F_DIRECT_LAUNCH 0x2u /* launch the kernels on the stream at every run instead of replaying
                                     a HIP graph captured on the first run with the same arguments */
-#define MOE_F_PERSISTENT 0x4u    /* one persistent kernel per run on row-major weights instead of the
-                                    default three kernels per layer on repacked weights (router +
-                                    top-k, gate/up, down + combine); MOE_F_DIRECT_LAUNCH applies to
-                                    the default mode only */
 
 typedef struct moe_decode_handle moe_decode_handle;
 typedef struct fp8_head_handle fp8_head_handle;
@@ -140,8 +136,8 @@ typedef struct {
  * only on success. */
 moe_status moe_decode_create(const moe_decode_config* cfg, void* stream, moe_decode_handle** out);
 
-/* Copies the weights of layer `layer` (0-based) into the handle, on `stream` (repacked into lane
- * tiles by default, kept row-major with MOE_F_PERSISTENT). */
+/* Copies the weights of layer `layer` (0-based) into the handle, on `stream`, repacked into lane
+ * tiles (a permutation of 16-byte units and scale bytes; no value changes). */
 moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_layer_desc* desc, void* stream);
 
 /* Runs all L layers on x (BF16 [T][H], device, 16-byte aligned), 1 <= T <= max_tokens.
@@ -149,20 +145,14 @@ moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_l
  * MOE_F_DIRECT_LAUNCH is set, the first call with a given (x, T, outputs) captures the kernel
  * sequence (three kernels per layer, plus two small ones per layer at 3-4 tokens) into a HIP graph
  * owned by the handle and every later call with the same arguments replays it (up to 16 graphs;
- * they hold pointers, not data, so new contents of x and new weights are picked up).  With
- * MOE_F_PERSISTENT the whole pass is one cooperative launch of a persistent kernel (one
- * workgroup per compute unit; the device must not be running other work that keeps compute
- * units busy, or the launch fails with MOE_ERR_HIP). */
+ * they hold pointers, not data, so new contents of x and new weights are picked up). */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t num_tokens, const moe_outputs* out,
                           void* stream);
 
 moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_info* info);
 
-/* Waits for the device and reports whether any run of this handle was aborted.  The persistent
- * kernel (MOE_F_PERSISTENT) bounds every wait of one workgroup for another (200 ms); when a wait
- * expires, every workgroup leaves the kernel, the run's outputs are invalid and every later run
- * of the handle returns at once without computing.  Returns MOE_OK, or MOE_ERR_HIP with the round,
- * layer and workgroup of the first expired wait in moe_last_error(). */
+/* Waits for the handle's device to finish all work and returns MOE_ERR_HIP, with the runtime's
+ * message in moe_last_error(), when that work ended in an asynchronous error; MOE_OK otherwise. */
 moe_status moe_decode_check(moe_decode_handle* h);
 
 /* Frees the handle's device memory (synchronises the device first).  NULL is a no-op. */
@@ -199,7 +189,8 @@ moe_status fp8_head_verify(fp8_head_handle* h, const void* x, int32_t num_tokens
  * each decode step reads half the bytes; devotd.net, "dgx-spark-moe-inference-optimizations",
  * section 2).  For every row r of W (BF16 or FP32 [rows][cols], row-major, tag checked):
  *   scales[r]   = fl32(max_c |W[r][c]| / 448), or 1 for an all-zero row;
- *   codes[r][c] = OCP E4M3 round-to-nearest-even of fl32(W[r][c] / scales[r]).
+ *   codes[r][c] = OCP E4M3 round-to-nearest-even of fl32(W[r][c] / scales[r]) (a NaN element gives
+ *                 the NaN code S.1111.111 with its sign; NaNs do not enter the row maximum).
  * The outputs (E4M3 [rows][cols] and FP32 [rows], caller-owned device buffers, 8- and 4-byte
  * aligned) are the inputs fp8_head_create takes.  cols: a multiple of 256 up to 2560.  Only
  * enqueues work on `stream`; W may be freed after the stream has synchronised.  Errors:

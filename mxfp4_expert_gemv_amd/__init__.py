@@ -20,7 +20,6 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
 F_RMSNORM_INPUT = 0x1
 F_DIRECT_LAUNCH = 0x2
-F_PERSISTENT = 0x4
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
@@ -60,8 +59,7 @@ class Info(ctypes.Structure):
                 ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
 
 
-# kernel classes of the timing record: three kernels per layer (default), or the one whole-pass
-# kernel in class 0 (MOE_F_PERSISTENT)
+# kernel classes of the timing record
 TIMING_CLASSES = ("router", "gateup", "down")
 
 
@@ -127,32 +125,97 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _tensor(t, default_tag: int) -> Tensor:
-    """A torch tensor (tag from its slot) or a (tensor, tag) pair (explicit tag)."""
+def _dtype_tag(t, byte_tag: int) -> int:
+    """The tag of a torch tensor, from its own dtype: bfloat16 -> BF16, float32 -> FP32,
+    float8_e4m3fn -> E4M3, float8_e8m0fnu -> E8M0, float4_e2m1fn_x2 -> E2M1X2; raw bytes (uint8)
+    take the byte format of the slot they are passed in (E2M1X2, E8M0 or E4M3).  Any other dtype
+    gets tag -1, which every slot rejects."""
+    import torch
+    fixed = {torch.bfloat16: DT_BF16, torch.float32: DT_FP32}
+    for name, tag in (("float8_e4m3fn", DT_E4M3), ("float8_e8m0fnu", DT_E8M0), ("float4_e2m1fn_x2", DT_E2M1X2)):
+        if hasattr(torch, name):
+            fixed[getattr(torch, name)] = tag
+    if t.dtype == torch.uint8:
+        return byte_tag
+    return fixed.get(t.dtype, -1)
+
+
+def _check_buffer(t, name: str, nbytes: int) -> None:
+    """t must be a contiguous tensor on the GPU holding exactly nbytes."""
+    if not t.is_cuda:
+        raise ValueError(f"{name}: not a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    got = t.numel() * t.element_size()
+    if got != nbytes:
+        raise ValueError(f"{name}: {got} bytes, expected {nbytes} ({tuple(t.shape)} {t.dtype})")
+
+
+def _tensor(t, byte_tag: int, name: str = "tensor", nbytes: int | None = None) -> Tensor:
+    """A torch tensor, tagged from its own dtype (see _dtype_tag), or a (tensor, tag) pair with an
+    explicit tag.  With nbytes, the tensor's placement, layout and size are checked first."""
     if isinstance(t, tuple):
         t, tag = t
     else:
-        tag = default_tag
-    return Tensor(None if t is None else t.data_ptr(), tag)
+        tag = None if t is None else _dtype_tag(t, byte_tag)
+    if t is not None and nbytes is not None:
+        _check_buffer(t, name, nbytes)
+    return Tensor(None if t is None else t.data_ptr(), -1 if tag is None else tag)
+
+
+class Handle(ctypes.c_void_p):
+    """Opaque handle of the library, with the sizes it was created for (used by the argument
+    checks of this binding)."""
 
 
 def moe_decode_create(hidden: int, num_experts: int, top_k: int, num_shared: int, inter: int, max_tokens: int,
                       num_layers: int = 1, flags: int = 0, stream=None) -> ctypes.c_void_p:
     cfg = Config(ctypes.sizeof(Config), hidden, num_experts, top_k, num_shared, inter, max_tokens, num_layers, flags)
-    h = ctypes.c_void_p()
+    h = Handle()
     _check(lib().moe_decode_create(ctypes.byref(cfg), _stream(stream) if stream != 0 else None, ctypes.byref(h)))
+    h.sizes = dict(H=hidden, E=num_experts, k=top_k, S=num_shared, I=inter, T=max_tokens, L=num_layers)
     return h
 
 
 def moe_decode_set_layer(handle, layer: int, router, w13, w13_s, w2, w2_s, stream=None) -> None:
-    d = LayerDesc(_tensor(router, DT_BF16), _tensor(w13, DT_E2M1X2), _tensor(w13_s, DT_E8M0),
-                  _tensor(w2, DT_E2M1X2), _tensor(w2_s, DT_E8M0))
+    z = getattr(handle, "sizes", None)
+    H, E, S, I = (None,) * 4 if z is None else (z["H"], z["E"], z["S"], z["I"])
+    n = None if z is None else E + S
+
+    def nbytes(f):
+        return None if z is None else f()
+
+    d = LayerDesc(_tensor(router, DT_BF16, "router", nbytes(lambda: E * H * 2)),
+                  _tensor(w13, DT_E2M1X2, "w13", nbytes(lambda: n * I * H)),
+                  _tensor(w13_s, DT_E8M0, "w13_s", nbytes(lambda: n * 2 * I * H // 32)),
+                  _tensor(w2, DT_E2M1X2, "w2", nbytes(lambda: n * H * I // 2)),
+                  _tensor(w2_s, DT_E8M0, "w2_s", nbytes(lambda: n * H * I // 32)))
     _check(lib().moe_decode_set_layer(handle, layer, ctypes.byref(d), _stream(stream)))
 
 
 def moe_decode_run(handle, x, num_tokens: int | None = None, x_out=None, y=None, topk_ids=None, topk_w=None,
                    x_trace=None, x_scale=None, x_codes=None, stream=None) -> None:
+    import torch
     T = x.shape[0] if num_tokens is None else num_tokens
+    z = getattr(handle, "sizes", None)
+    if z is not None:
+        H, L, k = z["H"], z["L"], z["k"]
+        if x.dtype != torch.bfloat16:
+            raise ValueError(f"x: dtype {x.dtype}, expected torch.bfloat16")
+        if not 1 <= T <= z["T"] or x.numel() < T * H:
+            raise ValueError(f"x: {tuple(x.shape)} holds fewer than {T} tokens of {H}")
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError("x: not a contiguous GPU tensor")
+        for t, name, dt, nbytes in ((x_out, "x_out", torch.bfloat16, T * H * 2), (y, "y", torch.float32, T * H * 4),
+                                    (topk_ids, "topk_ids", torch.int32, L * T * k * 4),
+                                    (topk_w, "topk_w", torch.float32, L * T * k * 4),
+                                    (x_trace, "x_trace", torch.bfloat16, L * T * H * 2),
+                                    (x_scale, "x_scale", torch.float32, L * T * 4),
+                                    (x_codes, "x_codes", torch.uint8, L * T * H)):
+            if t is not None:
+                if t.dtype != dt:
+                    raise ValueError(f"{name}: dtype {t.dtype}, expected {dt}")
+                _check_buffer(t, name, nbytes)
     o = Outputs(ctypes.sizeof(Outputs), _ptr(x_out), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(x_trace),
                 _ptr(x_scale), _ptr(x_codes))
     _check(lib().moe_decode_run(handle, _ptr(x), T, ctypes.byref(o), _stream(stream)))
@@ -191,9 +254,10 @@ def moe_decode_timing_read(handle) -> dict:
 def fp8_head_create(w, row_scale, stream=None) -> ctypes.c_void_p:
     wt = w[0] if isinstance(w, tuple) else w
     vocab, hidden = wt.shape
-    h = ctypes.c_void_p()
-    _check(lib().fp8_head_create(vocab, hidden, _tensor(w, DT_E4M3), _tensor(row_scale, DT_FP32), _stream(stream),
-                                 ctypes.byref(h)))
+    h = Handle()
+    _check(lib().fp8_head_create(vocab, hidden, _tensor(w, DT_E4M3, "w", vocab * hidden),
+                                 _tensor(row_scale, DT_FP32, "row_scale", vocab * 4), _stream(stream), ctypes.byref(h)))
+    h.sizes = dict(V=vocab, H=hidden)
     return h
 
 
@@ -201,21 +265,44 @@ def bf16_head_create(w, stream=None) -> ctypes.c_void_p:
     """The BF16 head (w torch bfloat16 [V][H], device); run and free it with fp8_head_run and
     fp8_head_destroy."""
     vocab, hidden = w.shape
-    h = ctypes.c_void_p()
-    _check(lib().bf16_head_create(vocab, hidden, _tensor(w, DT_BF16), _stream(stream), ctypes.byref(h)))
+    h = Handle()
+    _check(lib().bf16_head_create(vocab, hidden, _tensor(w, DT_BF16, "w", vocab * hidden * 2), _stream(stream),
+                                  ctypes.byref(h)))
+    h.sizes = dict(V=vocab, H=hidden)
     return h
 
 
+def _check_head_io(handle, x, T, outs):
+    import torch
+    z = getattr(handle, "sizes", None)
+    if z is None:
+        return
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.numel() < T * z["H"]:
+        raise ValueError(f"x: needs a contiguous bfloat16 GPU tensor of {T} x {z['H']}")
+    for t, name, dt, nbytes in outs:
+        if t is not None:
+            if t.dtype != dt:
+                raise ValueError(f"{name}: dtype {t.dtype}, expected {dt}")
+            _check_buffer(t, name, nbytes(z))
+
+
 def fp8_head_run(handle, x, argmax, logits=None, num_tokens: int | None = None, stream=None) -> None:
+    import torch
     T = x.shape[0] if num_tokens is None else num_tokens
+    _check_head_io(handle, x, T, ((argmax, "argmax", torch.int32, lambda z: T * 4),
+                                  (logits, "logits", torch.float32, lambda z: T * z["V"] * 4)))
     _check(lib().fp8_head_run(handle, _ptr(x), T, _ptr(logits), _ptr(argmax), _stream(stream)))
 
 
 def fp8_head_verify(handle, x, draft, argmax, accept, stream=None) -> None:
     """Head of a verify step (x [T][H] bf16, draft int32 [T-1], argmax int32 [T], accept int32 [1],
     all on the device): argmax and the number of accepted drafts; enqueues only."""
-    _check(lib().fp8_head_verify(handle, _ptr(x), x.shape[0], _ptr(draft), _ptr(argmax), _ptr(accept),
-                                 _stream(stream)))
+    import torch
+    T = x.shape[0]
+    _check_head_io(handle, x, T, ((draft, "draft", torch.int32, lambda z: (T - 1) * 4),
+                                  (argmax, "argmax", torch.int32, lambda z: T * 4),
+                                  (accept, "accept", torch.int32, lambda z: 4)))
+    _check(lib().fp8_head_verify(handle, _ptr(x), T, _ptr(draft), _ptr(argmax), _ptr(accept), _stream(stream)))
 
 
 def fp8_head_destroy(handle) -> None:
@@ -227,5 +314,9 @@ def fp8_head_quantize(w, codes, scales, stream=None) -> None:
     (uint8 [rows][cols]) and scales (float32 [rows]); enqueues only."""
     import torch
     rows, cols = w.shape
-    dt = DT_BF16 if w.dtype == torch.bfloat16 else DT_FP32 if w.dtype == torch.float32 else -1
-    _check(lib().fp8_head_quantize(rows, cols, _tensor(w, dt), _ptr(codes), _ptr(scales), _stream(stream)))
+    _check_buffer(codes, "codes", rows * cols)
+    _check_buffer(scales, "scales", rows * 4)
+    if scales.dtype != torch.float32:
+        raise ValueError(f"scales: dtype {scales.dtype}, expected torch.float32")
+    _check(lib().fp8_head_quantize(rows, cols, _tensor(w, -1, "w", rows * cols * w.element_size()), _ptr(codes),
+                                   _ptr(scales), _stream(stream)))

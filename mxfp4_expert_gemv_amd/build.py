@@ -4,7 +4,7 @@ import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(_HERE, "libmoe_decode.so")
-SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("moe_kernels.hip", "moe_persistent.hip", "moe_api.cpp", "head_kernels.hip", "head_api.cpp")]
+SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("moe_kernels.hip", "moe_api.cpp", "head_kernels.hip", "head_api.cpp")]
 
 
 def build(hipcc: str, flags: list) -> str:

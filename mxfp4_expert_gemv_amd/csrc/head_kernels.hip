@@ -154,9 +154,12 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
             __hip_atomic_store(a.pidx + (size_t)vt * T + t, idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // the last workgroup to arrive reduces the per-tile maxima.  No fence: the partials were written
-    // through to the device-coherent level, and vmcnt(0) waits for those stores to complete.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // the last workgroup to arrive reduces the per-tile maxima.  Ordering rests on the ISA, not on
+    // release/acquire (an L2 write-back in each of the 2,456 workgroups made the head ten times
+    // slower): the partials are agent-scope atomic stores, written through to the device-coherent
+    // level, vmcnt(0) waits for the memory's acknowledgement before the arrival, and the last
+    // workgroup reads them with agent-scope atomic loads, which do not hit in the non-coherent L2.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tid == 0)
         is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
@@ -231,8 +234,13 @@ __global__ __launch_bounds__(256) void quantize_rows(const void* __restrict__ w,
         if (c < NC) {
             uint32_t d[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                d[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[j][2 * q] / s, v[j][2 * q + 1] / s, 0, false) & 0xffffu;
+            for (int q = 0; q < 4; ++q) {
+                const float a = v[j][2 * q] / s, b = v[j][2 * q + 1] / s;
+                d[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+                // the hardware conversion writes 0xFF for every NaN; keep the NaN's sign (S.1111.111)
+                if (__builtin_isnan(a)) d[q] = (d[q] & 0xff00u) | ((__float_as_uint(a) >> 24) & 0x80u) | 0x7fu;
+                if (__builtin_isnan(b)) d[q] = (d[q] & 0x00ffu) | ((((__float_as_uint(b) >> 24) & 0x80u) | 0x7fu) << 8);
+            }
             ((uint2*)codes)[(size_t)row * NC + c] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
         }
     }

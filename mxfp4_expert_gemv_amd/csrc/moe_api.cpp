@@ -12,7 +12,6 @@
 
 #include "../../include/moe_decode.h"
 #include "moe_launch.h"
-#include "moe_persistent.h"
 
 
 using moe::Shape;
@@ -35,11 +34,6 @@ struct moe_decode_handle {
     moe_decode_config cfg;
     Shape sh;
     int device;
-    // three kernels per layer (default) or one persistent whole-stack kernel (MOE_F_PERSISTENT)
-    bool persistent;
-    int grid_n = 0, rmax = 0;
-    long long timeout_ticks = 0;
-    moe::pk::StackArgs pargs{};  // exchange buffers, control words, layer table (workspace pointers)
     // per layer: one allocation holding router, w13, w13_s, w2, w2_s (256-byte aligned pieces)
     std::vector<uint8_t*> layer_mem;
     std::vector<char> layer_set;
@@ -113,7 +107,7 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->inter % moe::kBlock || !moe::shape_supported(sh))
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
                     c->hidden, c->inter);
-    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_PERSISTENT))
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH))
         return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
@@ -187,14 +181,6 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     const uint64_t o_xn = o; o += align256((uint64_t)T * sh.H * 2);
     const uint64_t o_hq = o; o += align256((uint64_t)sh.pairs(T) * sh.I);
     const uint64_t o_hs = o; o += align256((uint64_t)sh.pairs(T) * 4);
-    // persistent kernel: exchange buffers, control words, per-layer pointer table
-    const uint64_t o_xw = o; o += align256(moe::pk::xw_bytes(sh));
-    const uint64_t o_lw = o; o += align256(moe::pk::lw_bytes(sh));
-    const uint64_t o_shw = o; o += align256(moe::pk::shw_bytes(sh));
-    const uint64_t o_hw = o; o += align256(moe::pk::hw_bytes(sh));
-    const uint64_t o_dw = o; o += align256(moe::pk::dw_bytes(sh));
-    const uint64_t o_ctl = o; o += moe::pk::kCtlBytes;
-    const uint64_t o_lt = o; o += align256((uint64_t)cfg->num_layers * sizeof(moe::LayerPtrs));
     h->ws_bytes = o;
     if (hipMalloc(&h->ws, o) != hipSuccess) {
         (void)hipGetLastError();
@@ -221,54 +207,6 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->xn = (uint16_t*)(h->ws + o_xn);
     h->hq = h->ws + o_hq;
     h->hs = (float*)(h->ws + o_hs);
-    h->persistent = (cfg->flags & MOE_F_PERSISTENT) != 0;
-    if (h->persistent) {
-        int cus = 0, clock_khz = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
-            hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess ||
-            cus <= 0 || clock_khz <= 0) {
-            free_handle(h);
-            return fail(MOE_ERR_HIP, "device attribute query failed");
-        }
-        h->grid_n = moe::pk::grid_size(sh, cus);
-        h->rmax = moe::pk::rows_max(sh, h->grid_n);
-        h->timeout_ticks = (long long)clock_khz * 200;  // 200 ms per wait
-        for (int t = 1; t <= cfg->max_tokens; ++t) {
-            int per_cu = 0;
-            if (moe::pk::check_resident(sh, t, h->grid_n, &per_cu) != hipSuccess || per_cu < 1) {
-                free_handle(h);
-                return fail(MOE_ERR_UNSUPPORTED, "persistent kernel (%d tokens) cannot be resident on every compute unit",
-                            t);
-            }
-        }
-        std::vector<moe::LayerPtrs> table(cfg->num_layers);
-        for (int l = 0; l < cfg->num_layers; ++l) {
-            uint8_t* m = h->layer_mem[l];
-            table[l] = moe::LayerPtrs{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s};
-        }
-        if (hipMemcpy(h->ws + o_lt, table.data(), table.size() * sizeof(moe::LayerPtrs), hipMemcpyHostToDevice) !=
-            hipSuccess) {
-            free_handle(h);
-            return fail(MOE_ERR_HIP, "layer table upload failed");
-        }
-        moe::pk::StackArgs& a = h->pargs;
-        a.layers = (const moe::LayerPtrs*)(h->ws + o_lt);
-        a.xw = (uint64_t*)(h->ws + o_xw);
-        a.lw = (uint64_t*)(h->ws + o_lw);
-        a.shw = (uint64_t*)(h->ws + o_shw);
-        a.hw = (uint64_t*)(h->ws + o_hw);
-        a.dw = (uint64_t*)(h->ws + o_dw);
-        a.ctl = (uint32_t*)(h->ws + o_ctl);
-        a.H = sh.H;
-        a.E = sh.E;
-        a.k = sh.k;
-        a.S = sh.S;
-        a.I = sh.I;
-        a.L = cfg->num_layers;
-        a.normalize = (cfg->flags & MOE_F_RMSNORM_INPUT) ? 1 : 0;
-        a.rmax = h->rmax;
-        a.timeout = h->timeout_ticks;
-    }
     *out = h;
     g_err[0] = 0;
     return MOE_OK;
@@ -295,24 +233,6 @@ extern "C" moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, 
     if ((s = check_tensor(d->w2_s, MOE_DT_E8M0, "w2_s")) != MOE_OK) return s;
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     uint8_t* m = h->layer_mem[layer];
-    if (h->persistent) {  // canonical layout: plain copies
-        const Shape& sh = h->sh;
-        const uint64_t nexp = (uint64_t)sh.E + sh.S;
-        const struct {
-            const void* src;
-            uint64_t off, bytes;
-        } parts[5] = {{d->router.ptr, 0, sh.router_bytes()},
-                      {d->w13.ptr, h->off_w13, nexp * sh.w13_bytes_per_expert()},
-                      {d->w13_s.ptr, h->off_w13s, nexp * sh.w13s_bytes_per_expert()},
-                      {d->w2.ptr, h->off_w2, nexp * sh.w2_bytes_per_expert()},
-                      {d->w2_s.ptr, h->off_w2s, nexp * sh.w2s_bytes_per_expert()}};
-        for (const auto& pt : parts) {
-            hipError_t e = hipMemcpyAsync(m + pt.off, pt.src, pt.bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
-            if (e != hipSuccess) return fail(MOE_ERR_HIP, "weight copy failed: %s", hipGetErrorString(e));
-        }
-        h->layer_set[layer] = 1;
-        return MOE_OK;
-    }
     hipError_t e = moe::launch_repack(h->sh, d->router.ptr, d->w13.ptr, d->w13_s.ptr, d->w2.ptr, d->w2_s.ptr, m,
                                       m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s,
                                       (hipStream_t)stream);
@@ -376,29 +296,6 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
     if (o.x_codes && (uintptr_t)o.x_codes % 8) return fail(MOE_ERR_INVALID_ARG, "x_codes not 8-byte aligned");
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     const bool timing = h->timing_runs < h->timing_max_runs;
-    if (h->persistent) {
-        moe::pk::StackArgs a = h->pargs;
-        const Shape& sh = h->sh;
-        a.x_in = (const uint16_t*)x;
-        a.x_out = (uint16_t*)o.x_out;
-        a.y = o.y;
-        a.ids_out = o.topk_ids;
-        a.w_out = o.topk_w;
-        a.trace = (uint16_t*)o.x_trace;
-        a.x_scale = o.x_scale;
-        a.x_codes = o.x_codes;
-        hipEvent_t* ev = timing ? &h->events[(size_t)h->timing_runs * L * 2 * MOE_TIMING_CLASSES] : nullptr;
-        if (ev && hipEventRecord(ev[0], (hipStream_t)stream) != hipSuccess)
-            return fail(MOE_ERR_HIP, "hipEventRecord failed");
-        hipError_t e = moe::pk::launch_stack(sh, T, h->grid_n, a, (hipStream_t)stream);
-        if (e != hipSuccess) return fail(MOE_ERR_HIP, "stack kernel launch failed: %s", hipGetErrorString(e));
-        if (ev) {
-            if (hipEventRecord(ev[1], (hipStream_t)stream) != hipSuccess)
-                return fail(MOE_ERR_HIP, "hipEventRecord failed");
-            ++h->timing_runs;
-        }
-        return MOE_OK;
-    }
     if (timing || (h->cfg.flags & MOE_F_DIRECT_LAUNCH)) {
         moe_status st = enqueue_run(h, x, T, o, (hipStream_t)stream, timing);
         if (st == MOE_OK && timing) ++h->timing_runs;
@@ -460,18 +357,6 @@ extern "C" moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_ti
     out->struct_size = ss;
     out->runs = h->timing_runs;
     const int L = h->cfg.num_layers;
-    if (h->persistent) {  // one kernel per run: class 0 holds the whole-pass kernel
-        for (int r = 0; r < h->timing_runs; ++r) {
-            hipEvent_t* ev = &h->events[(size_t)r * L * 2 * MOE_TIMING_CLASSES];
-            float ms = 0.0f;
-            if (hipEventSynchronize(ev[1]) != hipSuccess || hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess)
-                return fail(MOE_ERR_HIP, "event timing failed");
-            out->total_ms[0] += ms;
-            out->launches[0] += 1;
-        }
-        h->timing_runs = 0;
-        return MOE_OK;
-    }
     for (int r = 0; r < h->timing_runs; ++r) {
         for (int l = 0; l < L; ++l) {
             hipEvent_t* ev = &h->events[((size_t)r * L + l) * 2 * MOE_TIMING_CLASSES];
@@ -496,11 +381,7 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
         return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
     const Shape& sh = h->sh;
     memset(info->variant, 0, sizeof info->variant);
-    if (h->persistent)
-        snprintf(info->variant, sizeof info->variant, "gfx950-persistent-n%d-dn%dx%d", h->grid_n, sh.ksub(),
-                 sh.iters());
-    else
-        snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s", sh.gw(), sh.bpl(), sh.ksub(),
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s", sh.gw(), sh.bpl(), sh.ksub(),
                  sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph");
     info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
     info->workspace_bytes = h->ws_bytes;
@@ -516,16 +397,8 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
 extern "C" moe_status moe_decode_check(moe_decode_handle* h) {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
-    if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "hipDeviceSynchronize failed");
-    if (!h->persistent) return MOE_OK;
-    uint32_t ctl[8];
-    if (hipMemcpy(ctl, h->pargs.ctl, sizeof ctl, hipMemcpyDeviceToHost) != hipSuccess)
-        return fail(MOE_ERR_HIP, "control word read failed");
-    static const char* rounds[] = {"?", "layer input", "router logits", "shared-expert h", "routed h",
-                                   "routed down outputs", "end of pass"};
-    if (ctl[2] != 0u)
-        return fail(MOE_ERR_HIP, "a pass was aborted: wait for %s timed out (layer %u, workgroup %u)",
-                    ctl[3] < 7 ? rounds[ctl[3]] : "?", ctl[4], ctl[5]);
+    const hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "device synchronisation failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 

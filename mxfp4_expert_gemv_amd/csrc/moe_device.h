@@ -24,12 +24,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// E8M0 byte -> fp32 2^(b-127) by placing b in the fp32 exponent field (exact for 1 <= b <= 254).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __uint_as_float((b & 0xffu) << 23); }
+// E8M0 byte -> fp32 2^(b-127) (OCP MX): b in the fp32 exponent field for 1 <= b <= 254; b = 0 is
+// 2^-127, the fp32 subnormal 0x00400000; b = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    b &= 0xffu;
+    const uint32_t u = b == 0u ? 0x00400000u : b == 255u ? 0x7fc00000u : b << 23;
+    return __uint_as_float(u);
+}
 
-// Two fp32 values -> two OCP E4M3 codes (round to nearest even) in the low 16 bits.
+// E4M3 NaN code with the sign of the fp32 NaN v: S.1111.111 (the hardware conversion writes 0xFF
+// for every NaN).
+__device__ __forceinline__ uint32_t e4m3_nan(float v) { return ((__float_as_uint(v) >> 24) & 0x80u) | 0x7fu; }
+
+// Two fp32 values -> two OCP E4M3 codes (round to nearest even, saturating to +-448) in the low 16
+// bits; a NaN keeps its sign.
 __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    if (__builtin_isnan(a)) c = (c & 0xff00u) | e4m3_nan(a);
+    if (__builtin_isnan(b)) c = (c & 0x00ffu) | (e4m3_nan(b) << 8);
+    return c;
 }
 
 // Two E4M3 codes (low 16 bits) -> their exact f16 values.

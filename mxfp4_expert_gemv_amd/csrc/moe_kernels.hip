@@ -851,8 +851,12 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
     }
     if constexpr (CENTRAL) {
         // 3-4 tokens: the last router workgroup to arrive takes the top-k of every token (the gate/up
-        // workgroups would otherwise each redo it for all tokens)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's logit stores have completed
+        // workgroups would otherwise each redo it for all tokens).  Ordering rests on the ISA, not on
+        // release/acquire (whose L2 write-back in every workgroup costs microseconds): the logits are
+        // agent-scope atomic stores, written through to the device-coherent level; vmcnt(0) waits
+        // until the memory has acknowledged them, before the barrier and the arrival; the last
+        // workgroup reads them with agent-scope atomic loads, which do not hit in the non-coherent L2.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         if (tid == 0)
             is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==

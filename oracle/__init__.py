@@ -33,6 +33,11 @@ PINS = {
     "head": "argmax brute force; duplicate-row tie; BLAS GEMV special case",
     "mtp_accept": "hand cases: all, none, first-mismatch positions, a match after a mismatch is not accepted",
     "head_bf16": "BLAS GEMV special case; equals the FP8 head exactly on rows that are E4M3 values times a power of two",
+    "route.bounds": "fp32 sums in natural, reversed, pairwise, permuted and the router kernel's order stay within it; "
+                    "an adversarial half-ulp sum reaches at least half of it (a 16x looser bound is caught)",
+    "head.bounds": "the same soundness and tightness checks for the FP8 and BF16 heads",
+    "topk_margin_ok": "hand cases: a gap equal to the bound sum fails, a failing pair at rank 3 and at rank k fails",
+    "argmax_margin_ok": "hand cases: a gap equal to the bound sum fails, a tie fails",
 }
 
 

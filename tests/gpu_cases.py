@@ -64,20 +64,9 @@ class DeviceLayer:
         return {e: synth.expert(self.shape, self.seed, self.layer, e) for e in used}
 
 
-# kernel variants of the library: three kernels per layer (default) and the persistent whole-pass
-# kernel; the parity tests run on both
-VARIANTS = {"persistent": moe.F_PERSISTENT, "three_kernels": 0}
-DEFAULT_VARIANT = "three_kernels"
-_variant = {"flags": 0}
-
-
-def set_variant(name: str):
-    _variant["flags"] = VARIANTS[name]
-
-
 def create(shape: synth.Shape, max_tokens: int = 4, num_layers: int = 1, flags: int = 0):
     return moe.moe_decode_create(shape.hidden, shape.num_experts, shape.top_k, shape.num_shared, shape.inter,
-                                 max_tokens, num_layers, flags | _variant["flags"])
+                                 max_tokens, num_layers, flags)
 
 
 def run_layer(handle, shape: synth.Shape, x_host: np.ndarray, num_layers: int = 1) -> dict:
@@ -95,7 +84,7 @@ def run_layer(handle, shape: synth.Shape, x_host: np.ndarray, num_layers: int = 
            "x_codes": torch.empty((num_layers, T, H), dtype=torch.uint8, device=dev())}
     moe.moe_decode_run(handle, x, T, **out)
     torch.cuda.synchronize()
-    moe.moe_decode_check(handle)  # raises if a wait of the persistent kernel expired
+    moe.moe_decode_check(handle)  # raises on an asynchronous device error
     res = {n: t.cpu().numpy() for n, t in out.items() if t.dtype != torch.bfloat16}
     res["x_out"] = bf16_bits(out["x_out"])
     res["x_trace"] = bf16_bits(out["x_trace"])

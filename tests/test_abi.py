@@ -103,3 +103,31 @@ def test_head_quantize_arguments_checked_before_device():
 def test_head_verify_arguments():
     L = moe.lib()
     assert L.fp8_head_verify(None, None, 4, None, None, None, None) == -1
+
+
+def test_binding_tags_tensors_from_their_own_dtype():
+    """The binding derives each tag from the tensor's dtype (raw bytes take the slot's byte format),
+    so a float32 or bf16 tensor cannot be passed off as FP8 or MXFP4 bytes."""
+    import torch
+    t = lambda dt: torch.zeros(4, dtype=dt)  # noqa: E731
+    assert moe._dtype_tag(t(torch.bfloat16), moe.DT_E2M1X2) == moe.DT_BF16
+    assert moe._dtype_tag(t(torch.float32), moe.DT_BF16) == moe.DT_FP32
+    assert moe._dtype_tag(t(torch.uint8), moe.DT_E8M0) == moe.DT_E8M0
+    assert moe._dtype_tag(t(torch.uint8), moe.DT_E4M3) == moe.DT_E4M3
+    assert moe._dtype_tag(t(torch.float8_e4m3fn), moe.DT_E2M1X2) == moe.DT_E4M3
+    assert moe._dtype_tag(t(torch.int32), moe.DT_BF16) == -1
+    # bf16 weights offered to the FP8 head: the library refuses the tag before any device call
+    w = torch.zeros((64, 256), dtype=torch.bfloat16)
+    s = torch.ones(64, dtype=torch.float32)
+    h = ctypes.c_void_p()
+    st = moe.lib().fp8_head_create(64, 256, moe._tensor(w, moe.DT_E4M3), moe._tensor(s, moe.DT_FP32), None,
+                                   ctypes.byref(h))
+    assert st == -3
+    # a float32 router offered where bf16 belongs is tagged FP32 (the set-layer tag check refuses it)
+    assert moe._tensor(torch.zeros((16, 256), dtype=torch.float32), moe.DT_BF16).dtype == moe.DT_FP32
+
+
+def test_binding_refuses_host_and_missized_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        moe._tensor(torch.zeros(16, dtype=torch.uint8), moe.DT_E8M0, "w", 16)  # host memory

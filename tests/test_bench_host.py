@@ -29,8 +29,6 @@ def test_kernel_names_follow_the_variant_string():
     assert n == {"router": "void moe::k1_router<1, 8>(moe::K1Args)",
                  "gateup": "void moe::k2_gateup<1, 8, 4>(moe::K2Args)",
                  "down": "void moe::k3_down<8, 3, 1, 1>(moe::K3Args)"}
-    p = bench.kernel_names("gfx950-persistent-n256-dn8x3", 4)
-    assert p == {"stack": "void moe::pk::stack_kernel<4, 8, 3>(moe::pk::StackArgs)"}
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):

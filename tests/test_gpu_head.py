@@ -191,7 +191,7 @@ def test_full_bf16_head_argmax():
     assert (np.abs(lg[:, rows] - lg_o[:, rows]) <= bd_o[:, rows]).all()
 
 
-@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("T", [2, 3, 4])
 def test_verify_accepts_longest_matching_prefix(T):
     """Greedy acceptance fused after the argmax: drafts built from the oracle's target tokens so that
     every accept count 0 .. T-1 occurs, plus a draft that matches only after a mismatch."""
@@ -220,3 +220,73 @@ def test_verify_accepts_longest_matching_prefix(T):
         assert am.cpu().numpy().tolist() == am_o.tolist()
         assert int(acc.item()) == oracle.mtp_accept(am_o, d), (d, am_o.tolist())
     moe.fp8_head_destroy(h)
+
+
+def _e4m3_boundaries():
+    """For each positive E4M3 code c = 1 .. 126, the smallest positive fp32 bit pattern that the
+    oracle encodes to c or above (bisection over bit patterns; the oracle's encoder is monotonic,
+    which its exhaustive CPU pin establishes).  The oracle's code of any |v| <= 448 is then the number
+    of boundaries at or below |v|'s bit pattern."""
+    codes = np.arange(1, 127)
+    lo = np.zeros(codes.size, dtype=np.int64)             # encodes below c
+    hi = np.full(codes.size, 0x43E00000, dtype=np.int64)  # 448.0 encodes to 126 >= c
+    while (hi - lo > 1).any():
+        mid = (lo + hi) // 2
+        enc = oracle.e4m3_encode(mid.astype(np.uint32).view(np.float32)).astype(np.int64)
+        up = enc >= codes
+        hi = np.where(up, mid, hi)
+        lo = np.where(up, lo, mid)
+    return hi
+
+
+def test_device_e4m3_conversion_exhaustive_sweep():
+    """Every fp32 bit pattern with |v| <= 448 (both signs), and NaNs, through the device's FP8
+    conversion as the kernels use it (codes = RNE-satfinite(fl32(v / s)); each row holds 448, so its
+    scale s is exactly 1 and fl32(v / s) = v), against the oracle's encoding.  Stops at the first
+    mismatch.  Rows whose maximum exceeds 448 then check the saturation of quotients just above 448."""
+    H = 2560
+    bounds = torch.from_numpy(_e4m3_boundaries().astype(np.int32)).to(dev())
+    top = 0x43E00000  # 448.0
+    rows = 16384
+    per = rows * (H - 1)
+    codes = torch.empty((rows, H), dtype=torch.uint8, device=dev())
+    scales = torch.empty((rows,), dtype=torch.float32, device=dev())
+    checked = 0
+    for sign in (0, 1):
+        for p0 in range(0, top + 1, per):
+            n = min(per, top + 1 - p0)
+            nr = (n + H - 2) // (H - 1)
+            bits = torch.arange(p0, p0 + nr * (H - 1), dtype=torch.int64, device=dev())
+            bits = torch.clamp(bits, max=top).to(torch.int32)  # the tail of the last row repeats 448
+            vals = torch.empty((nr, H), dtype=torch.int32, device=dev())
+            vals[:, 0] = top
+            vals[:, 1:] = bits.view(nr, H - 1)
+            v = vals.view(torch.float32)
+            if sign:
+                v = -v
+            moe.fp8_head_quantize(v, codes[:nr], scales[:nr])
+            want = torch.searchsorted(bounds, bits, right=True, out_int32=True).to(torch.uint8) | (0x80 * sign)
+            got = codes[:nr, 1:].reshape(-1)
+            assert bool((scales[:nr] == 1.0).all()), "a row's scale is not exactly 1"
+            bad = torch.nonzero(got != want)
+            if bad.numel():
+                i = int(bad[0])
+                f = float(np.array([int(bits[i])], dtype=np.int32).view(np.float32)[0]) * (-1 if sign else 1)
+                raise AssertionError(f"{bad.numel()} codes differ; first v = {f!r}: device {int(got[i]):#04x}, "
+                                     f"oracle {int(want[i]):#04x}")
+            checked += n
+            del vals, v, bits, want
+    assert checked == 2 * (top + 1)
+    # NaNs (quiet, signalling, both signs) and quotients just above 448
+    nan_bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF812345, 0x7FFFFFFF], dtype=np.uint32)
+    W = np.zeros((4, H), dtype=np.float32)
+    W[0, 0] = 448.0
+    W[0, 1:6] = nan_bits.view(np.float32)
+    for r, amax in ((1, 448.01), (2, 455.0), (3, 464.0)):
+        W[r, 0] = amax
+        W[r, 1:64] = amax * (1 - np.arange(63, dtype=np.float32) * 2.0 ** -20)
+        W[r, 64:128] = -W[r, 1:65]
+    c, s = _gpu_quantize(torch.from_numpy(W).to(dev()))
+    Wq_o, s_o = oracle.head_quantize(W)
+    assert (s.view(np.uint32) == s_o.view(np.uint32)).all()
+    assert (c == Wq_o).all(), np.argwhere(c != Wq_o)[:8]

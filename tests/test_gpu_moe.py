@@ -11,21 +11,17 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import (DEFAULT_VARIANT, MANIFEST, VARIANTS, DeviceLayer, check_layer, create, margin_attempt, normwise_err,
-                       run_layer, set_variant, to_dev_u16)
+from gpu_cases import (MANIFEST, DeviceLayer, check_layer, create, margin_attempt, normwise_err, run_layer,
+                       to_dev_u16)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module", autouse=True, params=sorted(VARIANTS))
-def variant(request):
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     torch.cuda.init()
-    print(f"variant {request.param}", flush=True)
-    set_variant(request.param)
-    yield request.param
-    set_variant(DEFAULT_VARIANT)
 
 
 def _layer_case(shape, seed, x, layer_obj=None, handle=None):
@@ -94,7 +90,7 @@ def test_zero_input_gives_zero_output():
 
 
 @pytest.fixture(scope="module")
-def flash_t1(variant):
+def flash_t1():
     m = MANIFEST["layer_t1"]
     shape = synth.FLASH
     lay = DeviceLayer(shape, m["seed"])
@@ -180,8 +176,86 @@ def test_run_before_set_is_a_state_error():
     moe.moe_decode_destroy(h)
 
 
-def test_query_reports_variant_and_bytes(flash_t1, variant):
+def test_query_reports_variant_and_bytes(flash_t1):
     shape, lay, h, m = flash_t1
     info = moe.moe_decode_query(h)
-    assert info["variant"].startswith("gfx950-persistent" if variant == "persistent" else "gfx950-3k")
+    assert info["variant"].startswith("gfx950-3k")
     assert info["bytes_per_layer_t1"] == 30_822_400
+
+
+def _extreme_scales(w13, w13_s, w2, w2_s, I, xp):
+    """Crafted E8M0 bytes on every expert (xp: numpy or torch; arrays [experts][rows][...] or one
+    expert's [rows][...] when given 3-D / 2-D views).  Down rows 0-7: scale byte 0 (2^-127, an fp32
+    subnormal); rows 8-15: byte 1 (2^-126); rows 16-23: byte 127 (1.0); rows 24-31: byte 254 (2^127) on
+    all-zero codes, so a decode of 254 to anything but a finite value would turn 0 into NaN; row 32,
+    block 0: byte 255 (NaN).  Gate rows 4-7: byte 254 on all-zero codes; gate rows 0-1, first four
+    blocks: byte 0."""
+    w2_s[..., 0:8, :] = 0
+    w2_s[..., 8:16, :] = 1
+    w2_s[..., 16:24, :] = 127
+    w2_s[..., 24:32, :] = 254
+    w2[..., 24:32, :] = 0
+    w2_s[..., 32, 0] = 255
+    w13_s[..., 4:8, :] = 254
+    w13[..., 4:8, :] = 0
+    w13_s[..., 0:2, 0:4] = 0
+
+
+@pytest.mark.parametrize("shape", [synth.Shape(256, 16, 1, 0, 64), synth.Shape(256, 16, 2, 1, 64)],
+                         ids=["k1_no_shared", "k2_shared"])
+def test_e8m0_extreme_scale_bytes(shape):
+    """E8M0 bytes 0 (2^-127), 1, 127, 254 (2^127) and 255 (NaN) decode as OCP MX defines them:
+    NaN reaches exactly the outputs it reaches in the oracle, the subnormal scale is not flushed
+    (rows whose every block has byte 0 or 1 match the oracle to 2e-3 of their own magnitude) and
+    byte 254 on zero codes contributes 0, not NaN."""
+    lay = DeviceLayer(shape, 41)
+    _extreme_scales(lay.w13, lay.w13_s, lay.w2, lay.w2_s, shape.inter, torch)
+    torch.cuda.synchronize()
+    h = create(shape)
+    lay.set_into(h, 0)
+    a, x = margin_attempt(shape, lay.router_host, 41, 2)
+    gpu = run_layer(h, shape, x)
+    moe.moe_decode_destroy(h)
+    ro = oracle.route(shape, lay.router_host, x)
+    experts = lay.oracle_experts(ro["ids"])
+    for e in experts.values():
+        _extreme_scales(e["w13"], e["w13_s"], e["w2"], e["w2_s"], shape.inter, np)
+    ref_y, ref_tr = oracle.moe_layer(shape, lay.router_host, experts, x)
+    assert (gpu["topk_ids"][0] == ref_tr["ids"]).all()
+    assert (np.isnan(gpu["y"]) == np.isnan(ref_y)).all(), np.argwhere(np.isnan(gpu["y"]) != np.isnan(ref_y))[:8]
+    assert np.isnan(ref_y[:, 32]).all() and not np.isnan(np.delete(ref_y, 32, axis=1)).any()
+    for rows in (slice(0, 8), slice(8, 16), slice(16, 24)):
+        g, r = gpu["y"][:, rows].astype(np.float64), ref_y[:, rows].astype(np.float64)
+        mag = np.abs(r).max(axis=1, keepdims=True)
+        assert (mag > 0).all() and (np.abs(g - r) <= Y_TOL_ROWS * mag).all(), (rows, g, r)
+    assert (ref_y[:, 24:32] == ref_y[:, 24:32]).all()  # finite
+    ok = ~np.isnan(ref_y)
+    err = np.abs(gpu["y"][ok] - ref_y[ok]).max() / np.abs(ref_y[ok]).max()
+    assert err <= 2e-3
+
+
+Y_TOL_ROWS = 2e-3
+
+
+def test_binding_derives_dtype_tags_from_tensors(flash_t1):
+    """A float32 router with the right byte count, and E4M3 codes handed over as bf16, are refused by
+    the library's tag check (the binding tags each tensor from its own dtype); a tensor of the wrong
+    size is refused by the binding before any device work."""
+    shape, lay, h, m = flash_t1
+    f32_router = lay.router.view(torch.float32)  # same bytes, float32 dtype
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_decode_set_layer(h, 0, f32_router, lay.w13, lay.w13_s, lay.w2, lay.w2_s)
+    assert ei.value.status == -3
+    with pytest.raises(ValueError):
+        moe.moe_decode_set_layer(h, 0, lay.router[:-1], lay.w13, lay.w13_s, lay.w2, lay.w2_s)
+    # E4M3 head weights handed over as bf16 values: refused (tag BF16 in an E4M3 slot, or a size
+    # that is not one byte per weight)
+    w_bf16 = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    scales = torch.ones((64,), dtype=torch.float32, device="cuda")
+    with pytest.raises((moe.MoeError, ValueError)):
+        moe.fp8_head_create(w_bf16, scales)
+    # the same bytes presented as one byte per weight but tagged from the bf16 tensor they came from
+    w_bytes = torch.zeros((64, 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.fp8_head_create((w_bytes, moe._dtype_tag(w_bf16, moe.DT_E4M3)), scales)
+    assert ei.value.status == -3

@@ -1,7 +1,9 @@
 """GPU parity of the full-size 42-layer MoE decode stack (hidden 2560, 512 experts, top-8 + 1
-shared, width 768, ~67.6 GB of resident MXFP4 experts), at 1 and 4 tokens, teacher-forced: for
-sampled layers the oracle recomputes the layer from the GPU's own input residual x_l (traced by the
-library) and checks ids, FP8 activation codes, and the layer's effect on the residual.
+shared, width 768, ~67.6 GB of resident MXFP4 experts), at 1 and 4 tokens, teacher-forced on every
+layer: the oracle recomputes each layer from the GPU's own input residual x_l (traced by the
+library) and checks the ids (exact wherever the routing is well posed), the FP8 activation scale
+and codes (exact), and the layer's effect on the residual (x_(l+1) within half a bf16 ulp of
+x_l + y, with y within the normwise tolerance of the oracle's).
 """
 import numpy as np
 import pytest
@@ -10,19 +12,18 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import DEFAULT_VARIANT, MANIFEST, VARIANTS, DeviceLayer, Y_TOL, create, normwise_err, run_layer, set_variant
+from gpu_cases import MANIFEST, DeviceLayer, Y_TOL, create, normwise_err, run_layer
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = (0, 1, 2, 21, 40, 41)
+# at least this many of the 42 layers must have a well-posed routing for the ids to count as checked
+MIN_WELL_POSED = 36
 
 
-@pytest.fixture(scope="module", params=sorted(VARIANTS))
-def stack(request):
+@pytest.fixture(scope="module")
+def stack():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    print(f"variant {request.param}", flush=True)
-    set_variant(request.param)
     st = MANIFEST["stack"]
     shape, L = synth.FLASH, st["layers"]
     h = create(shape, max_tokens=4, num_layers=L, flags=moe.F_RMSNORM_INPUT)
@@ -33,7 +34,6 @@ def stack(request):
         torch.cuda.synchronize()
         layers.append((lay.router_host, st["seed"], l))
         del lay
-    set_variant(DEFAULT_VARIANT)
     yield shape, h, layers, st
     moe.moe_decode_destroy(h)
 
@@ -45,15 +45,16 @@ def _ulp_bf16(v):
 
 
 @pytest.mark.parametrize("T", [1, 4])
-def test_stack_teacher_forced(stack, T):
+def test_stack_teacher_forced_every_layer(stack, T):
     shape, h, layers, st = stack
     L = len(layers)
     x0 = synth.tokens(shape.hidden, st["seed"], 4, st["x_attempt"])[:T]
     gpu = run_layer(h, shape, x0, num_layers=L)
     assert (gpu["x_trace"][0] == x0).all()
     diverged = [l for l in range(L) if gpu["topk_ids"][l].tolist() != st["ids_t4"][l][:T]]
-    print(f"T={T}: layers whose ids differ from the oracle's own trajectory: {diverged}")
-    for l in SAMPLE:
+    print(f"T={T}: layers whose ids differ from the oracle's own free-running trajectory: {diverged}", flush=True)
+    not_posed, worst = [], 0.0
+    for l in range(L):
         router_host, seed, _ = layers[l]
         x_l = gpu["x_trace"][l]
         xin = oracle.rmsnorm_bf16(x_l)
@@ -62,20 +63,28 @@ def test_stack_teacher_forced(stack, T):
         experts = {e: synth.expert(shape, seed, l, e) for e in sorted(set(ro["ids"].reshape(-1).tolist())) + [512]}
         y_o, tr = oracle.moe_layer(shape, router_host, experts, xin)
         if well_posed:
-            assert (gpu["topk_ids"][l] == tr["ids"]).all(), l
-        assert np.abs(gpu["topk_w"][l] - tr["w"]).max() <= 1e-5
+            assert (gpu["topk_ids"][l] == tr["ids"]).all(), f"layer {l}: ids {gpu['topk_ids'][l].tolist()} vs {tr['ids'].tolist()}"
+            assert np.abs(gpu["topk_w"][l] - tr["w"]).max() <= 1e-5, l
+        else:
+            not_posed.append(l)
         assert (gpu["x_scale"][l] == tr["sx"]).all(), l
         assert (gpu["x_codes"][l] == tr["qx"]).all(), l
         if l < L - 1:
-            # x_{l+1} = bf16(x_l + y): within half a bf16 ulp of x_l + y_gpu, y_gpu within Y_TOL of y_ref
+            # x_(l+1) = bf16(x_l + y): within half a bf16 ulp of x_l + y_gpu, y_gpu within Y_TOL of y_ref
             x_next = oracle.bf16_decode(gpu["x_trace"][l + 1]).astype(np.float64)
             exact = oracle.bf16_decode(x_l).astype(np.float64) + y_o.astype(np.float64)
-            slack = 0.5 * _ulp_bf16(x_next) * (1 + 2.0 ** -7) + Y_TOL * np.abs(y_o).max(axis=1, keepdims=True)
+            scale = np.abs(y_o).max(axis=1, keepdims=True)
+            slack = 0.5 * _ulp_bf16(x_next) * (1 + 2.0 ** -7) + Y_TOL * scale
             assert (np.abs(x_next - exact) <= slack).all(), l
+            excess = np.maximum(np.abs(x_next - exact) - 0.5 * _ulp_bf16(x_next) * (1 + 2.0 ** -7), 0) / scale
+            worst = max(worst, float(excess.max()))
         else:
             err = normwise_err(gpu["y"], y_o)
-            print(f"T={T}: last-layer normwise y error {err}")
+            print(f"T={T}: last-layer normwise y error {err}", flush=True)
             assert (err <= Y_TOL).all()
             x_out = oracle.bf16_decode(gpu["x_out"]).astype(np.float64)
             exact = oracle.bf16_decode(x_l).astype(np.float64) + gpu["y"].astype(np.float64)
             assert (np.abs(x_out - exact) <= 0.5 * _ulp_bf16(x_out) * (1 + 2.0 ** -7)).all()
+    print(f"T={T}: ids checked on {L - len(not_posed)} of {L} layers; not well posed: {not_posed}; "
+          f"largest residual deviation beyond rounding, relative to max|y|: {worst:.2e}", flush=True)
+    assert L - len(not_posed) >= MIN_WELL_POSED, f"only {L - len(not_posed)} well-posed layers: {not_posed}"

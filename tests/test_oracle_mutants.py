@@ -41,6 +41,12 @@ MUTANTS = {
     "residual_sign": ("oracle_bf16_decode(x[i]) + y[i]", "oracle_bf16_decode(x[i]) - y[i]"),
     "head_scale_dropped": ("double lg = (double)scale[r] * acc;", "double lg = acc;"),
     "head_ties_high_index": ("if (lg > bestv) { bestv = lg; best = r; }", "if (lg >= bestv) { bestv = lg; best = r; }"),
+    "router_bound_gamma_x16": ("if (bounds) bounds[e] = gamma * mag;", "if (bounds) bounds[e] = 16.0 * gamma * mag;"),
+    "head_bound_gamma_x16": ("(double)scale[r] * gamma * mag + 0x1p-24 * fabs(lg);",
+                             "(double)scale[r] * 16.0 * gamma * mag + 0x1p-24 * fabs(lg);"),
+    "bf16_head_bound_gamma_x16": ("if (bounds) bounds[(size_t)t * V + r] = gamma * mag;",
+                                  "if (bounds) bounds[(size_t)t * V + r] = 16.0 * gamma * mag;"),
+    "router_bound_dropped": ("if (bounds) bounds[e] = gamma * mag;", "if (bounds) bounds[e] = 0.0;"),
 }
 
 
@@ -111,8 +117,15 @@ def _checks():
         _, _, am2 = oracle.head_logits(Wq2, s2, x, want_logits=False, want_bounds=False)
         assert am2[0] == am[0]
 
+    def bounds():
+        import test_oracle_bounds as tb
+        tb.test_router_bounds_hold_for_every_summation_order(0)
+        tb.test_router_bound_is_tight_on_an_adversarial_sum()
+        tb.test_head_bound_is_tight_on_an_adversarial_sum()
+        tb.test_bf16_head_bounds_hold_and_are_tight()
+
     for name, fn in (("codecs", codecs), ("layer", layer), ("zero_input", zero_input), ("stack", stack),
-                     ("head", head)):
+                     ("head", head), ("bounds", bounds)):
         run(name, fn)
     return failed
 
