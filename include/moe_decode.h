@@ -184,6 +184,20 @@ moe_status fp8_head_destroy(fp8_head_handle* h);
 moe_status fp8_head_verify(fp8_head_handle* h, const void* x, int32_t num_tokens, const int32_t* draft,
                            int32_t* argmax, int32_t* accept, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the computation of fp8_head_run on the caller's own row-major
+ * weights, with no handle.  w: E4M3 [vocab][hidden] row-major (16-byte aligned); row_scale: FP32
+ * [vocab]; x, logits (nullable), argmax and num_tokens as in fp8_head_run.  Allocates nothing: the
+ * argmax reduction's scratch (an arrival counter and per-tile maxima, 131,328 bytes) is one fixed
+ * device array per GPU, held until the process ends; every call on a GPU uses that GPU's copy, so
+ * calls that overlap on one GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The last workgroup of each call resets the counter to zero.  vocab above
+ * MOE_NOALLOC_MAX_VOCAB returns MOE_ERR_INVALID_ARG; other errors as fp8_head_run.  Only enqueues
+ * work on `stream`. */
+#define MOE_NOALLOC_MAX_VOCAB 262144
+moe_status fp8_head_run_noalloc(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale, const void* x,
+                                int32_t num_tokens, float* logits, int32_t* argmax, void* stream);
+
 /* Per-row FP8 quantisation of an LM-head weight matrix at load time, the step that makes the FP8
  * head (tanhow.com, section "三项优化是什么", item 2: the head is kept in FP8 instead of BF16 so that
  * each decode step reads half the bytes; devotd.net, "dgx-spark-moe-inference-optimizations",

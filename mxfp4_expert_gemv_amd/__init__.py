@@ -24,7 +24,8 @@ F_DIRECT_LAUNCH = 0x2
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
            "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize", "bf16_head_create", "fp8_head_verify",
-           "moe_status_string", "moe_last_error")
+           "fp8_head_run_noalloc", "moe_status_string", "moe_last_error")
+NOALLOC_MAX_VOCAB = 262144
 
 
 class MoeError(RuntimeError):
@@ -94,6 +95,7 @@ def lib():
             "fp8_head_quantize": [i32, i32, Tensor, vp, vp, vp],
             "bf16_head_create": [i32, i32, Tensor, vp, ctypes.POINTER(vp)],
             "fp8_head_verify": [vp, vp, i32, vp, vp, vp, vp],
+            "fp8_head_run_noalloc": [i32, i32, Tensor, Tensor, vp, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -303,6 +305,24 @@ def fp8_head_verify(handle, x, draft, argmax, accept, stream=None) -> None:
                                   (argmax, "argmax", torch.int32, lambda z: T * 4),
                                   (accept, "accept", torch.int32, lambda z: 4)))
     _check(lib().fp8_head_verify(handle, _ptr(x), T, _ptr(draft), _ptr(argmax), _ptr(accept), _stream(stream)))
+
+
+def fp8_head_run_noalloc(w, row_scale, x, argmax, logits=None, num_tokens: int | None = None, stream=None) -> None:
+    """The FP8 head on the caller's row-major E4M3 weights w [V][H] (uint8 or float8_e4m3fn) and row
+    scales [V] (float32), without a handle and without any device allocation; enqueues only."""
+    import torch
+    vocab, hidden = w.shape
+    T = x.shape[0] if num_tokens is None else num_tokens
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.numel() < T * hidden:
+        raise ValueError(f"x: needs a contiguous bfloat16 GPU tensor of {T} x {hidden}")
+    for t, name, dt, nbytes in ((argmax, "argmax", torch.int32, T * 4), (logits, "logits", torch.float32, T * vocab * 4)):
+        if t is not None:
+            if t.dtype != dt:
+                raise ValueError(f"{name}: dtype {t.dtype}, expected {dt}")
+            _check_buffer(t, name, nbytes)
+    _check(lib().fp8_head_run_noalloc(vocab, hidden, _tensor(w, DT_E4M3, "w", vocab * hidden),
+                                      _tensor(row_scale, DT_FP32, "row_scale", vocab * 4), _ptr(x), T, _ptr(logits),
+                                      _ptr(argmax), _stream(stream)))
 
 
 def fp8_head_destroy(handle) -> None:

@@ -14,6 +14,9 @@ hipError_t launch_quantize_rows(const void* w, bool bf16, int V, int H, void* co
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
                        float* pval, int32_t* pidx, unsigned* ticket, const int32_t* draft, int32_t* accept, int V,
                        int H, bool fp8, hipStream_t stream);
+hipError_t noalloc_scratch(void** out);
+hipError_t launch_head_rowmajor(const void* w, const float* scale, const uint16_t* x, int T, float* logits,
+                                int32_t* argmax, void* scratch_dev, int V, int H, hipStream_t stream);
 }
 
 struct fp8_head_handle {
@@ -142,6 +145,37 @@ extern "C" moe_status fp8_head_quantize(int32_t rows, int32_t cols, moe_tensor w
     hipError_t e = head::launch_quantize_rows(w.ptr, w.dtype == MOE_DT_BF16, rows, cols, codes, scales,
                                               (hipStream_t)stream);
     if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head quantisation launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" moe_status fp8_head_run_noalloc(int32_t vocab, int32_t hidden, moe_tensor w, moe_tensor row_scale,
+                                           const void* x, int32_t T, float* logits, int32_t* argmax, void* stream) {
+    if (vocab <= 0 || hidden <= 0) return moe_fail(MOE_ERR_INVALID_ARG, "vocab and hidden must be positive");
+    if (vocab > MOE_NOALLOC_MAX_VOCAB)
+        return moe_fail(MOE_ERR_INVALID_ARG, "vocab %d exceeds the no-allocation limit of %d rows", vocab,
+                        MOE_NOALLOC_MAX_VOCAB);
+    if (hidden % 256 || hidden > 2560)
+        return moe_fail(MOE_ERR_UNSUPPORTED, "hidden %d (multiple of 256 up to 2560 supported)", hidden);
+    if (!w.ptr || (uintptr_t)w.ptr % 16) return moe_fail(MOE_ERR_INVALID_ARG, "w is NULL or not 16-byte aligned");
+    if (!row_scale.ptr || (uintptr_t)row_scale.ptr % 4)
+        return moe_fail(MOE_ERR_INVALID_ARG, "row_scale is NULL or not 4-byte aligned");
+    if (w.dtype != MOE_DT_E4M3) return moe_fail(MOE_ERR_DTYPE, "w: dtype tag %d, expected E4M3 (%d)", w.dtype, MOE_DT_E4M3);
+    if (row_scale.dtype != MOE_DT_FP32)
+        return moe_fail(MOE_ERR_DTYPE, "row_scale: dtype tag %d, expected FP32 (%d)", row_scale.dtype, MOE_DT_FP32);
+    if (!x || (uintptr_t)x % 16) return moe_fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+    if (!argmax) return moe_fail(MOE_ERR_INVALID_ARG, "argmax is NULL");
+    if (T < 1 || T > 4) return moe_fail(MOE_ERR_INVALID_ARG, "num_tokens %d out of range [1, 4]", T);
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    void* sp = nullptr;
+    hipError_t e = head::noalloc_scratch(&sp);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "scratch lookup failed: %s", hipGetErrorString(e));
+    e = head::launch_head_rowmajor(w.ptr, (const float*)row_scale.ptr, (const uint16_t*)x, T, logits, argmax, sp, vocab,
+                                   hidden, (hipStream_t)stream);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "LM-head launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 

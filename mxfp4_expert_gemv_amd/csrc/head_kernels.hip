@@ -17,10 +17,13 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace head {
 
 constexpr int kWave = 64;
 constexpr int kSlice = 256;  // K elements per wave: 16 units of 16 E4M3 codes, or 32 units of 8 bf16
+constexpr int kNoAllocMaxVocab = 262144;  // largest vocabulary of fp8_head_run_noalloc (its scratch size)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -72,8 +75,10 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
 }
 
 // FP8: rows of E4M3 codes (16 per 16-byte unit), converted exactly to bf16 pairs; otherwise rows of
-// bf16 (8 per unit), the unquantised head the FP8 one replaces (its scales are 1).
-template <int T, bool FP8>
+// bf16 (8 per unit), the unquantised head the FP8 one replaces (its scales are 1).  RM: the weights
+// are the caller's row-major [V][H] matrix instead of the repacked tiles (lane l of tile vt reads
+// row vt * 64 + l, rows past V repeat the last one and are left out of the argmax; scales [V]).
+template <int T, bool FP8, bool RM = false>
 __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     constexpr int kUnit = FP8 ? 16 : 8;             // K elements per 16-byte unit
     constexpr int kUnitsPerWave = kSlice / kUnit;
@@ -85,7 +90,11 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     const int H = a.H, NU = H / kUnit, Hh = H / 2;
 
     uint4 wr[kUnitsPerWave];
-    {
+    if constexpr (RM) {
+        const uint4* p = a.w + (size_t)min(vt * kWave + lane, a.V - 1) * NU + (size_t)wv * kUnitsPerWave;
+#pragma unroll
+        for (int i = 0; i < kUnitsPerWave; ++i) wr[i] = ld_nt(p + i);
+    } else {
         const uint4* p = a.w + ((size_t)vt * NU + (size_t)wv * kUnitsPerWave) * kWave + lane;
 #pragma unroll
         for (int i = 0; i < kUnitsPerWave; ++i) wr[i] = ld_nt(p + i * kWave);
@@ -268,15 +277,15 @@ hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, 
     return hipGetLastError();
 }
 
-template <bool FP8>
+template <bool FP8, bool RM = false>
 static hipError_t launch_head_t(const HeadArgs& a, int T, int VT, hipStream_t stream) {
     const unsigned block = kWave * (a.H / kSlice);
     const size_t lds = (size_t)T * a.H * 2;
     switch (T) {
-        case 1: head_kernel<1, FP8><<<VT, block, lds, stream>>>(a); break;
-        case 2: head_kernel<2, FP8><<<VT, block, lds, stream>>>(a); break;
-        case 3: head_kernel<3, FP8><<<VT, block, lds, stream>>>(a); break;
-        case 4: head_kernel<4, FP8><<<VT, block, lds, stream>>>(a); break;
+        case 1: head_kernel<1, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 2: head_kernel<2, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 3: head_kernel<3, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 4: head_kernel<4, FP8, RM><<<VT, block, lds, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -288,6 +297,54 @@ hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int
     const int VT = (V + kWave - 1) / kWave;
     HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, draft, accept, V, H};
     return fp8 ? launch_head_t<true>(a, T, VT, stream) : launch_head_t<false>(a, T, VT, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// The head without a handle, for callers that cannot allocate: its scratch (the arrival counter and
+// the per-tile maxima of the argmax reduction) is this fixed device array, one copy per GPU that
+// the library runs on, held until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it is a stand-in, not a device address); it passes the address that
+// hipGetSymbolAddress returns for the current device.
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kNoAllocMaxTiles = kNoAllocMaxVocab / kWave;
+constexpr size_t kScratchTicket = 0;                                                 // unsigned, zero between calls
+constexpr size_t kScratchVal = 256;                                                  // float [tiles][4]
+constexpr size_t kScratchIdx = kScratchVal + (size_t)kNoAllocMaxTiles * 4 * 4;       // int32 [tiles][4]
+constexpr size_t kScratchBytes = kScratchIdx + (size_t)kNoAllocMaxTiles * 4 * 4;     // 131,328 bytes
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];  // zero when the library is loaded
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of the scratch array on the current device (looked up once per device).
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+// fp8_head_run's kernel on row-major E4M3 weights [V][H] and scales [V], with the scratch above
+// (V <= kNoAllocMaxVocab, checked by the caller).
+hipError_t launch_head_rowmajor(const void* w, const float* scale, const uint16_t* x, int T, float* logits,
+                                int32_t* argmax, void* scratch_dev, int V, int H, hipStream_t stream) {
+    const int VT = (V + kWave - 1) / kWave;
+    uint8_t* sp = (uint8_t*)scratch_dev;
+    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, (float*)(sp + kScratchVal), (int32_t*)(sp + kScratchIdx),
+               (unsigned*)(sp + kScratchTicket), nullptr, nullptr, V, H};
+    return launch_head_t<true, true>(a, T, VT, stream);
 }
 
 }  // namespace head
