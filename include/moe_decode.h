@@ -212,6 +212,12 @@ moe_status fp8_head_run_noalloc(int32_t vocab, int32_t hidden, moe_tensor w, moe
  * MOE_ERR_DTYPE (tag), MOE_ERR_NO_DEVICE, MOE_ERR_HIP (launch). */
 moe_status fp8_head_quantize(int32_t rows, int32_t cols, moe_tensor w, void* codes, float* scales, void* stream);
 
+/* Measurement probe: reads `bytes` (a multiple of 16) of device memory at src (16-byte aligned)
+ * with the weight kernels' 16-byte non-temporal loads, `grid` workgroups of 256 threads, and writes
+ * one fold of the data per workgroup to out (UINT32 [grid], device).  Timing it gives the practical
+ * HBM read ceiling of that access pattern, reported beside the 8 TB/s peak.  Only enqueues work. */
+moe_status moe_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out, int32_t grid, void* stream);
+
 /* Kernel timing instrumentation.  moe_decode_timing_enable(h, max_runs) makes the next up to
  * max_runs calls of moe_decode_run launch their kernels one by one on the caller's stream (no
  * graph), each with a start and a stop HIP event that the runtime stamps with that kernel's own

@@ -24,7 +24,7 @@ F_DIRECT_LAUNCH = 0x2
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
            "moe_decode_destroy", "moe_decode_check", "moe_decode_timing_enable", "moe_decode_timing_read", "fp8_head_create", "fp8_head_run", "fp8_head_destroy", "fp8_head_quantize", "bf16_head_create", "fp8_head_verify",
-           "fp8_head_run_noalloc", "moe_status_string", "moe_last_error")
+           "fp8_head_run_noalloc", "moe_probe_stream_read", "moe_status_string", "moe_last_error")
 NOALLOC_MAX_VOCAB = 262144
 
 
@@ -96,6 +96,7 @@ def lib():
             "bf16_head_create": [i32, i32, Tensor, vp, ctypes.POINTER(vp)],
             "fp8_head_verify": [vp, vp, i32, vp, vp, vp, vp],
             "fp8_head_run_noalloc": [i32, i32, Tensor, Tensor, vp, i32, vp, vp, vp],
+            "moe_probe_stream_read": [vp, ctypes.c_uint64, vp, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -323,6 +324,13 @@ def fp8_head_run_noalloc(w, row_scale, x, argmax, logits=None, num_tokens: int |
     _check(lib().fp8_head_run_noalloc(vocab, hidden, _tensor(w, DT_E4M3, "w", vocab * hidden),
                                       _tensor(row_scale, DT_FP32, "row_scale", vocab * 4), _ptr(x), T, _ptr(logits),
                                       _ptr(argmax), _stream(stream)))
+
+
+def moe_probe_stream_read(src, out, grid: int, stream=None) -> None:
+    """Streaming read of the whole device tensor src (the practical HBM read ceiling); out: uint32
+    [grid] on the device.  Enqueues only."""
+    _check(lib().moe_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), grid,
+                                       _stream(stream)))
 
 
 def fp8_head_destroy(handle) -> None:

@@ -19,6 +19,25 @@ hipError_t launch_head_rowmajor(const void* w, const float* scale, const uint16_
                                 int32_t* argmax, void* scratch_dev, int V, int H, hipStream_t stream);
 }
 
+namespace probe {
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* out, int grid, hipStream_t stream);
+}
+
+extern "C" moe_status moe_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out, int32_t grid,
+                                            void* stream) {
+    if (!src || (uintptr_t)src % 16 || bytes % 16 || bytes == 0)
+        return moe_fail(MOE_ERR_INVALID_ARG, "src must be 16-byte aligned and bytes a positive multiple of 16");
+    if (!out || grid < 1 || grid > 65536) return moe_fail(MOE_ERR_INVALID_ARG, "out is NULL or grid out of range");
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    hipError_t e = probe::launch_stream_read(src, bytes, out, grid, (hipStream_t)stream);
+    if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
 struct fp8_head_handle {
     int V, H, VT, device;
     bool fp8;          // E4M3 rows with scales, or bf16 rows (bf16_head_create)

@@ -348,3 +348,41 @@ hipError_t launch_head_rowmajor(const void* w, const float* scale, const uint16_
 }
 
 }  // namespace head
+
+namespace probe {
+
+// Reads n16 16-byte units with the weight kernels' load (16 bytes per lane, non-temporal), several
+// independent loads in flight per lane, and folds them into one word per workgroup so that the
+// loads are kept.  The practical HBM read ceiling of this access pattern.
+__global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src, uint64_t n16, uint32_t* out) {
+    constexpr int kUnroll = 8;
+    uint32_t acc = 0;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) v[j] = head::ld_nt(src + i + j * stride);
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = head::ld_nt(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < (int)blockDim.x; ++t) r ^= red[t];
+        out[blockIdx.x] = r;
+    }
+}
+
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* out, int grid, hipStream_t stream) {
+    stream_read<<<grid, 256, 0, stream>>>((const uint4*)src, bytes / 16, out);
+    return hipGetLastError();
+}
+
+}  // namespace probe

@@ -135,20 +135,27 @@ __global__ void repack_w2s(const uint8_t* __restrict__ src, uint8_t* __restrict_
 // shared pieces: MoE input, FP8 quantisation of the input, gate/up tile
 // ------------------------------------------------------------------------------------------------
 
-// The MoE input of T tokens in one workgroup: x_in = x, or bf16(fl32(x * r)) with
-// r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in fp64 (sum of squares in fp64), staged in LDS
-// xb[T][H]; and its per-token FP8 scale s = max|x_in| / 448 (1 when x_in = 0), returned in sx.
-// The maximum of |x_in| is bf16(max|x| * r) because rounding is monotonic, so both reductions
-// share one barrier.  red_d, red_m: LDS [waves][T].  Ends with a barrier.
+// The MoE input of T tokens in one workgroup, in two steps so that the caller can issue the load of
+// x before other loads (the loads of a wave complete in issue order):
+// moe_input_load: this thread's 8-element chunk of every token of x (threads past H / 8 load none).
+// moe_input_finish: x_in = x, or bf16(fl32(x * r)) with r = 1 / sqrt(mean(x^2) + 1e-6) evaluated in
+// fp64 (sum of squares in fp64), staged in LDS xb[T][H]; and its per-token FP8 scale
+// s = max|x_in| / 448 (1 when x_in = 0), returned in sx.  The maximum of |x_in| is bf16(max|x| * r)
+// because rounding is monotonic, so both reductions share one barrier.  red_d, red_m: LDS
+// [waves][T].  Ends with a barrier.
 template <int T>
-__device__ void moe_input(const uint16_t* __restrict__ x, int H, bool normalize, uint16_t* xb, double* red_d,
-                          float* red_m, float (&sx)[T]) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
-    const bool has = tid < NC;
-    uint4 v[T];
+__device__ __forceinline__ void moe_input_load(const uint16_t* __restrict__ x, int H, uint4 (&v)[T]) {
+    const int tid = threadIdx.x, NC = H / 8;
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        if (has) v[t] = *(const uint4*)(x + (size_t)t * H + tid * 8);
+        if (tid < NC) v[t] = *(const uint4*)(x + (size_t)t * H + tid * 8);
+}
+
+template <int T>
+__device__ void moe_input_finish(uint4 (&v)[T], int H, bool normalize, uint16_t* xb, double* red_d, float* red_m,
+                                 float (&sx)[T]) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6, NC = H / 8;
+    const bool has = tid < NC;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         double ss = 0.0;
@@ -801,6 +808,10 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
         }
     }
     const int e = blockIdx.x * NW + wv;
+    // 1-2 tokens: x first, so that waiting for it does not wait for the router rows
+    uint4 xv[T];
+    if constexpr (!CENTRAL) moe_input_load<T>(a.x, H, xv);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 wr[kMaxWaves];
     {
         const uint4* p = (const uint4*)(a.router + (size_t)min(e, a.E - 1) * H);
@@ -812,7 +823,7 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
         __syncthreads();
     } else {
         float sx[T];
-        moe_input<T>(a.x, H, a.normalize != 0, xb, red_d, wmax, sx);
+        moe_input_finish<T>(xv, H, a.normalize != 0, xb, red_d, wmax, sx);
         if (blockIdx.x == 0 && a.trace)
             for (int i = tid; i < T * NU; i += blockDim.x) ((uint4*)a.trace)[i] = ((const uint4*)a.x)[i];
         quantize_slice<T>(xb, H, sx, a.xq, a.xs, a.x_codes, a.x_scale);

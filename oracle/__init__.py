@@ -17,7 +17,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB = os.path.join(_HERE, "libmoe_oracle.so")
-GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-shared", "-fPIC"]
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-shared", "-fPIC", "-fopenmp"]
 
 # Which independent check pins each oracle function (tests/test_oracle_*.py).
 PINS = {
@@ -84,6 +84,10 @@ def _load(path):
     for n in ("oracle_e4m3_encode_array", "oracle_bf16_encode_array"):
         getattr(L, n).restype = None
         getattr(L, n).argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64]
+    L.oracle_set_threads.restype = None
+    L.oracle_set_threads.argtypes = [ctypes.c_int]
+    L.oracle_max_threads.restype = ctypes.c_int
+    L.oracle_max_threads.argtypes = []
     L.oracle_route.restype = ctypes.c_int
     L.oracle_route.argtypes = [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -140,6 +144,16 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's loops over independent output rows (1 = single-threaded, the
+    default); results do not depend on it."""
+    lib().oracle_set_threads(n)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
 
 
 # ---- codecs ------------------------------------------------------------------------------------

@@ -4,10 +4,13 @@
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline
  * leg load this file's library.  The GPU library never links, calls or includes it, and it shares
- * no code, header, table or helper with the GPU path.  It is plain, slow and single-threaded:
- * every sum runs in natural index order in fp64, and every quantisation step is written out as
- * its definition.  The block-scaled sums are exact in fp64 for the generated value ranges (each
- * term is an integer multiple of 2^-16 below 2^26, a 2560-term sum stays below 2^38).
+ * no code, header, table or helper with the GPU path.  It is plain and slow: every sum runs in
+ * natural index order in fp64, and every quantisation step is written out as its definition.  It
+ * runs on one thread unless oracle_set_threads asks for more; then the loops over independent
+ * output rows (router rows, gate/up rows, down rows) are split over OpenMP threads, each row still
+ * summed in order by one thread, so no result changes.  The block-scaled sums are exact in fp64
+ * for the generated value ranges (each term is an integer multiple of 2^-16 below 2^26, a
+ * 2560-term sum stays below 2^38).
  *
  * Pages cited (titles as printed; sections named on each page):
  *   [tanhow]  tanhow.com, "NVIDIA 在单台 DGX Spark 上叠加三项优化，Ling-3.0-flash 的 MoE 推理吞吐提升 42.5%"
@@ -40,6 +43,7 @@
  *     the maxima.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -125,6 +129,11 @@ void oracle_bf16_encode_array(const float* in, uint16_t* out, uint64_t n) {
     for (uint64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(in[i]);
 }
 
+/* Number of threads for the row loops below (1 by default). */
+static int g_threads = 1;
+void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int oracle_max_threads(void) { return omp_get_num_procs(); }
+
 /* Decode tables, filled from the decoders above on first use. */
 static double g_e2m1[16], g_e8m0[256], g_e4m3[256];
 static int g_tables_ready = 0;
@@ -198,6 +207,7 @@ static void router_logits(const oracle_shape* s, const uint16_t* router, const f
     const int H = s->hidden;
     const double nu = (double)(H - 1) * 0x1p-24;
     const double gamma = nu / (1.0 - nu);
+#pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int e = 0; e < s->num_experts; ++e) {
         double acc = 0.0, mag = 0.0;
         for (int c = 0; c < H; ++c) {
@@ -313,6 +323,7 @@ int oracle_moe_layer(const oracle_shape* s, const oracle_weights* W, const uint1
             const uint8_t* w2 = W->w2[e];
             const uint8_t* w2s = W->w2_s[e];
             if (!w13 || !w13s || !w2 || !w2s) { rc = -2; goto done; }
+#pragma omp parallel for num_threads(g_threads) schedule(static)
             for (int i = 0; i < I; ++i) {
                 double ag = 0.0, au = 0.0;
                 for (int c = 0; c < H; ++c) {
@@ -325,6 +336,7 @@ int oracle_moe_layer(const oracle_shape* s, const oracle_weights* W, const uint1
             }
             float sh = quantize_e4m3(h, I, qh);
             for (int i = 0; i < I; ++i) hh[i] = g_e4m3[qh[i]];
+#pragma omp parallel for num_threads(g_threads) schedule(static)
             for (int r = 0; r < H; ++r) {
                 double acc = 0.0;
                 for (int i = 0; i < I; ++i) acc += mx_elem(w2, w2s, I, r, i) * hh[i];
