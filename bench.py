@@ -3,15 +3,21 @@
 Workload timed for ``value``: the 42-layer MoE decode stack at 1 token (hidden 2560, 512 routed
 experts, top-8 + 1 shared, SwiGLU width 768, MXFP4 experts, FP8 activations, unweighted RMSNorm on
 each layer's input and a bf16 residual), ~67.6 GB of distinct expert weights resident in HBM, run
-back to back through the C ABI.  One step = one pass through all 42 layers.  ``value`` is the
-algorithmic HBM bytes of a pass (router + the touched experts, counted from the returned ids)
-divided by the pass time.  Also reported: the same stack at 4 tokens (disjoint top-8 sets, 33
-experts per layer), single layers at 1 and 4 tokens with the 256 MB last-level cache flushed
-between passes, the roofline of the dominant kernel of a 1-token layer (kernel times from HIP
-events stamped by the kernel launches themselves), and the CPU oracle timed on a bounded sample of
-the same stack on the host cores.
+back to back through the C ABI (graph replays).  One step = one pass through all 42 layers.
+``value`` is the algorithmic HBM bytes of a pass (router + the touched experts, counted from the
+returned ids) divided by the pass time of K back-to-back steps.  Also reported:
+  - the same stack at 4 tokens (disjoint top-8 sets, 33 experts per layer);
+  - per-pass statistics (median, p10, p90, min) of both stacks, warm (back to back) and with the
+    256 MB last-level cache flushed before every pass (a 1 GiB write outside the timed events);
+  - kernel times of a layer launched kernel by kernel (events stamped by the launches themselves);
+  - single layers at 1 and 4 tokens with the cache flushed between passes;
+  - the roofline of the dominant 1-token kernel against 8 TB/s and against the practical read
+    ceiling that a plain streaming-read probe reaches on the same box;
+  - the FP8 LM head, the BF16 head it replaces, and the head's load-time quantisation;
+  - the CPU oracle on a bounded sample of the same stack, on one thread and on every core;
+  - the GPU, ROCm version and clocks.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--graph-only]
 """
 from __future__ import annotations
 
@@ -40,6 +46,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 LM-head measurement")
+    ap.add_argument("--no-jit", action="store_true", help="skip the run-time compiled (hipRTC) kernels' measurement")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="time only graph replays of the stack (no direct-launch kernel timing, no single layers, "
+                         "head or probe): the command to run under a kernel-trace profiler")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
@@ -115,13 +125,46 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def pass_stats(T, passes, flush):
+        """Each pass timed on its own (events around the pass only); with flush, a 1 GiB buffer is
+        written before every pass, outside the events, to evict the last-level cache."""
+        times = []
+        for _ in range(passes):
+            if flush is not None:
+                flush.add_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.moe_decode_run(h, x4[:T], T, x_out=x_out[:T])
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in times]) / L
+        return {"us_per_layer_median": round(float(np.median(us)), 3), "p10": round(float(np.percentile(us, 10)), 3),
+                "p90": round(float(np.percentile(us, 90)), 3), "min": round(float(us.min()), 3), "passes": passes}
+
     def kernel_times(T, runs):
-        moe.moe_decode_timing_enable(h, runs)
+        """Kernels launched one by one between kernel-stamped events: us per launch, per class."""
+        moe.moe_decode_timing_enable(h, runs, 0)
         for _ in range(runs):
             moe.moe_decode_run(h, x4[:T], T, x_out=x_out[:T])
         t = moe.moe_decode_timing_read(h)
         moe.moe_decode_timing_enable(h, 0)
-        return {c: t[c]["total_ms"] / max(t[c]["launches"], 1) * 1e3 for c in moe.TIMING_CLASSES}  # us/launch
+        return {c: t[c]["total_ms"] / t[c]["launches"] * 1e3 for c in moe.TIMING_CLASSES if t[c]["launches"]}
+
+    def graph_breakdown(T, runs):
+        """Graph-replayed passes whose kernels stamp the device wall clock per workgroup: per class the
+        mean span (first workgroup's start to last workgroup's end) and the mean gap before it; spans
+        and gaps of a layer add up to the layer's share of the pass."""
+        moe.moe_decode_timing_enable(h, runs, 1)
+        for _ in range(runs):
+            moe.moe_decode_run(h, x4[:T], T, x_out=x_out[:T])
+        t = moe.moe_decode_timing_read(h)
+        moe.moe_decode_timing_enable(h, 0)
+        out = {c: {"span_us": round(t[c]["total_ms"] / t[c]["launches"] * 1e3, 3),
+                   "gap_before_us": round(t[c]["gap_ms"] / max(t[c]["gap_launches"], 1) * 1e3, 3)}
+               for c in moe.TIMING_CLASSES if t[c]["launches"]}
+        out["layer_us"] = round(sum(v["span_us"] + v["gap_before_us"] for v in out.values()), 3)
+        return out
 
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -133,17 +176,70 @@ def main():
         log(f"copy probe: 4 copies of {COPY_PROBE_BYTES} bytes")
 
     results = {}
+    flush_buf = None if args.graph_only else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for T in (1, 4):
         nbytes, distinct = pass_bytes(T)
         ms = time_stack(T, args.steps, args.warmup)
         moe.moe_decode_check(h)  # no asynchronous device error
-        kt = kernel_times(T, min(args.steps, 50))
         gbs = nbytes / (ms * 1e-3) / 1e9
         results[T] = {"ms_per_pass": ms, "us_per_layer": ms * 1e3 / L, "tokens_per_s": T / (ms * 1e-3),
                       "bytes_per_pass": nbytes, "gb_s": gbs, "pct_of_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
-                      "distinct_experts_per_layer": sorted(set(distinct)), "kernel_us": kt}
+                      "distinct_experts_per_layer": sorted(set(distinct))}
         log(f"stack T={T}: {ms * 1e3:.1f} us/pass, {ms * 1e3 / L:.2f} us/layer, {gbs:.0f} GB/s "
-            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); per-kernel us {kt}")
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+        if args.graph_only:
+            continue
+        npass = max(20, min(args.steps, 100))
+        warm = pass_stats(T, npass, None)
+        flushed = pass_stats(T, npass, flush_buf)
+        kt = kernel_times(T, min(args.steps, 50))
+        gb = graph_breakdown(T, min(args.steps, 20))
+        results[T].update({"warm": warm, "flushed": flushed, "kernel_us_direct_launch": kt,
+                           "kernel_sum_us_per_layer": round(sum(kt.values()), 3), "graph_replay_breakdown": gb})
+        log(f"stack T={T}: per pass, warm {warm}; last-level cache flushed before each pass {flushed}; "
+            f"kernels launched one by one (us) {kt}; graph replays, per-kernel span and gap before it (us) {gb}")
+    if args.graph_only:
+        r1 = results[1]
+        print(json.dumps({"metric": METRIC, "value": round(r1["gb_s"], 1), "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r1["ms_per_pass"], 5),
+                          "mode": "graph replays only", "stack_t4_ms_per_pass": round(results[4]["ms_per_pass"], 5)}),
+              flush=True)
+        moe.moe_decode_destroy(h)
+        return
+    del flush_buf
+    # the same stack on kernels compiled at run time for this shape (hipRTC), against the
+    # ahead-of-time build just timed
+    jit = None
+    if not args.no_jit:
+        import tempfile
+        moe.moe_decode_destroy(h)
+        torch.cuda.synchronize()
+        cache = tempfile.mkdtemp(prefix="moe_jit_cache_")  # an empty cache: the first create compiles
+        os.environ["MOE_JIT_CACHE_DIR"] = cache
+        t0 = time.time()
+        h = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, L,
+                                  moe.F_RMSNORM_INPUT | moe.F_JIT)
+        create_s = time.time() - t0
+        t0 = time.time()  # a second handle of the same shape loads the cached code object
+        h2 = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, 1,
+                                   moe.F_RMSNORM_INPUT | moe.F_JIT)
+        cached_create_s = time.time() - t0
+        cached = moe.moe_decode_query(h2)["jit_from_cache"]
+        moe.moe_decode_destroy(h2)
+        for l in range(L):
+            layer_tensors(st["seed"], l, st["router_attempts"][l], bufs)
+            moe.moe_decode_set_layer(h, l, bufs["router"], bufs["w13"], bufs["w13_s"], bufs["w2"], bufs["w2_s"])
+        torch.cuda.synchronize()
+        ji = moe.moe_decode_query(h)
+        jit = {"variant": ji["variant"], "compile_ms": round(ji["jit_compile_ms"], 1),
+               "from_cache": ji["jit_from_cache"], "create_s": round(create_s, 3),
+               "second_create_from_cache": cached, "second_create_s": round(cached_create_s, 3)}
+        for T in (1, 4):
+            ms = time_stack(T, args.steps, args.warmup)
+            jit[f"t{T}_us_per_layer"] = round(ms * 1e3 / L, 3)
+            jit[f"t{T}_vs_ahead_of_time"] = round(results[T]["ms_per_pass"] / ms, 4)
+        log(f"run-time compiled kernels: {jit}")
+    probe = hbm_probe(moe, torch, dev, stream)
 
     # single layers (1 and 4 tokens), last-level cache flushed between passes
     single = {}
@@ -189,7 +285,7 @@ def main():
         del flush
 
     # roofline of the dominant kernel of a 1-token layer (the one with the largest kernel time)
-    kt1 = results[1]["kernel_us"]
+    kt1 = results[1]["kernel_us_direct_launch"]
     names = kernel_names(info["variant"], 1)
     kb = kernel_bytes(shape, 1, shape.top_k)
     per_kernel = {c: {"kernel": names[c], "bytes_per_launch": kb[c], "us_per_launch": round(kt1[c], 3),
@@ -199,7 +295,9 @@ def main():
     traffic = measured_traffic(names[dom])
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": names[dom],
-                "bytes_per_launch": kb[dom], "us_per_launch": round(kt1[dom], 3), "all_kernels_t1": per_kernel}
+                "bytes_per_launch": kb[dom], "us_per_launch": round(kt1[dom], 3), "all_kernels_t1": per_kernel,
+                "practical_read_ceiling_gb_s": probe["best_gb_s"],
+                "frac_of_practical_ceiling": round(achieved / probe["best_gb_s"], 4)}
     log(f"roofline: dominant {names[dom]} {kt1[dom]:.2f} us/launch, {achieved:.0f} GB/s; {per_kernel}")
 
     head = None if args.no_head else time_head(moe, dev, stream)
@@ -207,6 +305,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, st, x4_host[:1], expert_bytes, router_bytes)
+    env = environment(torch)
 
     r1 = results[1]
     out = {"metric": METRIC, "value": round(r1["gb_s"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -215,10 +314,12 @@ def main():
            "config": {"workload": "42-layer MoE decode stack, 1 token", "hidden": H, "experts": shape.num_experts,
                       "top_k": shape.top_k, "shared": shape.num_shared, "inter": I, "layers": L, "tokens": 1},
            "us_per_layer": round(r1["us_per_layer"], 3), "tokens_per_s": round(r1["tokens_per_s"], 1),
-           "pct_of_hbm_peak": round(r1["pct_of_hbm_peak"], 2), "kernel_us_t1": r1["kernel_us"],
+           "pct_of_hbm_peak": round(r1["pct_of_hbm_peak"], 2),
+           "pct_of_practical_read_ceiling": round(100 * r1["gb_s"] / probe["best_gb_s"], 2),
+           "stack_t1": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r1.items()},
            "stack_t4": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[4].items()},
-           "single_layer": single, "lm_head": head, "variant": info["variant"], "roofline": roofline,
-           "cpu_baseline": cpu}
+           "single_layer": single, "lm_head": head, "hbm_read_probe": probe, "jit": jit, "variant": info["variant"],
+           "roofline": roofline, "cpu_baseline": cpu, "env": env}
     moe.moe_decode_destroy(h)
     print(json.dumps(out), flush=True)
 
@@ -412,12 +513,86 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
     return out
 
 
-def cpu_baseline(shape, st, x_host, expert_bytes, router_bytes, budget_s=12.0):
-    """The oracle (single-threaded C, fp64) run layer by layer along the same 1-token stack on the
-    host cores until about budget_s of compute; reported in GB/s of the same algorithmic bytes."""
+def hbm_probe(moe, torch, dev, stream, nbytes=4 << 30, reps=10):
+    """Practical HBM read ceiling: the library's streaming-read probe (16-byte non-temporal loads, as
+    the weight kernels use) over a 4 GiB buffer, far above the 256 MB last-level cache, at several
+    grid sizes; the best is reported."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(65536, dtype=torch.int32, device=dev)
+    by_grid = {}
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        moe.moe_probe_stream_read(buf, out, grid)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            moe.moe_probe_stream_read(buf, out, grid)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        by_grid[grid] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del buf, out
+    best = max(by_grid.values())
+    log(f"streaming-read probe over {nbytes >> 20} MiB: GB/s by grid {by_grid}")
+    return {"bytes": nbytes, "best_gb_s": best, "pct_of_8_tb_s": round(100 * best / HBM_PEAK_GBS, 2),
+            "gb_s_by_grid": by_grid}
+
+
+def environment(torch):
+    """GPU, ROCm version and clocks of the box the numbers were taken on."""
+    import subprocess
+    env = {"gpu": torch.cuda.get_device_name(0),
+           "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    for cmd in (["rocm-smi", "--showclocks"], ["rocm-smi", "--showpower"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            lines = [l.strip() for l in r.stdout.splitlines() if "GPU[" in l]
+            env[" ".join(cmd[1:])] = lines[:12]
+        except (OSError, subprocess.SubprocessError):
+            env[" ".join(cmd[1:])] = None
+    return env
+
+
+def host_cpu():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def cpu_baseline(shape, st, x_host, expert_bytes, router_bytes, budget_s=10.0):
+    """The oracle (C, fp64) run layer by layer along the same 1-token stack on the host cores until
+    about budget_s of compute, once on one thread and once with its loops over independent rows
+    split over every core available to the process; reported in GB/s of the same algorithmic
+    bytes.  The main figure is the multi-threaded one."""
+    import oracle
+
+    hc = host_cpu()
+    n = max(1, hc["affinity"])
+    single = _oracle_leg(shape, st, x_host, expert_bytes, router_bytes, budget_s, 1)
+    multi = _oracle_leg(shape, st, x_host, expert_bytes, router_bytes, budget_s, n)
+    oracle.set_threads(1)
+    return {"value": multi["gb_s"], "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"first {multi['layers']} layers of the 1-token 42-layer stack (compute only, weights "
+                      f"pre-generated), oracle loops over independent rows on {n} threads",
+            "us_per_layer": multi["us_per_layer"], "host": hc,
+            "single_thread": {"value": single["gb_s"], "unit": "GB/s", "cores": 1, "layers": single["layers"],
+                              "us_per_layer": single["us_per_layer"]}}
+
+
+def _oracle_leg(shape, st, x_host, expert_bytes, router_bytes, budget_s, threads):
     import oracle
     import synth
 
+    oracle.set_threads(threads)
     x = x_host.copy()
     spent, layers = 0.0, 0
     for l in range(st["layers"]):
@@ -436,10 +611,8 @@ def cpu_baseline(shape, st, x_host, expert_bytes, router_bytes, budget_s=12.0):
             break
     per_layer = router_bytes + (shape.top_k + shape.num_shared) * expert_bytes
     gbs = layers * per_layer / spent / 1e9
-    log(f"cpu oracle: {layers} layers in {spent:.1f}s ({spent / layers * 1e3:.0f} ms/layer)")
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {layers} layers of the 1-token 42-layer stack (compute only, weights pre-generated)",
-            "us_per_layer": round(spent / layers * 1e6, 1)}
+    log(f"cpu oracle, {threads} thread(s): {layers} layers in {spent:.1f}s ({spent / layers * 1e3:.0f} ms/layer)")
+    return {"gb_s": round(gbs, 4), "layers": layers, "us_per_layer": round(spent / layers * 1e6, 1)}
 
 
 if __name__ == "__main__":

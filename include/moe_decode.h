@@ -79,6 +79,16 @@ typedef enum {
 #define MOE_F_RMSNORM_INPUT 0x1u /* each layer's MoE input is RMSNorm(x), eps 1e-6, unweighted */
 #define MOE_F_DIRECT_LAUNCH 0x2u /* launch the kernels on the stream at every run instead of replaying
                                     a HIP graph captured on the first run with the same arguments */
+#define MOE_F_JIT 0x8u           /* compile the kernels at create time, with hipRTC, for this shape (H, E, k,
+                                    S, I), input normalisation and the current device's architecture,
+                                    instead of using the ahead-of-time build (tanhow.com, "NVIDIA 在单台 DGX
+                                    Spark 上叠加三项优化...", section "三项优化是什么", item 1: kernels compiled
+                                    at run time for the actual shapes, dtypes and GPU).  The code object is
+                                    cached on disk (MOE_JIT_CACHE_DIR, else $XDG_CACHE_HOME or
+                                    $HOME/.cache under mxfp4_expert_gemv_amd), keyed by shape, architecture
+                                    and a digest of source, options and kernels; a later create with the
+                                    same key loads it.  A failed compile makes create fail (MOE_ERR_HIP);
+                                    nothing falls back to the ahead-of-time kernels. */
 
 typedef struct moe_decode_handle moe_decode_handle;
 typedef struct fp8_head_handle fp8_head_handle;
@@ -129,6 +139,9 @@ typedef struct {
     uint64_t workspace_bytes;     /* handle-owned scratch memory */
     uint64_t bytes_per_layer_t1;  /* algorithmic HBM bytes of one layer, 1 token */
     int32_t layers_set;           /* number of layers set so far */
+    int32_t jit_from_cache;       /* MOE_F_JIT: 1 if the kernels were loaded from the cache, 0 if compiled */
+    double jit_compile_ms;        /* MOE_F_JIT: hipRTC compile time at create (0 on a cache hit) */
+    char jit_code_object[512];    /* MOE_F_JIT: path of the cached code object; "" otherwise */
 } moe_decode_info;
 
 /* Creates a handle bound to the current device: allocates repacked weight storage for all layers
@@ -218,20 +231,31 @@ moe_status fp8_head_quantize(int32_t rows, int32_t cols, moe_tensor w, void* cod
  * HBM read ceiling of that access pattern, reported beside the 8 TB/s peak.  Only enqueues work. */
 moe_status moe_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out, int32_t grid, void* stream);
 
-/* Kernel timing instrumentation.  moe_decode_timing_enable(h, max_runs) makes the next up to
- * max_runs calls of moe_decode_run launch their kernels one by one on the caller's stream (no
- * graph), each with a start and a stop HIP event that the runtime stamps with that kernel's own
- * begin and end times (hipExtLaunchKernel); 0 disables.  moe_decode_timing_read waits for those
- * events and returns, per kernel class, the number of launches and the summed kernel time, then
- * clears the record.  Meant for a measurement pass of its own. */
-#define MOE_TIMING_CLASSES 3 /* 0 router + top-k, 1 gate/up, 2 down + combine */
+/* Kernel timing instrumentation, for a measurement pass of its own.  moe_decode_timing_enable(h,
+ * max_runs, mode) records the next up to max_runs calls of moe_decode_run; max_runs 0 disables.
+ *   mode 0: the kernels are launched one by one on the caller's stream (no graph), each between a
+ *           start and a stop HIP event that the runtime stamps with that kernel's own begin and end
+ *           (hipExtLaunchKernel); total_ms[c] sums those durations.
+ *   mode 1: the pass is replayed from a HIP graph as in normal runs, and every workgroup of every
+ *           kernel writes the device's constant-rate wall clock at its start and end into a record
+ *           that the library allocates at enable; each run waits for its pass and reduces the
+ *           record: total_ms[c] sums, per kernel, the span from its first workgroup's start to its
+ *           last workgroup's end, gap_ms[c] the time from the previous kernel's end to its start (the
+ *           first kernel of a pass has none).  Over a pass, spans and gaps add up to the pass time.
+ * moe_decode_timing_read waits for the recorded runs, returns per kernel class the number of
+ * launches and the summed times, and clears the record. */
+#define MOE_TIMING_CLASSES 5 /* 0 input (3-4 tokens), 1 router + top-k, 2 gate/up, 3 h requantisation
+                                (3-4 tokens), 4 down + combine */
 typedef struct {
     uint32_t struct_size;                     /* sizeof(moe_decode_timing) */
     int32_t runs;                             /* runs recorded */
+    int32_t mode;                             /* the mode they were recorded in */
     uint64_t launches[MOE_TIMING_CLASSES];
     double total_ms[MOE_TIMING_CLASSES];
+    uint64_t gap_launches[MOE_TIMING_CLASSES]; /* mode 1: launches with a previous kernel in the pass */
+    double gap_ms[MOE_TIMING_CLASSES];         /* mode 1 */
 } moe_decode_timing;
-moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs);
+moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs, int32_t mode);
 moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_timing* out);
 
 const char* moe_status_string(moe_status s);

@@ -20,6 +20,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
 F_RMSNORM_INPUT = 0x1
 F_DIRECT_LAUNCH = 0x2
+F_JIT = 0x8
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",
@@ -57,16 +58,19 @@ class Outputs(ctypes.Structure):
 class Info(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("variant", ctypes.c_char * 64),
                 ("weight_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
-                ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32)]
+                ("bytes_per_layer_t1", ctypes.c_uint64), ("layers_set", ctypes.c_int32),
+                ("jit_from_cache", ctypes.c_int32), ("jit_compile_ms", ctypes.c_double),
+                ("jit_code_object", ctypes.c_char * 512)]
 
 
 # kernel classes of the timing record
-TIMING_CLASSES = ("router", "gateup", "down")
+TIMING_CLASSES = ("input", "router", "gateup", "requant", "down")
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("struct_size", ctypes.c_uint32), ("runs", ctypes.c_int32),
-                ("launches", ctypes.c_uint64 * 3), ("total_ms", ctypes.c_double * 3)]
+    _fields_ = [("struct_size", ctypes.c_uint32), ("runs", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("launches", ctypes.c_uint64 * 5), ("total_ms", ctypes.c_double * 5),
+                ("gap_launches", ctypes.c_uint64 * 5), ("gap_ms", ctypes.c_double * 5)]
 
 
 _lib = None
@@ -87,7 +91,7 @@ def lib():
             "moe_decode_query": [vp, ctypes.POINTER(Info)],
             "moe_decode_destroy": [vp],
             "moe_decode_check": [vp],
-            "moe_decode_timing_enable": [vp, i32],
+            "moe_decode_timing_enable": [vp, i32, i32],
             "moe_decode_timing_read": [vp, ctypes.POINTER(Timing)],
             "fp8_head_create": [i32, i32, Tensor, Tensor, vp, ctypes.POINTER(vp)],
             "fp8_head_run": [vp, vp, i32, vp, vp, vp],
@@ -230,7 +234,8 @@ def moe_decode_query(handle) -> dict:
     _check(lib().moe_decode_query(handle, ctypes.byref(info)))
     return {"variant": info.variant.decode(), "weight_bytes": info.weight_bytes,
             "workspace_bytes": info.workspace_bytes, "bytes_per_layer_t1": info.bytes_per_layer_t1,
-            "layers_set": info.layers_set}
+            "layers_set": info.layers_set, "jit_from_cache": bool(info.jit_from_cache),
+            "jit_compile_ms": info.jit_compile_ms, "jit_code_object": info.jit_code_object.decode()}
 
 
 def moe_decode_check(handle) -> None:
@@ -242,16 +247,19 @@ def moe_decode_destroy(handle) -> None:
     _check(lib().moe_decode_destroy(handle))
 
 
-def moe_decode_timing_enable(handle, max_runs: int) -> None:
-    _check(lib().moe_decode_timing_enable(handle, max_runs))
+def moe_decode_timing_enable(handle, max_runs: int, mode: int = 0) -> None:
+    """mode 0: kernels launched one by one between kernel-stamped events; mode 1: graph replays with
+    per-workgroup wall-clock stamps (spans and gaps)."""
+    _check(lib().moe_decode_timing_enable(handle, max_runs, mode))
 
 
 def moe_decode_timing_read(handle) -> dict:
     t = Timing()
     t.struct_size = ctypes.sizeof(Timing)
     _check(lib().moe_decode_timing_read(handle, ctypes.byref(t)))
-    return {"runs": t.runs, **{c: {"launches": t.launches[i], "total_ms": t.total_ms[i]}
-                               for i, c in enumerate(TIMING_CLASSES)}}
+    return {"runs": t.runs, "mode": t.mode,
+            **{c: {"launches": t.launches[i], "total_ms": t.total_ms[i], "gap_launches": t.gap_launches[i],
+                   "gap_ms": t.gap_ms[i]} for i, c in enumerate(TIMING_CLASSES)}}
 
 
 def fp8_head_create(w, row_scale, stream=None) -> ctypes.c_void_p:

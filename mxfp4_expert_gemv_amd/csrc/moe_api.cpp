@@ -7,10 +7,12 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
 #include "../../include/moe_decode.h"
+#include "moe_jit.h"
 #include "moe_launch.h"
 
 
@@ -57,19 +59,42 @@ struct moe_decode_handle {
         const void* x;
         int32_t T;
         moe_outputs out;
+        bool stamped;  // the timing record's variant (mode 1)
         hipGraphExec_t exec;
     };
     std::vector<GraphEntry> graphs;
     hipStream_t capture_stream = nullptr;
-    // timing instrumentation: 4 events per layer per recorded run
+    // timing instrumentation.  Mode 0: two events around each kernel of each layer of each recorded
+    // run (kernels launched one by one).  Mode 1: graph replays whose kernels write wall-clock stamps
+    // per workgroup into `stamps` (offsets per layer and kernel kind), reduced after each run.
+    int timing_mode = 0;
     std::vector<hipEvent_t> events;
+    std::vector<int> timing_T;  // token count of each recorded run
     int timing_max_runs = 0, timing_runs = 0;
+    unsigned long long* stamps = nullptr;
+    uint64_t stamp_count = 0;                          // 64-bit words
+    std::vector<uint64_t> stamp_off;                   // [L][kinds] word offsets
+    std::vector<unsigned long long> stamp_host;
+    double clock_khz = 0.0;
+    double span_ms[MOE_TIMING_CLASSES] = {}, gap_ms[MOE_TIMING_CLASSES] = {};
+    uint64_t span_n[MOE_TIMING_CLASSES] = {}, gap_n[MOE_TIMING_CLASSES] = {};
+    // kernels compiled at run time for this shape (MOE_F_JIT)
+    bool jit_on = false;
+    moe::JitResult jit{};
 };
 
 static void free_events(moe_decode_handle* h) {
     for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
     h->events.clear();
+    h->timing_T.clear();
     h->timing_max_runs = h->timing_runs = 0;
+    if (h->stamps) (void)hipFree(h->stamps);
+    h->stamps = nullptr;
+    h->stamp_count = 0;
+    for (int c = 0; c < MOE_TIMING_CLASSES; ++c) {
+        h->span_ms[c] = h->gap_ms[c] = 0.0;
+        h->span_n[c] = h->gap_n[c] = 0;
+    }
 }
 
 extern "C" const char* moe_status_string(moe_status s) {
@@ -107,7 +132,7 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->inter % moe::kBlock || !moe::shape_supported(sh))
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
                     c->hidden, c->inter);
-    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH))
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_JIT))
         return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
@@ -128,6 +153,7 @@ static void free_graphs(moe_decode_handle* h) {
 
 static void free_handle(moe_decode_handle* h) {
     free_events(h);
+    moe::jit_release(&h->jit);
     free_graphs(h);
     if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
     for (uint8_t* p : h->layer_mem)
@@ -207,6 +233,14 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->xn = (uint16_t*)(h->ws + o_xn);
     h->hq = h->ws + o_hq;
     h->hs = (float*)(h->ws + o_hs);
+    if (cfg->flags & MOE_F_JIT) {
+        s = moe::jit_build(sh, cfg->max_tokens, (cfg->flags & MOE_F_RMSNORM_INPUT) != 0, &h->jit);
+        if (s != MOE_OK) {
+            free_handle(h);
+            return s;
+        }
+        h->jit_on = true;
+    }
     *out = h;
     g_err[0] = 0;
     return MOE_OK;
@@ -241,9 +275,14 @@ extern "C" moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, 
     return MOE_OK;
 }
 
-// Enqueues the kernels of every layer on `stream` (timing: with the event records).
+// Enqueues the kernels of every layer on `stream` (timing: with the event records; stamped: with the
+// wall-clock stamps of the timing record, after clearing them).
 static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, const moe_outputs& o, hipStream_t stream,
-                              bool timing) {
+                              bool timing, bool stamped = false) {
+    if (stamped) {
+        hipError_t e = moe::launch_clear_u64(h->stamps, h->stamp_count, stream);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "timing record clear failed: %s", hipGetErrorString(e));
+    }
     const Shape& sh = h->sh;
     const bool norm = (h->cfg.flags & MOE_F_RMSNORM_INPUT) != 0;
     const int L = h->cfg.num_layers;
@@ -273,9 +312,50 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
         p.hs = h->hs;
         hipEvent_t* ev = nullptr;
         if (timing) ev = &h->events[((size_t)h->timing_runs * L + l) * 2 * MOE_TIMING_CLASSES];
-        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev);
+        if (stamped)
+            for (int k = 0; k < MOE_TIMING_CLASSES; ++k)
+                p.stamp[k] = moe::layer_grid(sh, T, k) ? h->stamps + h->stamp_off[(size_t)l * MOE_TIMING_CLASSES + k]
+                                                       : nullptr;
+        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev, h->jit_on ? &h->jit.kernels : nullptr);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
     }
+    return MOE_OK;
+}
+
+// Timing record, mode 1: waits for the pass, reads the stamps and adds, per kernel kind, the span from
+// its first workgroup's start to its last workgroup's end, and the gap from the previous kernel's end
+// to its start (the first kernel of the pass has no previous one).
+static moe_status reduce_stamps(moe_decode_handle* h, int T, hipStream_t stream) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(MOE_ERR_HIP, "timing record: synchronisation failed");
+    h->stamp_host.resize(h->stamp_count);
+    if (hipMemcpy(h->stamp_host.data(), h->stamps, h->stamp_count * 8, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(MOE_ERR_HIP, "timing record: read-back failed");
+    const double ms_per_tick = 1.0 / h->clock_khz;
+    const int L = h->cfg.num_layers;
+    bool have_prev = false;
+    unsigned long long prev_end = 0;
+    for (int l = 0; l < L; ++l)
+        for (int k = 0; k < MOE_TIMING_CLASSES; ++k) {
+            const int grid = moe::layer_grid(h->sh, T, k);
+            if (!grid) continue;
+            const unsigned long long* s = h->stamp_host.data() + h->stamp_off[(size_t)l * MOE_TIMING_CLASSES + k];
+            unsigned long long lo = ~0ull, hi = 0;
+            for (int b = 0; b < grid; ++b) {
+                if (!s[2 * b] || !s[2 * b + 1]) continue;  // a workgroup that wrote no record
+                lo = std::min(lo, s[2 * b]);
+                hi = std::max(hi, s[2 * b + 1]);
+            }
+            if (hi == 0) return fail(MOE_ERR_HIP, "timing record: kernel %d of layer %d left no stamps", k, l);
+            h->span_ms[k] += (double)(hi - lo) * ms_per_tick;
+            h->span_n[k] += 1;
+            if (have_prev) {
+                h->gap_ms[k] += (double)((long long)lo - (long long)prev_end) * ms_per_tick;
+                h->gap_n[k] += 1;
+            }
+            have_prev = true;
+            prev_end = hi;
+        }
+    ++h->timing_runs;
     return MOE_OK;
 }
 
@@ -296,24 +376,29 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
     if (o.x_codes && (uintptr_t)o.x_codes % 8) return fail(MOE_ERR_INVALID_ARG, "x_codes not 8-byte aligned");
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     const bool timing = h->timing_runs < h->timing_max_runs;
-    if (timing || (h->cfg.flags & MOE_F_DIRECT_LAUNCH)) {
-        moe_status st = enqueue_run(h, x, T, o, (hipStream_t)stream, timing);
-        if (st == MOE_OK && timing) ++h->timing_runs;
+    const bool stamped = timing && h->timing_mode == 1;
+    if ((timing && !stamped) || (h->cfg.flags & MOE_F_DIRECT_LAUNCH)) {
+        moe_status st = enqueue_run(h, x, T, o, (hipStream_t)stream, timing && !stamped, stamped);
+        if (st == MOE_OK && timing && !stamped) {
+            h->timing_T.push_back(T);
+            ++h->timing_runs;
+        }
+        if (st == MOE_OK && stamped) st = reduce_stamps(h, T, (hipStream_t)stream);
         return st;
     }
     // replay the captured launch sequence of this exact call (capture it on first use)
     for (auto& g : h->graphs) {
-        if (g.x == x && g.T == T && memcmp(&g.out, &o, sizeof o) == 0) {
+        if (g.x == x && g.T == T && g.stamped == stamped && memcmp(&g.out, &o, sizeof o) == 0) {
             if (hipGraphLaunch(g.exec, (hipStream_t)stream) != hipSuccess)
                 return fail(MOE_ERR_HIP, "hipGraphLaunch failed");
-            return MOE_OK;
+            return stamped ? reduce_stamps(h, T, (hipStream_t)stream) : MOE_OK;
         }
     }
     if (h->graphs.size() >= 16) free_graphs(h);
     hipGraph_t graph = nullptr;
     if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return fail(MOE_ERR_HIP, "hipStreamBeginCapture failed");
-    moe_status st = enqueue_run(h, x, T, o, h->capture_stream, false);
+    moe_status st = enqueue_run(h, x, T, o, h->capture_stream, false, stamped);
     hipError_t e = hipStreamEndCapture(h->capture_stream, &graph);
     if (st != MOE_OK) {
         if (graph) (void)hipGraphDestroy(graph);
@@ -324,25 +409,51 @@ extern "C" moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
-    h->graphs.push_back({x, T, o, exec});
+    h->graphs.push_back({x, T, o, stamped, exec});
     if (hipGraphLaunch(exec, (hipStream_t)stream) != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphLaunch failed");
-    return MOE_OK;
+    return stamped ? reduce_stamps(h, T, (hipStream_t)stream) : MOE_OK;
 }
 
-extern "C" moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs) {
+extern "C" moe_status moe_decode_timing_enable(moe_decode_handle* h, int32_t max_runs, int32_t mode) {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
     if (max_runs < 0 || max_runs > 100000) return fail(MOE_ERR_INVALID_ARG, "max_runs %d out of range", max_runs);
+    if (mode != 0 && mode != 1) return fail(MOE_ERR_INVALID_ARG, "timing mode %d (0 or 1)", mode);
     if (hipSetDevice(h->device) != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice failed");
     free_events(h);
-    const size_t n = (size_t)max_runs * h->cfg.num_layers * 2 * MOE_TIMING_CLASSES;
-    h->events.reserve(n);
-    for (size_t i = 0; i < n; ++i) {
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) {
-            free_events(h);
-            return fail(MOE_ERR_HIP, "hipEventCreate failed");
+    free_graphs(h);  // a stamped graph holds the record's pointers
+    h->timing_mode = mode;
+    if (max_runs == 0) return MOE_OK;
+    if (mode == 0) {
+        const size_t n = (size_t)max_runs * h->cfg.num_layers * 2 * MOE_TIMING_CLASSES;
+        h->events.reserve(n);
+        for (size_t i = 0; i < n; ++i) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) {
+                free_events(h);
+                return fail(MOE_ERR_HIP, "hipEventCreate failed");
+            }
+            h->events.push_back(e);
         }
-        h->events.push_back(e);
+    } else {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess || khz <= 0)
+            return fail(MOE_ERR_HIP, "wall clock rate query failed");
+        h->clock_khz = khz;
+        const int L = h->cfg.num_layers;
+        h->stamp_off.assign((size_t)L * MOE_TIMING_CLASSES, 0);
+        uint64_t words = 0;
+        for (int l = 0; l < L; ++l)
+            for (int k = 0; k < MOE_TIMING_CLASSES; ++k) {
+                int g = 0;
+                for (int T = 1; T <= h->cfg.max_tokens; ++T) g = std::max(g, moe::layer_grid(h->sh, T, k));
+                h->stamp_off[(size_t)l * MOE_TIMING_CLASSES + k] = words;
+                words += 2 * (uint64_t)g;
+            }
+        if (hipMalloc(&h->stamps, words * 8) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_OOM, "timing record allocation failed");
+        }
+        h->stamp_count = words;
     }
     h->timing_max_runs = max_runs;
     return MOE_OK;
@@ -355,23 +466,38 @@ extern "C" moe_status moe_decode_timing_read(moe_decode_handle* h, moe_decode_ti
     const uint32_t ss = out->struct_size;
     memset(out, 0, sizeof *out);
     out->struct_size = ss;
+    out->mode = h->timing_mode;
     out->runs = h->timing_runs;
     const int L = h->cfg.num_layers;
+    if (h->timing_mode == 1) {
+        for (int c = 0; c < MOE_TIMING_CLASSES; ++c) {
+            out->launches[c] = h->span_n[c];
+            out->total_ms[c] = h->span_ms[c];
+            out->gap_launches[c] = h->gap_n[c];
+            out->gap_ms[c] = h->gap_ms[c];
+            h->span_ms[c] = h->gap_ms[c] = 0.0;
+            h->span_n[c] = h->gap_n[c] = 0;
+        }
+        h->timing_runs = 0;
+        return MOE_OK;
+    }
     for (int r = 0; r < h->timing_runs; ++r) {
+        const int T = h->timing_T[r];
         for (int l = 0; l < L; ++l) {
             hipEvent_t* ev = &h->events[((size_t)r * L + l) * 2 * MOE_TIMING_CLASSES];
-            if (hipEventSynchronize(ev[2 * MOE_TIMING_CLASSES - 1]) != hipSuccess)
-                return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
             for (int c = 0; c < MOE_TIMING_CLASSES; ++c) {
+                if (!moe::layer_grid(h->sh, T, c)) continue;
                 float ms = 0.0f;
-                if (hipEventElapsedTime(&ms, ev[2 * c], ev[2 * c + 1]) != hipSuccess)
-                    return fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
+                if (hipEventSynchronize(ev[2 * c + 1]) != hipSuccess ||
+                    hipEventElapsedTime(&ms, ev[2 * c], ev[2 * c + 1]) != hipSuccess)
+                    return fail(MOE_ERR_HIP, "event timing failed");
                 out->total_ms[c] += ms;
                 out->launches[c] += 1;
             }
         }
     }
     h->timing_runs = 0;
+    h->timing_T.clear();
     return MOE_OK;
 }
 
@@ -381,8 +507,8 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
         return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
     const Shape& sh = h->sh;
     memset(info->variant, 0, sizeof info->variant);
-    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s", sh.gw(), sh.bpl(), sh.ksub(),
-                 sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph");
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s%s", sh.gw(), sh.bpl(), sh.ksub(),
+             sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph", h->jit_on ? "-jit" : "");
     info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
     info->workspace_bytes = h->ws_bytes;
     const uint64_t expert = sh.w13_bytes_per_expert() + sh.w13s_bytes_per_expert() + sh.w2_bytes_per_expert() +
@@ -391,6 +517,10 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
     int n = 0;
     for (char c : h->layer_set) n += c ? 1 : 0;
     info->layers_set = n;
+    info->jit_compile_ms = h->jit_on ? h->jit.compile_ms : 0.0;
+    info->jit_from_cache = h->jit_on && h->jit.from_cache ? 1 : 0;
+    memset(info->jit_code_object, 0, sizeof info->jit_code_object);
+    if (h->jit_on) snprintf(info->jit_code_object, sizeof info->jit_code_object, "%s", h->jit.path);
     return MOE_OK;
 }
 

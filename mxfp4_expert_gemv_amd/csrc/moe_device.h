@@ -1,8 +1,17 @@
 // moe_device.h -- device helpers shared by the MoE decode kernels (gfx950): format conversions,
 // MX block dot products, lane exchanges and reductions, top-k keys.  Private to the library.
 #pragma once
+#ifndef __HIPCC_RTC__
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#else  // hipRTC provides the runtime header itself, and the fixed-width integer types in a namespace
+using __hip_internal::int32_t;
+using __hip_internal::int64_t;
+using __hip_internal::uint16_t;
+using __hip_internal::uint32_t;
+using __hip_internal::uint64_t;
+using __hip_internal::uint8_t;
+#endif
 
 namespace moe {
 

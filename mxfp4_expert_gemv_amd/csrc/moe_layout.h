@@ -19,7 +19,9 @@
 // Per-call intermediate data lives in the handle's workspace, indexed by "pair" p = t*(k+S) + r:
 // token t, rank r < k (routed) or r = k (the shared expert).
 #pragma once
+#ifndef __HIPCC_RTC__
 #include <stdint.h>
+#endif
 
 namespace moe {
 

@@ -64,9 +64,19 @@ class DeviceLayer:
         return {e: synth.expert(self.shape, self.seed, self.layer, e) for e in used}
 
 
+# the two kernel builds behind the same calls: compiled ahead of time (default) and compiled at run
+# time for the handle's shape (MOE_F_JIT); the MoE parity tests run on both
+VARIANTS = {"aot": 0, "jit": moe.F_JIT}
+_variant = {"flags": 0}
+
+
+def set_variant(name: str):
+    _variant["flags"] = VARIANTS[name]
+
+
 def create(shape: synth.Shape, max_tokens: int = 4, num_layers: int = 1, flags: int = 0):
     return moe.moe_decode_create(shape.hidden, shape.num_experts, shape.top_k, shape.num_shared, shape.inter,
-                                 max_tokens, num_layers, flags)
+                                 max_tokens, num_layers, flags | _variant["flags"])
 
 
 def run_layer(handle, shape: synth.Shape, x_host: np.ndarray, num_layers: int = 1) -> dict:

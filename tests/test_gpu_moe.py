@@ -11,17 +11,21 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import (MANIFEST, DeviceLayer, check_layer, create, margin_attempt, normwise_err, run_layer,
-                       to_dev_u16)
+from gpu_cases import (MANIFEST, VARIANTS, DeviceLayer, check_layer, create, margin_attempt, normwise_err, run_layer,
+                       set_variant, to_dev_u16)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module", autouse=True)
-def gpu():
+@pytest.fixture(scope="module", autouse=True, params=sorted(VARIANTS))
+def variant(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     torch.cuda.init()
+    print(f"kernels: {request.param}", flush=True)
+    set_variant(request.param)
+    yield request.param
+    set_variant("aot")
 
 
 def _layer_case(shape, seed, x, layer_obj=None, handle=None):
@@ -90,7 +94,7 @@ def test_zero_input_gives_zero_output():
 
 
 @pytest.fixture(scope="module")
-def flash_t1():
+def flash_t1(variant):
     m = MANIFEST["layer_t1"]
     shape = synth.FLASH
     lay = DeviceLayer(shape, m["seed"])
@@ -176,10 +180,10 @@ def test_run_before_set_is_a_state_error():
     moe.moe_decode_destroy(h)
 
 
-def test_query_reports_variant_and_bytes(flash_t1):
+def test_query_reports_variant_and_bytes(flash_t1, variant):
     shape, lay, h, m = flash_t1
     info = moe.moe_decode_query(h)
-    assert info["variant"].startswith("gfx950-3k")
+    assert info["variant"].startswith("gfx950-3k") and info["variant"].endswith("-jit") == (variant == "jit")
     assert info["bytes_per_layer_t1"] == 30_822_400
 
 

@@ -12,7 +12,7 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import MANIFEST, DeviceLayer, Y_TOL, create, normwise_err, run_layer
+from gpu_cases import MANIFEST, VARIANTS, DeviceLayer, Y_TOL, create, normwise_err, run_layer, set_variant
 
 pytestmark = pytest.mark.gpu
 
@@ -20,10 +20,12 @@ pytestmark = pytest.mark.gpu
 MIN_WELL_POSED = 36
 
 
-@pytest.fixture(scope="module")
-def stack():
+@pytest.fixture(scope="module", params=sorted(VARIANTS))
+def stack(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    print(f"kernels: {request.param}", flush=True)
+    set_variant(request.param)
     st = MANIFEST["stack"]
     shape, L = synth.FLASH, st["layers"]
     h = create(shape, max_tokens=4, num_layers=L, flags=moe.F_RMSNORM_INPUT)
@@ -34,6 +36,7 @@ def stack():
         torch.cuda.synchronize()
         layers.append((lay.router_host, st["seed"], l))
         del lay
+    set_variant("aot")
     yield shape, h, layers, st
     moe.moe_decode_destroy(h)
 
