@@ -242,6 +242,8 @@ moe_status moe_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out,
  *           record: total_ms[c] sums, per kernel, the span from its first workgroup's start to its
  *           last workgroup's end, gap_ms[c] the time from the previous kernel's end to its start (the
  *           first kernel of a pass has none).  Over a pass, spans and gaps add up to the pass time.
+ *           The stamping kernels are separate ahead-of-time instances (also on a MOE_F_JIT handle):
+ *           the kernels of normal runs carry no timing code.
  * moe_decode_timing_read waits for the recorded runs, returns per kernel class the number of
  * launches and the summed times, and clears the record. */
 #define MOE_TIMING_CLASSES 5 /* 0 input (3-4 tokens), 1 router + top-k, 2 gate/up, 3 h requantisation

@@ -16,14 +16,18 @@
 
 namespace moe {
 
-// Timing record of a graph-replayed pass (moe_decode_timing_enable, mode 1): when the kernel
-// argument `stamp` is set, thread 0 of every workgroup writes the device's constant-rate wall clock
-// at the workgroup's start (stamp[2 b]) and, after a final barrier, at its end (stamp[2 b + 1]).
+// Timing record of a graph-replayed pass (moe_decode_timing_enable, mode 1): the kernels' STAMP
+// instances write, from thread 0 of every workgroup, the device's constant-rate wall clock at the
+// workgroup's start (stamp[2 b]) and, after a final barrier, at its end (stamp[2 b + 1]).  The other
+// instances, those of normal runs, carry none of this.
+template <bool STAMP>
 __device__ __forceinline__ void stamp_start(unsigned long long* s) {
-    if (s && threadIdx.x == 0) s[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+    if constexpr (STAMP)
+        if (threadIdx.x == 0) s[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
 }
+template <bool STAMP>
 __device__ __forceinline__ void stamp_end(unsigned long long* s) {
-    if (s) {
+    if constexpr (STAMP) {
         __syncthreads();
         if (threadIdx.x == 0) s[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
     }
@@ -588,8 +592,9 @@ struct K0Args {
 };
 
 // One workgroup per token (H/4 <= 1024 quads: one load per thread).
+template <bool STAMP = false>
 __global__ __launch_bounds__(1024) void k0_input(K0Args a) {
-    stamp_start(a.stamp);
+    stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem0[];
     __shared__ double redd[16];
     __shared__ float redf[16];
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(1024) void k0_input(K0Args a) {
     norm_quant<1>(a.x + o, MOE_SHAPE(H, a.H), MOE_SHAPE(NORM, a.normalize) != 0, (uint16_t*)smem0, a.xn + o, a.xq + o, a.xs + t,
                   a.trace ? a.trace + o : nullptr, a.x_scale ? a.x_scale + t : nullptr,
                   a.x_codes ? a.x_codes + o : nullptr, redd, redf);
-    stamp_end(a.stamp);
+    stamp_end<STAMP>(a.stamp);
 }
 
 struct KQArgs {
@@ -612,8 +617,9 @@ struct KQArgs {
 
 // One workgroup per h row (token, rank r <= k; r = k is the shared expert): s_h = max|h| / 448
 // (1 when h = 0) from the tile maxima, codes = RNE(h / s_h).
+template <bool STAMP = false>
 __global__ __launch_bounds__(256) void kq_requant(KQArgs a) {
-    stamp_start(a.stamp);
+    stamp_start<STAMP>(a.stamp);
     __shared__ float s;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int I = MOE_SHAPE(I, a.I), tiles = I / kGuOut, Ih = I / 2;
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(256) void kq_requant(KQArgs a) {
         const float2 w = *(const float2*)(a.h + (size_t)row * I + 2 * q);
         ((uint16_t*)(a.hq + (size_t)row * I))[q] = (uint16_t)e4m3_pack2(w.x / sv, w.y / sv);
     }
-    stamp_end(a.stamp);
+    stamp_end<STAMP>(a.stamp);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -679,9 +685,9 @@ struct K1Args {
 // One expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row; bf16 x bf16
 // products in fp32 FMA, one logit per wave and token.  At 1-2 tokens every workgroup also
 // normalises the input and stores the FP8 codes of its share of it.
-template <int T, int BPL>
+template <int T, int BPL, bool STAMP = false>
 __global__ __launch_bounds__(320) void k1_router(K1Args a) {
-    stamp_start(a.stamp);
+    stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem1[];
     uint16_t* xb = (uint16_t*)smem1;  // [T][H] bf16 MoE input
     __shared__ double red_d[kMaxWaves * T];
@@ -727,7 +733,7 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
                 pair[j] = j * (MOE_SHAPE(K, a.k) + MOE_SHAPE(S, a.S)) + MOE_SHAPE(K, a.k);
             }
             gateup_tile<T, BPL>(L, xh, H, sx, a.ntok, tok, pair, tile, MOE_SHAPE(I, a.I), a.h, a.hamax, red);
-            stamp_end(a.stamp);
+            stamp_end<STAMP>(a.stamp);
             return;
         }
     }
@@ -810,7 +816,7 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
             if (tid == 0) *a.ticket = 0u;  // read again only by the next layer's router, after this kernel
         }
     }
-    stamp_end(a.stamp);
+    stamp_end<STAMP>(a.stamp);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -839,9 +845,9 @@ struct K2Args {
 // token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
 // tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
 // the weights.
-template <int T, int BPL, int W>
+template <int T, int BPL, int W, bool STAMP = false>
 __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
-    stamp_start(a.stamp);
+    stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem2[];
     half2_t* xh = (half2_t*)smem2;  // [T][H/2] f16 values of the input's FP8 codes
     __shared__ float red[kMaxWaves * T * kGuRows];
@@ -909,7 +915,8 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
         // the slot's entries: from LDS (routed here) or straight from the stored list (uniform loads)
         const SlotTable& sl = ROUTE ? st : *a.slots;
         if (slot >= sl.n) {  // no expert for this slot: the whole workgroup leaves
-            if (a.stamp && threadIdx.x == 0) a.stamp[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+            if constexpr (STAMP)
+                if (threadIdx.x == 0) a.stamp[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
             return;
         }
         L.issue(a.w13, a.w13s, sl.expert[slot], tile, tiles, NW);
@@ -923,7 +930,7 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     }
     __syncthreads();
     gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
-    stamp_end(a.stamp);
+    stamp_end<STAMP>(a.stamp);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -953,9 +960,9 @@ struct K3Args {
 // the waves, R = 64 / KSUB units per wave and group, KSUB lanes per unit (ITERS blocks of 32 each),
 // UPW groups per wave.  Each unit's routing-weighted result goes to LDS and the epilogue sums a
 // row's units in slot order.  h vectors are indexed by their row t*(k+S) + r (r = k: shared).
-template <int KSUB, int ITERS, int T, int UPW>
+template <int KSUB, int ITERS, int T, int UPW, bool STAMP = false>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
-    stamp_start(a.stamp);
+    stamp_start<STAMP>(a.stamp);
     constexpr int R = kWave / KSUB;  // units per wave and group; rows per repacked tile
     constexpr bool CODES = T >= 3;   // FP8 h codes from the requantisation kernel
     constexpr int MAXP = CODES ? 1 : T == 1 ? 5 : 9;  // h columns (rows of h) per thread, loaded up front
@@ -1160,7 +1167,7 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
         if (a.y) a.y[o] = ysum;
         if (a.xnext) a.xnext[o] = f32_to_bf16(bf16_to_f32(idx == tid ? xr_pre : a.xres[o]) + ysum);
     }
-    stamp_end(a.stamp);
+    stamp_end<STAMP>(a.stamp);
 }
 
 }  // namespace moe

@@ -183,10 +183,10 @@ int layer_grid(const Shape& sh, int T, int kind) {
 bool jit_kernel_names(const Shape& sh, int T, std::string (&names)[kLayerKernels]) {
     if (T < 1 || T > kMaxTokens || !shape_supported(sh)) return false;
     const std::string t = std::to_string(T), bpl = std::to_string(sh.bpl());
-    names[kKernInput] = T >= 3 ? "moe::k0_input" : "";
+    names[kKernInput] = T >= 3 ? "moe::k0_input<false>" : "";
     names[kKernRouter] = "moe::k1_router<" + t + ", " + bpl + ">";
     names[kKernGateup] = "moe::k2_gateup<" + t + ", " + bpl + ", " + std::to_string(gateup_wt(sh, T)) + ">";
-    names[kKernRequant] = T >= 3 ? "moe::kq_requant" : "";
+    names[kKernRequant] = T >= 3 ? "moe::kq_requant<false>" : "";
     names[kKernDown] = "moe::k3_down<" + std::to_string(sh.ksub()) + ", " + std::to_string(sh.iters()) + ", " + t +
                        ", " + std::to_string(down_two_per_cu(sh, T) ? 2 : T) + ">";
     return true;
@@ -217,7 +217,7 @@ static hipError_t launch(Kern kern, hipFunction_t jf, unsigned grid, unsigned bl
         if (e_ != hipSuccess) return e_;    \
     } while (0)
 
-template <int T, int BPL, int KSUB, int ITERS>
+template <int T, int BPL, int KSUB, int ITERS, bool STAMP>
 static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev, const JitKernels* jit) {
     const int GW = sh.gw(), tiles = sh.gu_tiles(), R = sh.down_rows();
@@ -227,7 +227,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     if (CENTRAL) {
         K0Args a0{P.x, P.xn, P.xq, P.xs, P.trace, P.x_scale, P.x_codes, sh.H, normalize ? 1 : 0};
         a0.stamp = P.stamp[kKernInput];
-        MOE_TRY(launch(k0_input, jf(kKernInput), T, 1024, (size_t)sh.H * 2, stream, evk(kKernInput), a0));
+        MOE_TRY(launch(k0_input<STAMP>, jf(kKernInput), T, 1024, (size_t)sh.H * 2, stream, evk(kKernInput), a0));
     }
     const int n_router_wg = (sh.E + GW - 1) / GW;
     const int n_sh1 = CENTRAL ? sh.S * tiles : 0;  // shared gate/up tiles in the router kernel
@@ -236,7 +236,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
               CENTRAL ? P.ids : nullptr, CENTRAL ? P.w : nullptr, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h,
               P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
     a1.stamp = P.stamp[kKernRouter];
-    MOE_TRY(launch(k1_router<T, BPL>, jf(kKernRouter), n_router_wg + n_sh1, 64 * GW, (size_t)T * sh.H * 2, stream,
+    MOE_TRY(launch(k1_router<T, BPL, STAMP>, jf(kKernRouter), n_router_wg + n_sh1, 64 * GW, (size_t)T * sh.H * 2, stream,
                    evk(kKernRouter), a1));
 
     const int n_sh_wg = CENTRAL ? 0 : sh.S * tiles;  // 1-2 tokens: shared gate/up tiles here
@@ -247,16 +247,16 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     const size_t lds2 = (size_t)T * sh.H * 2;
     constexpr int WT = T == 1 ? 4 : T == 2 ? 2 : 1;
     if (gateup_wt(sh, T) == WT)
-        MOE_TRY(launch(k2_gateup<T, BPL, WT>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
+        MOE_TRY(launch(k2_gateup<T, BPL, WT, STAMP>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
                        evk(kKernGateup), a2));
     else
-        MOE_TRY(launch(k2_gateup<T, BPL, 1>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
+        MOE_TRY(launch(k2_gateup<T, BPL, 1, STAMP>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
                        evk(kKernGateup), a2));
 
     if (CENTRAL) {
         KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
         aq.stamp = P.stamp[kKernRequant];
-        MOE_TRY(launch(kq_requant, jf(kKernRequant), sh.pairs(T), 256, 0, stream, evk(kKernRequant), aq));
+        MOE_TRY(launch(kq_requant<STAMP>, jf(kKernRequant), sh.pairs(T), 256, 0, stream, evk(kKernRequant), aq));
     }
     // down: one workgroup per CU-sized share of the rows (or two per CU, above); (slot, row) units
     // spread over up to 12 waves, UPW groups of 64 / KSUB units per wave
@@ -271,23 +271,32 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     a3.stamp = P.stamp[kKernDown];
     const size_t lds3 = (size_t)sh.pairs(T) * sh.I * 2 + (size_t)units_max * T * 4;
     if (two_per_cu)
-        MOE_TRY(launch(k3_down<KSUB, ITERS, T, 2>, jf(kKernDown), dgrid, 64 * nw, lds3, stream, evk(kKernDown),
+        MOE_TRY(launch(k3_down<KSUB, ITERS, T, 2, STAMP>, jf(kKernDown), dgrid, 64 * nw, lds3, stream, evk(kKernDown),
                        a3));
     else
-        MOE_TRY(launch(k3_down<KSUB, ITERS, T, T>, jf(kKernDown), dgrid, 64 * nw, lds3, stream, evk(kKernDown),
+        MOE_TRY(launch(k3_down<KSUB, ITERS, T, T, STAMP>, jf(kKernDown), dgrid, 64 * nw, lds3, stream, evk(kKernDown),
                        a3));
     return hipSuccess;
 }
 
+template <int T, int BPL, bool STAMP>
+static hipError_t launch_layer_s(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                                 hipStream_t stream, hipEvent_t* ev, const JitKernels* jit) {
+    const int ks = sh.ksub(), it = sh.iters();
+    if (ks == 8 && it == 3) return launch_layer_t<T, BPL, 8, 3, STAMP>(sh, L, P, normalize, stream, ev, jit);
+    if (ks == 8 && it == 1) return launch_layer_t<T, BPL, 8, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
+    if (ks == 4 && it == 1) return launch_layer_t<T, BPL, 4, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
+    if (ks == 2 && it == 1) return launch_layer_t<T, BPL, 2, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
+    return hipErrorInvalidValue;
+}
+
+// The stamped instances (timing record, mode 1) are the ahead-of-time ones: the run-time compiled
+// module holds only the instances of normal runs.
 template <int T, int BPL>
 static hipError_t launch_layer_b(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev, const JitKernels* jit) {
-    const int ks = sh.ksub(), it = sh.iters();
-    if (ks == 8 && it == 3) return launch_layer_t<T, BPL, 8, 3>(sh, L, P, normalize, stream, ev, jit);
-    if (ks == 8 && it == 1) return launch_layer_t<T, BPL, 8, 1>(sh, L, P, normalize, stream, ev, jit);
-    if (ks == 4 && it == 1) return launch_layer_t<T, BPL, 4, 1>(sh, L, P, normalize, stream, ev, jit);
-    if (ks == 2 && it == 1) return launch_layer_t<T, BPL, 2, 1>(sh, L, P, normalize, stream, ev, jit);
-    return hipErrorInvalidValue;
+    if (P.stamp[kKernRouter]) return launch_layer_s<T, BPL, true>(sh, L, P, normalize, stream, ev, nullptr);
+    return launch_layer_s<T, BPL, false>(sh, L, P, normalize, stream, ev, jit);
 }
 
 template <int T>

@@ -263,3 +263,29 @@ def test_binding_derives_dtype_tags_from_tensors(flash_t1):
     with pytest.raises(moe.MoeError) as ei:
         moe.fp8_head_create((w_bytes, moe._dtype_tag(w_bf16, moe.DT_E4M3)), scales)
     assert ei.value.status == -3
+
+
+def test_graph_replay_timing_record(flash_t1):
+    """Timing mode 1 (graph replays with per-workgroup wall-clock stamps): one span per kernel and
+    layer of every recorded run, gaps for every kernel after the first, and the record's spans and
+    gaps add up to no more than the wall time of the runs; the outputs are unchanged."""
+    shape, lay, h, m = flash_t1
+    x = synth.tokens(shape.hidden, m["seed"], 1, m["x_attempt"])
+    ref = run_layer(h, shape, x)
+    moe.moe_decode_timing_enable(h, 3, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        got = run_layer(h, shape, x)
+    e1.record()
+    torch.cuda.synchronize()
+    t = moe.moe_decode_timing_read(h)
+    moe.moe_decode_timing_enable(h, 0)
+    assert t["mode"] == 1 and t["runs"] == 3
+    for c in ("router", "gateup", "down"):
+        assert t[c]["launches"] == 3 and t[c]["total_ms"] > 0, (c, t[c])
+    assert t["router"]["gap_launches"] == 0 and t["gateup"]["gap_launches"] == 3 and t["down"]["gap_launches"] == 3
+    assert t["input"]["launches"] == 0 and t["requant"]["launches"] == 0
+    recorded = sum(t[c]["total_ms"] + t[c]["gap_ms"] for c in moe.TIMING_CLASSES)
+    assert 0 < recorded <= e0.elapsed_time(e1)
+    assert (got["y"] == ref["y"]).all()
