@@ -325,13 +325,18 @@ def main():
 
 
 COPY_PROBE_BYTES = 256 << 20
-KERNEL_SOURCE = os.path.join(ROOT, "mxfp4_expert_gemv_amd", "csrc", "moe_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "mxfp4_expert_gemv_amd", "csrc", f)
+                  for f in ("moe_kernels.hip", "moe_kernels.h", "moe_device.h", "moe_layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_stack_t1.md")
 
 
 def source_digest():
+    """Digest of the MoE kernels' device sources (the .hip file and the headers it compiles)."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    d = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        d.update(os.path.basename(f).encode() + b"\0" + open(f, "rb").read())
+    return d.hexdigest()[:16]
 
 
 def measured_traffic(kernel):
@@ -428,15 +433,16 @@ def kernel_bytes(shape, T, distinct):
 
 
 def kernel_names(variant, T):
-    """Full names of the kernels as the profiler lists them, from the library's variant string
-    (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-...)."""
-    gu, dn = variant.split("-")[2:4]
+    """Full names of the kernels of a 1-2 token layer as the profiler lists them, from the library's
+    variant string (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-<launch>[-jit][-mfma])."""
+    parts = variant.split("-")
+    gu, dn = parts[2:4]
     bpl = int(gu[2:].split("x")[1])
     ksub, iters = (int(v) for v in dn[2:].split("x"))
-    spw = 1 if T == 1 else 2 if T == 2 else 4
-    return {"router": f"void moe::k1_router<{T}, {bpl}>(moe::K1Args)",
-            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {4 if T == 1 else 2 if T == 2 else 1}>(moe::K2Args)",
-            "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {spw}>(moe::K3Args)"}
+    mf = "true" if "mfma" in parts[4:] else "false"
+    return {"router": f"void moe::k1_router<{T}, {bpl}, {mf}, false>(moe::K1Args)",
+            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {4 if T == 1 else 2}, {mf}, false>(moe::K2Args)",
+            "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {T}, false>(moe::K3Args)"}
 
 
 def time_head(moe, dev, stream, steps=50, warmup=5):

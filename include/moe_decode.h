@@ -89,6 +89,18 @@ typedef enum {
                                     and a digest of source, options and kernels; a later create with the
                                     same key loads it.  A failed compile makes create fail (MOE_ERR_HIP);
                                     nothing falls back to the ahead-of-time kernels. */
+#define MOE_F_MFMA 0x10u         /* gate/up dot products on the matrix cores: per MX block (32 K) one
+                                    v_mfma_f32_16x16x32_bf16 for the tile's 16 gate rows and one for its 16
+                                    up rows, the E2M1 weights times their E8M0 block scale converted
+                                    exactly to bf16, times the exact bf16 values of the E4M3 input codes,
+                                    fp32 accumulation (within 2.7 * 2^-24 * sum |terms| per instruction,
+                                    measured).  moe_decode_set_layer repacks the gate/up weights into that
+                                    instruction's operand layout (same bytes per layer).  Without it the
+                                    VALU form converts both to f16 and uses dot products.  The W4A8
+                                    product (tanhow.com, section "为什么 DGX Spark 上的 MoE 解码是内存受限
+                                    的"; devotd.net, section 2) is the same in both; measured on the
+                                    42-layer stack it is faster at 4 tokens (the verify step) and slower at
+                                    1, so it is a choice per handle, not the default. */
 
 typedef struct moe_decode_handle moe_decode_handle;
 typedef struct fp8_head_handle fp8_head_handle;

@@ -21,6 +21,7 @@ DT_BF16, DT_FP32, DT_E4M3, DT_E2M1X2, DT_E8M0 = 1, 2, 3, 4, 5
 F_RMSNORM_INPUT = 0x1
 F_DIRECT_LAUNCH = 0x2
 F_JIT = 0x8
+F_MFMA = 0x10
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",

@@ -8,11 +8,25 @@
 //
 // The same kernel also runs the unquantised BF16 head (bf16_head_create), for comparison.
 //
-// Layout (repacked at create): [ceil(V/64) tiles][row bytes/16 units][64 lanes][16 B], lane = row
-// within the 64-row tile, so each wave-wide 16-byte load reads 1 KiB of contiguous HBM.  Each
-// workgroup owns one 64-row tile; its waves split the K range, E4M3 pairs are converted exactly to
-// bf16 pairs in VGPRs and multiplied with bf16 x pairs from LDS by v_dot2_f32_bf16 (exact products,
-// fp32 accumulation).  The last workgroup to finish reduces the per-tile (max, index) pairs.
+// Each workgroup owns one 64-row tile and has H / 256 waves; wave w takes K [256 w, 256 w + 256) of
+// the tile's rows on the matrix cores: v_mfma_f32_16x16x32_bf16 on four 16-row groups, A = the
+// weights (E4M3 codes converted exactly to bf16 in VGPRs, or the bf16 weights themselves), B = x
+// (bf16, from LDS; column n = token n, zero columns past T), fp32 accumulators.  Measured on gfx950,
+// one such instruction is within 2.7 * 2^-24 * sum |terms| of the exact sum (C + 32 products), so
+// the logits stay inside the any-order fp32 summation bound the argmax margin rule is built on.
+// At one token 15 of the 16 B columns are zero; the instruction still beat a VALU dot product
+// (v_dot2_f32_bf16) on the same registers, which needs one dot per code and token.
+//
+// Layout (repacked at create): [ceil(V/64) tiles][H/256 waves][U units][64 lanes][16 B], each wave-
+// wide 16-byte load reading 1 KiB of contiguous HBM, in the order the blocks consume them.  Lane l,
+// unit u = 4 s + r covers row 16 r + l % 16 of the tile: E4M3 (U = 16, s < 4): K 256 w + 64 s +
+// 16 (l / 16) .. +16, whose two halves are the lane's A operands of MFMA blocks 2 s and 2 s + 1;
+// BF16 (U = 32, s < 8): K 256 w + 32 s + 8 (l / 16) .. +8, the A operand of block s.  The B operand
+// of block j for lane l is x at the same K offsets.  The last workgroup to finish reduces the
+// per-tile (max, index) pairs.
+//
+// fp8_head_run_noalloc runs the same kernel on the caller's row-major matrix, read at the same K
+// offsets, so that its logits equal the handle's bit for bit.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,19 +51,27 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// NU 16-byte units per row (H / 16 for E4M3 rows, H / 8 for bf16 rows); ssrc null: scales of 1.
+// Row-major [V][H] -> the tile layout above (a permutation of 16-byte units; rows past V are zero,
+// with scale 0).  NU 16-byte units per row: H / 16 (E4M3) or H / 8 (bf16); ssrc null: scales of 1.
 __global__ void repack_head(const uint4* __restrict__ src, const float* __restrict__ ssrc, uint4* __restrict__ dst,
                             float* __restrict__ sdst, int V, int NU, int VT) {
+    const int NW = NU / 16 / (ssrc ? 1 : 2);  // waves per tile (H / 256)
+    const int U = NU / NW;                   // units per lane and wave
     const uint64_t total = (uint64_t)VT * NU * kWave;
-    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
-         u += (uint64_t)gridDim.x * blockDim.x) {
-        const int lane = (int)(u % kWave);
-        const uint64_t r1 = u / kWave;
-        const int unit = (int)(r1 % NU);
-        const uint64_t vt = r1 / NU;
-        const uint64_t row = vt * kWave + lane;
-        dst[u] = row < (uint64_t)V ? src[row * NU + unit] : make_uint4(0, 0, 0, 0);
-        if (unit == 0) sdst[row] = row < (uint64_t)V ? (ssrc ? ssrc[row] : 1.0f) : 0.0f;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(i % kWave);
+        uint64_t r = i / kWave;
+        const int u = (int)(r % U);
+        r /= U;
+        const int w = (int)(r % NW);
+        const uint64_t vt = r / NW;
+        const uint64_t row = vt * kWave + 16 * (u % 4) + (lane & 15);
+        // first unit of the wave's K slice, plus the unit's step within it (4 units per 64 K of
+        // E4M3, 4 per 32 K of bf16), plus the lane's quarter
+        const int unit = w * U + 4 * (u / 4) + (lane >> 4);
+        dst[i] = row < (uint64_t)V ? src[row * NU + unit] : make_uint4(0, 0, 0, 0);
+        if (u < 4 && lane < 16 && w == 0) sdst[row] = row < (uint64_t)V ? (ssrc ? ssrc[row] : 1.0f) : 0.0f;
     }
 }
 
@@ -74,78 +96,13 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
     }
 }
 
-// FP8: rows of E4M3 codes (16 per 16-byte unit), converted exactly to bf16 pairs; otherwise rows of
-// bf16 (8 per unit), the unquantised head the FP8 one replaces (its scales are 1).  RM: the weights
-// are the caller's row-major [V][H] matrix instead of the repacked tiles (lane l of tile vt reads
-// row vt * 64 + l, rows past V repeat the last one and are left out of the argmax; scales [V]).
-template <int T, bool FP8, bool RM = false>
-__global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
-    constexpr int kUnit = FP8 ? 16 : 8;             // K elements per 16-byte unit
-    constexpr int kUnitsPerWave = kSlice / kUnit;
-    extern __shared__ uint32_t xs[];  // [T][H/2] bf16 pairs
-    __shared__ float red[10][T][kWave];
-    __shared__ int is_last;
+// The end of every head kernel: red[w][t][r] holds wave w's partial sum of row r of the tile for
+// token t.  Sums the waves, scales, writes the logits, takes the tile's (max, lowest index) per
+// token, and the last workgroup to arrive reduces the tiles' maxima (and the verify acceptance).
+template <int T>
+__device__ void head_finish(const HeadArgs& a, const float (*red)[T][kWave], int* is_last) {
     const int vt = blockIdx.x, VT = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    const int H = a.H, NU = H / kUnit, Hh = H / 2;
-
-    uint4 wr[kUnitsPerWave];
-    if constexpr (RM) {
-        const uint4* p = a.w + (size_t)min(vt * kWave + lane, a.V - 1) * NU + (size_t)wv * kUnitsPerWave;
-#pragma unroll
-        for (int i = 0; i < kUnitsPerWave; ++i) wr[i] = ld_nt(p + i);
-    } else {
-        const uint4* p = a.w + ((size_t)vt * NU + (size_t)wv * kUnitsPerWave) * kWave + lane;
-#pragma unroll
-        for (int i = 0; i < kUnitsPerWave; ++i) wr[i] = ld_nt(p + i * kWave);
-    }
-    for (int i = tid; i < T * Hh; i += blockDim.x) xs[i] = ((const uint32_t*)a.x)[i];
-    __syncthreads();
-
-    float acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kUnitsPerWave; ++i) {
-        const int pbase = (wv * kUnitsPerWave + i) * (kUnit / 2);
-        if constexpr (!FP8) {
-            uint4 xv[T];
-#pragma unroll
-            for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bf16x2_t wq = __builtin_bit_cast(bf16x2_t, comp(wr[i], q));
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wq, __builtin_bit_cast(bf16x2_t, comp(xv[t], q)), acc[t],
-                                                            false);
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint4 xv[T];
-#pragma unroll
-                for (int t = 0; t < T; ++t) xv[t] = *(const uint4*)(xs + t * Hh + pbase + 4 * h);
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const uint32_t wd = comp(wr[i], 2 * h + q);
-                    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, false);
-                    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd, 1.0f, true);
-#pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q)),
-                                                                acc[t], false);
-                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(
-                            hi, __builtin_bit_cast(bf16x2_t, comp(xv[t], 2 * q + 1)), acc[t], false);
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) red[wv][t][lane] = acc[t];
-    __syncthreads();
-
     for (int t = wv; t < T; t += NW) {
         float s = 0.0f;
         for (int w = 0; w < NW; ++w) s += red[w][t][lane];
@@ -171,9 +128,9 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tid == 0)
-        is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
+        *is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
     __syncthreads();
-    if (!is_last) return;
+    if (!*is_last) return;
     __shared__ int32_t am_s[T];
     for (int t = wv; t < T; t += NW) {
         float bv = -INFINITY;
@@ -198,6 +155,106 @@ __global__ __launch_bounds__(640) void head_kernel(HeadArgs a) {
         }
     }
     if (tid == 0) *a.ticket = 0u;
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 E4M3 codes (two dwords) -> the bf16 A operand of one MFMA block (exact).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, true);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Register use: the wave's weights stream through a ring of RS steps (4 units each, one per 16-row
+// group): the loads of step s + RS are issued as soon as step s has been consumed, so a lane holds
+// 4 RS units instead of all of its 16 (E4M3) or 32 (bf16).  Occupancy: E4M3 at most 80 VGPRs (6
+// waves per SIMD), bf16 at most 64 (8 waves), so that two 10-wave workgroups (3, 3, 2, 2 waves on
+// the four SIMDs) always share a compute unit; all 16 units in registers (96 VGPRs, 5 waves) made
+// the head a third slower.  Measured on the 157,184 x 2,560 head: E4M3 with 2 steps (77-79 VGPRs)
+// and bf16 with 1 step (59-61) were the fastest of 1-4 steps at 6 and 8 waves.  The row-major form
+// takes 1 step: with 2 its row addresses spilled to scratch.
+template <bool FP8, bool RM>
+constexpr int head_ring_steps() { return FP8 && !RM ? 2 : 1; }
+template <int T, bool FP8, bool RM = false>
+__global__ __launch_bounds__(640) __attribute__((amdgpu_waves_per_eu(FP8 ? 6 : 8))) void head_mfma(HeadArgs a) {
+    constexpr int U = FP8 ? 16 : 32;  // units per lane
+    constexpr int S = U / 4;          // steps
+    constexpr int RS = head_ring_steps<FP8, RM>();
+    extern __shared__ uint32_t xs[];  // [T][H/2] bf16 pairs
+    __shared__ float red[10][T][kWave];
+    __shared__ int is_last;
+    const int vt = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+    const int H = a.H, Hh = H / 2;
+
+    uint4 wr[4 * RS];
+    const uint4* p = RM ? a.w : a.w + ((size_t)vt * NW + wv) * U * kWave + lane;
+    // row-major: the lane's first unit in each 16-row group (a 32-bit unit index: the caller's
+    // matrix is at most MOE_NOALLOC_MAX_VOCAB x 2560 bytes)
+    uint32_t ru[4];
+    if constexpr (RM) {
+        static_assert(FP8, "row-major weights are E4M3");
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            ru[r] = (uint32_t)min(vt * kWave + 16 * r + (lane & 15), a.V - 1) * (uint32_t)(H / 16) + wv * U + (lane >> 4);
+    }
+    // step st: unit 4 st + r of the lane (16-row group r) into ring slot st % RS
+    auto issue = [&](int st) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (RM)
+                wr[(st % RS) * 4 + r] = ld_nt(p + (ru[r] + 4 * st));
+            else
+                wr[(st % RS) * 4 + r] = ld_nt(p + (4 * st + r) * kWave);
+        }
+    };
+#pragma unroll
+    for (int st = 0; st < RS; ++st) issue(st);
+    for (int i = tid; i < T * Hh; i += blockDim.x) xs[i] = ((const uint32_t*)a.x)[i];
+    __syncthreads();
+
+    const int n = lane & 15, g = lane >> 4;
+    const bool on = n < T;
+    const uint16_t* xrow = (const uint16_t*)xs + (on ? n : 0) * H + wv * 256;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+        // E4M3: the step's units hold blocks 2 st and 2 st + 1 (their low and high halves); bf16:
+        // block st
+#pragma unroll
+        for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
+            const int kofs = FP8 ? 64 * st + 16 * g + 8 * h : 32 * st + 8 * g;
+            uint4 xb = make_uint4(0, 0, 0, 0);
+            if (on) xb = *(const uint4*)(xrow + kofs);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint4& q = wr[(st % RS) * 4 + r];
+                bf16x8_t w;
+                if constexpr (FP8)
+                    w = h ? e4m3x8_to_bf16x8(q.z, q.w) : e4m3x8_to_bf16x8(q.x, q.y);
+                else
+                    w = __builtin_bit_cast(bf16x8_t, q);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, b, acc[r], 0, 0, 0);
+            }
+        }
+        if (st + RS < S) issue(st + RS);
+    }
+    // lane l holds rows 16 r + 4 (l / 16) + i of the tile for token l % 16
+    if (on) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wv][n][16 * r + 4 * g + i] = acc[r][i];
+    }
+    __syncthreads();
+    head_finish<T>(a, red, &is_last);
 }
 
 // Per-row FP8 quantisation of the head at load time (the step the pages put before the FP8 head):
@@ -282,10 +339,10 @@ static hipError_t launch_head_t(const HeadArgs& a, int T, int VT, hipStream_t st
     const unsigned block = kWave * (a.H / kSlice);
     const size_t lds = (size_t)T * a.H * 2;
     switch (T) {
-        case 1: head_kernel<1, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 2: head_kernel<2, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 3: head_kernel<3, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 4: head_kernel<4, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 1: head_mfma<1, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 2: head_mfma<2, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 3: head_mfma<3, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 4: head_mfma<4, FP8, RM><<<VT, block, lds, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

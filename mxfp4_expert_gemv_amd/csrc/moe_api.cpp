@@ -132,7 +132,7 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->inter % moe::kBlock || !moe::shape_supported(sh))
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
                     c->hidden, c->inter);
-    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_JIT))
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_JIT | MOE_F_MFMA))
         return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
@@ -234,7 +234,8 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
     h->hq = h->ws + o_hq;
     h->hs = (float*)(h->ws + o_hs);
     if (cfg->flags & MOE_F_JIT) {
-        s = moe::jit_build(sh, cfg->max_tokens, (cfg->flags & MOE_F_RMSNORM_INPUT) != 0, &h->jit);
+        s = moe::jit_build(sh, cfg->max_tokens, (cfg->flags & MOE_F_RMSNORM_INPUT) != 0,
+                           (cfg->flags & MOE_F_MFMA) != 0, &h->jit);
         if (s != MOE_OK) {
             free_handle(h);
             return s;
@@ -269,7 +270,7 @@ extern "C" moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, 
     uint8_t* m = h->layer_mem[layer];
     hipError_t e = moe::launch_repack(h->sh, d->router.ptr, d->w13.ptr, d->w13_s.ptr, d->w2.ptr, d->w2_s.ptr, m,
                                       m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s,
-                                      (hipStream_t)stream);
+                                      (h->cfg.flags & MOE_F_MFMA) != 0, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "repack launch failed: %s", hipGetErrorString(e));
     h->layer_set[layer] = 1;
     return MOE_OK;
@@ -289,7 +290,8 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
     const size_t TH = (size_t)T * sh.H;
     for (int l = 0; l < L; ++l) {
         const uint8_t* m = h->layer_mem[l];
-        moe::LayerPtrs lp{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s};
+        moe::LayerPtrs lp{m, m + h->off_w13, m + h->off_w13s, m + h->off_w2, m + h->off_w2s,
+                          (h->cfg.flags & MOE_F_MFMA) != 0};
         moe::RunPtrs p{};
         p.x = l == 0 ? (const uint16_t*)x : h->xbuf[l & 1];
         const bool last = l == L - 1;
@@ -507,8 +509,9 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
         return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
     const Shape& sh = h->sh;
     memset(info->variant, 0, sizeof info->variant);
-    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s%s", sh.gw(), sh.bpl(), sh.ksub(),
-             sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph", h->jit_on ? "-jit" : "");
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s%s%s", sh.gw(), sh.bpl(), sh.ksub(),
+             sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph", h->jit_on ? "-jit" : "",
+             (h->cfg.flags & MOE_F_MFMA) ? "-mfma" : "");
     info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
     info->workspace_bytes = h->ws_bytes;
     const uint64_t expert = sh.w13_bytes_per_expert() + sh.w13s_bytes_per_expert() + sh.w2_bytes_per_expert() +

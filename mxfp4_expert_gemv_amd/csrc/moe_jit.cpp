@@ -78,7 +78,7 @@ static bool write_file(const std::string& path, const std::string& data) {
     return rename(tmp.c_str(), path.c_str()) == 0;
 }
 
-moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, JitResult* out) {
+moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, bool mfma, JitResult* out) {
     *out = JitResult{};
     int dev = 0;
     hipDeviceProp_t prop;
@@ -89,7 +89,7 @@ moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, JitResult*
     std::vector<std::string> exprs;
     std::string names[kMaxTokens][kLayerKernels];
     for (int T = 1; T <= max_tokens; ++T) {
-        if (!jit_kernel_names(sh, T, names[T - 1])) return moe_fail(MOE_ERR_UNSUPPORTED, "no kernels for this shape");
+        if (!jit_kernel_names(sh, T, mfma, names[T - 1])) return moe_fail(MOE_ERR_UNSUPPORTED, "no kernels for this shape");
         for (const std::string& n : names[T - 1])
             if (!n.empty() && std::find(exprs.begin(), exprs.end(), n) == exprs.end()) exprs.push_back(n);
     }
@@ -107,8 +107,8 @@ moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, JitResult*
     for (char& c : arch_tag)
         if (c == ':' || c == '+' || c == '/') c = c == '+' ? 'p' : '_';
     char base[256];
-    snprintf(base, sizeof base, "moe_h%d_e%d_k%d_s%d_i%d_n%d_t%d_%s_%016llx", sh.H, sh.E, sh.k, sh.S, sh.I,
-             normalize ? 1 : 0, max_tokens, arch_tag.c_str(), (unsigned long long)key);
+    snprintf(base, sizeof base, "moe_h%d_e%d_k%d_s%d_i%d_n%d_t%d%s_%s_%016llx", sh.H, sh.E, sh.k, sh.S, sh.I,
+             normalize ? 1 : 0, max_tokens, mfma ? "_mf" : "", arch_tag.c_str(), (unsigned long long)key);
     const std::string dir = jit_cache_dir();
     const std::string co_path = dir + "/" + base + ".co", names_path = dir + "/" + base + ".names";
     snprintf(out->path, sizeof out->path, "%s", co_path.c_str());

@@ -23,7 +23,7 @@ struct JitResult {
 std::string jit_cache_dir();
 // Compiles (or loads from the cache) the kernels of every token count 1..max_tokens for this shape
 // on the current device; on failure returns an error status with the message in moe_last_error().
-moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, JitResult* out);
+moe_status jit_build(const Shape& sh, int max_tokens, bool normalize, bool mfma, JitResult* out);
 void jit_release(JitResult* r);
 
 }  // namespace moe

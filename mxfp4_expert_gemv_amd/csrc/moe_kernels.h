@@ -268,24 +268,133 @@ template <int BPL>
 struct GuLoads {
     uint4 w[BPL];
     ScaleBytes<BPL> s;
-    // expert e, tile `tile` of `tiles`, this wave's BPL steps
+    uint4 sm[BPL / 4];  // MF: the scale bytes of the lane's gate row, then of its up row (4 BPL)
+    // expert e, tile `tile` of `tiles`, this wave's BPL steps; MF: the matrix-core layout, whose
+    // scale bytes are shared by the four lanes of a row (one address, one fetch)
+    template <bool MF = false>
     __device__ void issue(const uint4* w13, const uint8_t* w13s, int e, int tile, int tiles, int GW) {
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const size_t base = (((size_t)e * tiles + tile) * GW + wv);
         const uint4* p = w13 + base * BPL * kWave + lane;
 #pragma unroll
         for (int i = 0; i < BPL; ++i) w[i] = ld_nt(p + i * kWave);
-        s.load(w13s + (base * kWave + lane) * BPL);
+        if constexpr (MF) {
+            const uint4* q = (const uint4*)(w13s + (base * 16 + (lane & 15)) * (4 * BPL));
+#pragma unroll
+            for (int i = 0; i < BPL / 4; ++i) sm[i] = ld_nt(q + i);
+        } else {
+            s.load(w13s + (base * kWave + lane) * BPL);
+        }
     }
 };
 
-// The gate/up tile of one expert: 16 gate + 16 up rows over all H, for the nt tokens tok[j] (their
-// h goes to pair pair[j]); sx: LDS scales per token.  red: LDS [kMaxWaves][T][32].
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 E2M1 codes (a dword, even element in the low nibble of each byte) times the block scale ->
+// the bf16 A operand of one MFMA block.  v_cvt_scalef32_pk_bf16_fp4 takes the scale as the
+// exponent field of an f32 operand, read as E8M0 (mantissa and sign ignored: 0 is 2^-127, 255 is
+// NaN), so the operand is the scale byte shifted into that field.  The result is code x scale
+// exactly for every E8M0 byte: bf16 has the fp32 exponent range (0.5 x 2^-127 is a bf16
+// subnormal, 6 x 2^127 overflows to inf as in fp32; measured for all 16 codes).
+__device__ __forceinline__ bf16x8_t e2m1x8_to_bf16x8(uint32_t d, uint32_t scale_byte) {
+    const float scale = __uint_as_float(scale_byte << 23);
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 8 E4M3 codes (two dwords) -> 8 bf16 (exact).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, true)));
+}
+
+template <int BPL>
+__device__ __forceinline__ uint32_t scale_byte(const GuLoads<BPL>& L, int k) {
+    const uint4& v = L.sm[k >> 4];
+    const uint32_t d = (k & 15) < 4 ? v.x : (k & 15) < 8 ? v.y : (k & 15) < 12 ? v.z : v.w;
+    return (d >> (8 * (k & 3))) & 0xffu;
+}
+
+// Matrix-core form of the gate/up dot products (weights repacked for it, MOE_F_MFMA): each of the
+// wave's 2 BPL MX blocks is one v_mfma_f32_16x16x32_bf16 for the 16 gate rows and one for the 16
+// up rows of the tile.  A: lane l holds row l % 16 and K 8 (l / 16) .. +8 of the block (a dword of
+// its units: gate units 0 .. BPL/2-1, up units after them, four blocks per unit), converted with
+// the block scale; B: column n = l % 16 is the expert's n-th token (zero columns past its tokens),
+// the same K from xb (LDS, [T][H] bf16 of the input's E4M3 codes).  The per-token fp32 scale is
+// applied afterwards, as in the VALU form.  Measured on gfx950, one such instruction is within
+// 2.7 * 2^-24 * sum |terms| of the exact C + 32 products: the accuracy of fp32 accumulation.  The
+// tile's partial sums go to red in the VALU form's layout.
 template <int T, int BPL>
-__device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, const float* sx, int nt,
+__device__ void gateup_dot_mfma(const GuLoads<BPL>& L, const uint16_t* xb, int H, int nt, const int (&tok)[T],
+                                float* red) {
+    constexpr int BW = 2 * BPL;  // MX blocks per wave
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+    int tk = 0;
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+        if (n == j) tk = tok[j];
+    const bool on = n < nt;
+    const uint16_t* xr = xb + (size_t)tk * H + wv * BW * kBlock + 8 * g;
+    // one accumulator per matrix: two (shorter chains) took 76 VGPRs, one wave less per SIMD, and
+    // measured slower; capping registers at 64 spilled
+    f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < BW; ++j) {
+        uint4 xv = make_uint4(0, 0, 0, 0);
+        if (on) xv = *(const uint4*)(xr + j * kBlock);
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xv);
+        const uint4& wg = L.w[j >> 2];
+        const uint4& wu = L.w[BPL / 2 + (j >> 2)];
+        const uint32_t dg = (j & 3) == 0 ? wg.x : (j & 3) == 1 ? wg.y : (j & 3) == 2 ? wg.z : wg.w;
+        const uint32_t du = (j & 3) == 0 ? wu.x : (j & 3) == 1 ? wu.y : (j & 3) == 2 ? wu.z : wu.w;
+        const bf16x8_t ag = e2m1x8_to_bf16x8(dg, scale_byte(L, j));
+        const bf16x8_t au = e2m1x8_to_bf16x8(du, scale_byte(L, BW + j));
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, b, accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, b, accu, 0, 0, 0);
+    }
+    if (on) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            red[(wv * T + n) * kGuRows + 4 * g + i] = accg[i];
+            red[(wv * T + n) * kGuRows + kGuOut + 4 * g + i] = accu[i];
+        }
+    }
+}
+
+// LDS fill of the input's 8 E4M3 codes of thread slot i (bytes 8 i .. 8 i + 7 of token t's row):
+// f16 pairs [T][H/2] for the VALU form, bf16 [T][H] for the matrix-core form (MF).
+template <bool MF>
+__device__ __forceinline__ void store_codes(void* xact, int H, int t, int i, uint2 c) {
+    if constexpr (MF) {
+        *(uint4*)((uint16_t*)xact + (size_t)t * H + i * 8) = e4m3x8_to_bf16x8(c);
+    } else {
+        half2_t* o = (half2_t*)xact + t * (H / 2) + i * 4;
+        o[0] = e4m3x2_to_f16x2(c.x & 0xffffu);
+        o[1] = e4m3x2_to_f16x2(c.x >> 16);
+        o[2] = e4m3x2_to_f16x2(c.y & 0xffffu);
+        o[3] = e4m3x2_to_f16x2(c.y >> 16);
+    }
+}
+
+// The gate/up tile of one expert: 16 gate + 16 up rows over all H, for the nt tokens tok[j] (their
+// h goes to pair pair[j]); sx: LDS scales per token.  red: LDS [kMaxWaves][T][32].  xact: LDS
+// activations, f16 pairs [T][H/2] (VALU form) or bf16 [T][H] (MF, the matrix-core form).
+template <int T, int BPL, bool MF = false>
+__device__ void gateup_tile(const GuLoads<BPL>& L, const void* xact, int H, const float* sx, int nt,
                             const int (&tok)[T], const int (&pair)[T], int tile, int I, float* h, float* hamax,
                             float* red) {
     const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = nth >> 6, Hh = H / 2;
+    if constexpr (MF) {
+        gateup_dot_mfma<T, BPL>(L, (const uint16_t*)xact, H, nt, tok, red);
+    } else {
+    const half2_t* xh = (const half2_t*)xact;
     const int ks = lane & 1;
     float acc[T];
 #pragma unroll
@@ -309,6 +418,7 @@ __device__ void gateup_tile(const GuLoads<BPL>& L, const half2_t* xh, int H, con
     for (int j = 0; j < T; ++j) {
         acc[j] += xchg<0>(acc[j]);
         if (j < nt && ks == 0) red[(wv * T + j) * kGuRows + (lane >> 1)] = acc[j];
+    }
     }
     __syncthreads();
     const int tiles = I / kGuOut;
@@ -685,7 +795,7 @@ struct K1Args {
 // One expert row per wave: lane reads 16-byte units lane, lane + 64, ... of the row; bf16 x bf16
 // products in fp32 FMA, one logit per wave and token.  At 1-2 tokens every workgroup also
 // normalises the input and stores the FP8 codes of its share of it.
-template <int T, int BPL, bool STAMP = false>
+template <int T, int BPL, bool MF = false, bool STAMP = false>
 __global__ __launch_bounds__(320) void k1_router(K1Args a) {
     stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem1[];
@@ -705,7 +815,6 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
         if ((int)blockIdx.x >= a.n_router_wg) {  // the shared expert's gate/up tile, every token
             __shared__ float red[kMaxWaves * T * kGuRows];
             __shared__ float sx[T];
-            half2_t* xh = (half2_t*)smem1;  // [T][H/2] f16 values of the input's FP8 codes
             const int tiles = MOE_SHAPE(I, a.I) / kGuOut, tile = blockIdx.x - a.n_router_wg, NC = H / 8;
             uint2 xc[T];
             const int xi = min(tid, NC - 1) * 8;
@@ -713,18 +822,11 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
             for (int t = 0; t < T; ++t) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + xi);
             const float sxv = a.xs[tid < T ? tid : 0];
             GuLoads<BPL> L;
-            L.issue(a.w13, a.w13s, MOE_SHAPE(E, a.E), tile, tiles, NW);
+            L.template issue<MF>(a.w13, a.w13s, MOE_SHAPE(E, a.E), tile, tiles, NW);
             if (tid < T) sx[tid] = sxv;
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if (tid < NC) {
-                    half2_t* o = xh + t * (H / 2) + tid * 4;
-                    o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
-                    o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
-                    o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
-                    o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
-                }
-            }
+            for (int t = 0; t < T; ++t)
+                if (tid < NC) store_codes<MF>(smem1, H, t, tid, xc[t]);
             __syncthreads();
             int tok[T], pair[T];
 #pragma unroll
@@ -732,7 +834,8 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
                 tok[j] = j;
                 pair[j] = j * (MOE_SHAPE(K, a.k) + MOE_SHAPE(S, a.S)) + MOE_SHAPE(K, a.k);
             }
-            gateup_tile<T, BPL>(L, xh, H, sx, a.ntok, tok, pair, tile, MOE_SHAPE(I, a.I), a.h, a.hamax, red);
+            gateup_tile<T, BPL, MF>(L, smem1, H, sx, a.ntok, tok, pair, tile, MOE_SHAPE(I, a.I), a.h, a.hamax,
+                                    red);
             stamp_end<STAMP>(a.stamp);
             return;
         }
@@ -845,11 +948,11 @@ struct K2Args {
 // token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
 // tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
 // the weights.
-template <int T, int BPL, int W, bool STAMP = false>
+template <int T, int BPL, int W, bool MF = false, bool STAMP = false>
 __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem2[];
-    half2_t* xh = (half2_t*)smem2;  // [T][H/2] f16 values of the input's FP8 codes
+    // smem2: the input's FP8 codes as f16 pairs [T][H/2], or as bf16 [T][H] (MF)
     __shared__ float red[kMaxWaves * T * kGuRows];
     __shared__ float sx[T];
     __shared__ SlotTable st;
@@ -871,24 +974,17 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
     float lgv[8 / W];
     if constexpr (ROUTE) route_issue<T, W>(a.logits, MOE_SHAPE(E, a.E), lgv);  // shared workgroups load them too: exact waits below
 
-    // f16 values of the codes into LDS while the logits are in flight
+    // the codes' f16 (bf16) values into LDS while the logits are in flight
     if (tid < T) sx[tid] = sxv;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        if (tid < NC) {
-            half2_t* o = xh + t * (H / 2) + tid * 4;
-            o[0] = e4m3x2_to_f16x2(xc[t].x & 0xffffu);
-            o[1] = e4m3x2_to_f16x2(xc[t].x >> 16);
-            o[2] = e4m3x2_to_f16x2(xc[t].y & 0xffffu);
-            o[3] = e4m3x2_to_f16x2(xc[t].y >> 16);
-        }
-    }
+    for (int t = 0; t < T; ++t)
+        if (tid < NC) store_codes<MF>(smem2, H, t, tid, xc[t]);
 
     GuLoads<BPL> L;
     int tok[T], pair[T], nt, tile;
     if (is_shared) {
         tile = blockIdx.x;
-        L.issue(a.w13, a.w13s, MOE_SHAPE(E, a.E), blockIdx.x, tiles, NW);
+        L.template issue<MF>(a.w13, a.w13s, MOE_SHAPE(E, a.E), blockIdx.x, tiles, NW);
         nt = a.ntok;
 #pragma unroll
         for (int j = 0; j < T; ++j) {
@@ -919,7 +1015,7 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
                 if (threadIdx.x == 0) a.stamp[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
             return;
         }
-        L.issue(a.w13, a.w13s, sl.expert[slot], tile, tiles, NW);
+        L.template issue<MF>(a.w13, a.w13s, sl.expert[slot], tile, tiles, NW);
         nt = sl.ntok[slot];
 #pragma unroll
         for (int j = 0; j < T; ++j) {
@@ -929,7 +1025,7 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
         }
     }
     __syncthreads();
-    gateup_tile<T, BPL>(L, xh, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
+    gateup_tile<T, BPL, MF>(L, smem2, H, sx, nt, tok, pair, tile, I, a.h, a.hamax, red);
     stamp_end<STAMP>(a.stamp);
 }
 

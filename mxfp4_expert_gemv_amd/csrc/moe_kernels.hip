@@ -85,6 +85,54 @@ __global__ void repack_w13s(const uint8_t* __restrict__ src, uint8_t* __restrict
     }
 }
 
+// Matrix-core layout (MOE_F_MFMA).  w13: the same [E+S][I/16][GW][BPL][64 lanes][16 B] units, but
+// unit `step` of lane l holds, in dword q, the 8 codes of row (step < BPL/2 ? gate : up) row
+// 16 tile + l % 16, block w 2 BPL + 4 (step % (BPL/2)) + q, K 8 (l / 16) .. +8 (bytes 4 (l / 16)
+// .. +4 of that block): a permutation of dwords.  w13_s: [E+S][I/16][GW][16 rows][4 BPL] bytes,
+// row r's gate scales of the wave's 2 BPL blocks, then its up scales (the four lanes of a row
+// read the same 4 BPL bytes).
+__global__ void repack_w13_mf(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int nexp, int I, int H,
+                              int bpl) {
+    const int NB = H / kBlock, GW = NB / (2 * bpl), tiles = I / kGuOut, RD = H / 8;  // dwords per row
+    const uint64_t total = (uint64_t)nexp * tiles * GW * bpl * kWave * 4;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+         u += (uint64_t)gridDim.x * blockDim.x) {
+        const int q = (int)(u % 4);
+        uint64_t r = u / 4;
+        const int lane = (int)(r % kWave);
+        r /= kWave;
+        const int step = (int)(r % bpl);
+        r /= bpl;
+        const int w = (int)(r % GW);
+        r /= GW;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        const int half = bpl / 2, gu = step / half;
+        const int row = gu * I + tile * kGuOut + (lane & 15);
+        const int blk = w * 2 * bpl + 4 * (step - gu * half) + q;
+        dst[u] = src[(e * 2 * I + row) * RD + blk * 4 + (lane >> 4)];
+    }
+}
+
+__global__ void repack_w13s_mf(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nexp, int I, int H,
+                               int bpl) {
+    const int NB = H / kBlock, BW = 2 * bpl, GW = NB / BW, tiles = I / kGuOut;
+    const uint64_t total = (uint64_t)nexp * tiles * GW * 16 * 2 * BW;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+         u += (uint64_t)gridDim.x * blockDim.x) {
+        const int k = (int)(u % (2 * BW));
+        uint64_t r = u / (2 * BW);
+        const int rr = (int)(r % 16);
+        r /= 16;
+        const int w = (int)(r % GW);
+        r /= GW;
+        const int tile = (int)(r % tiles);
+        const uint64_t e = r / tiles;
+        const int gu = k / BW, j = k - gu * BW;
+        dst[u] = src[(e * 2 * I + gu * I + tile * kGuOut + rr) * NB + w * BW + j];
+    }
+}
+
 __global__ void repack_w2(const uint4* __restrict__ src, uint4* __restrict__ dst, int nexp, int H, int I, int ksub) {
     const int NI = I / kBlock, R = kWave / ksub, iters = NI / ksub, tiles = H / R;
     const uint64_t total = (uint64_t)nexp * tiles * iters * kWave;
@@ -129,15 +177,22 @@ static unsigned grid_for(uint64_t total, unsigned block) {
 
 hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,
                          const void* w2s, void* d_router, void* d_w13, void* d_w13s, void* d_w2, void* d_w2s,
-                         hipStream_t stream) {
+                         bool mfma, hipStream_t stream) {
     const int nexp = sh.E + sh.S;
     const unsigned B = 256;
     hipError_t e = hipMemcpyAsync(d_router, router, sh.router_bytes(), hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return e;
-    repack_w13<<<grid_for((uint64_t)nexp * sh.I * sh.H / 16, B), B, 0, stream>>>((const uint4*)w13, (uint4*)d_w13,
-                                                                                  nexp, sh.I, sh.H, sh.bpl());
-    repack_w13s<<<grid_for((uint64_t)nexp * 2 * sh.I * sh.H / 32, B), B, 0, stream>>>(
-        (const uint8_t*)w13s, (uint8_t*)d_w13s, nexp, sh.I, sh.H, sh.bpl());
+    if (mfma) {
+        repack_w13_mf<<<grid_for((uint64_t)nexp * sh.I * sh.H / 4, B), B, 0, stream>>>(
+            (const uint32_t*)w13, (uint32_t*)d_w13, nexp, sh.I, sh.H, sh.bpl());
+        repack_w13s_mf<<<grid_for((uint64_t)nexp * 2 * sh.I * sh.H / 32, B), B, 0, stream>>>(
+            (const uint8_t*)w13s, (uint8_t*)d_w13s, nexp, sh.I, sh.H, sh.bpl());
+    } else {
+        repack_w13<<<grid_for((uint64_t)nexp * sh.I * sh.H / 16, B), B, 0, stream>>>(
+            (const uint4*)w13, (uint4*)d_w13, nexp, sh.I, sh.H, sh.bpl());
+        repack_w13s<<<grid_for((uint64_t)nexp * 2 * sh.I * sh.H / 32, B), B, 0, stream>>>(
+            (const uint8_t*)w13s, (uint8_t*)d_w13s, nexp, sh.I, sh.H, sh.bpl());
+    }
     repack_w2<<<grid_for((uint64_t)nexp * sh.H * sh.I / 32, B), B, 0, stream>>>(
         (const uint4*)w2, (uint4*)d_w2, nexp, sh.H, sh.I, sh.ksub());
     repack_w2s<<<grid_for((uint64_t)nexp * sh.H * sh.I / 32, B), B, 0, stream>>>(
@@ -180,12 +235,13 @@ int layer_grid(const Shape& sh, int T, int kind) {
     }
 }
 
-bool jit_kernel_names(const Shape& sh, int T, std::string (&names)[kLayerKernels]) {
+bool jit_kernel_names(const Shape& sh, int T, bool mfma, std::string (&names)[kLayerKernels]) {
     if (T < 1 || T > kMaxTokens || !shape_supported(sh)) return false;
-    const std::string t = std::to_string(T), bpl = std::to_string(sh.bpl());
+    const std::string t = std::to_string(T), bpl = std::to_string(sh.bpl()), mf = mfma ? "true" : "false";
     names[kKernInput] = T >= 3 ? "moe::k0_input<false>" : "";
-    names[kKernRouter] = "moe::k1_router<" + t + ", " + bpl + ">";
-    names[kKernGateup] = "moe::k2_gateup<" + t + ", " + bpl + ", " + std::to_string(gateup_wt(sh, T)) + ">";
+    names[kKernRouter] = "moe::k1_router<" + t + ", " + bpl + ", " + mf + ">";
+    names[kKernGateup] =
+        "moe::k2_gateup<" + t + ", " + bpl + ", " + std::to_string(gateup_wt(sh, T)) + ", " + mf + ">";
     names[kKernRequant] = T >= 3 ? "moe::kq_requant<false>" : "";
     names[kKernDown] = "moe::k3_down<" + std::to_string(sh.ksub()) + ", " + std::to_string(sh.iters()) + ", " + t +
                        ", " + std::to_string(down_two_per_cu(sh, T) ? 2 : T) + ">";
@@ -236,8 +292,13 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
               CENTRAL ? P.ids : nullptr, CENTRAL ? P.w : nullptr, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h,
               P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
     a1.stamp = P.stamp[kKernRouter];
-    MOE_TRY(launch(k1_router<T, BPL, STAMP>, jf(kKernRouter), n_router_wg + n_sh1, 64 * GW, (size_t)T * sh.H * 2, stream,
-                   evk(kKernRouter), a1));
+    const size_t lds1 = (size_t)T * sh.H * 2;
+    if (L.w13_mfma)
+        MOE_TRY(launch(k1_router<T, BPL, true, STAMP>, jf(kKernRouter), n_router_wg + n_sh1, 64 * GW, lds1, stream,
+                       evk(kKernRouter), a1));
+    else
+        MOE_TRY(launch(k1_router<T, BPL, false, STAMP>, jf(kKernRouter), n_router_wg + n_sh1, 64 * GW, lds1, stream,
+                       evk(kKernRouter), a1));
 
     const int n_sh_wg = CENTRAL ? 0 : sh.S * tiles;  // 1-2 tokens: shared gate/up tiles here
     const int n_gu_wg = routed_slots_max(sh, T) * tiles;
@@ -246,11 +307,19 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     a2.stamp = P.stamp[kKernGateup];
     const size_t lds2 = (size_t)T * sh.H * 2;
     constexpr int WT = T == 1 ? 4 : T == 2 ? 2 : 1;
-    if (gateup_wt(sh, T) == WT)
-        MOE_TRY(launch(k2_gateup<T, BPL, WT, STAMP>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
+    const int n2 = n_sh_wg + n_gu_wg;
+    const bool wt = gateup_wt(sh, T) == WT;
+    if (L.w13_mfma && wt)
+        MOE_TRY(launch(k2_gateup<T, BPL, WT, true, STAMP>, jf(kKernGateup), n2, 64 * GW, lds2, stream,
+                       evk(kKernGateup), a2));
+    else if (L.w13_mfma)
+        MOE_TRY(launch(k2_gateup<T, BPL, 1, true, STAMP>, jf(kKernGateup), n2, 64 * GW, lds2, stream,
+                       evk(kKernGateup), a2));
+    else if (wt)
+        MOE_TRY(launch(k2_gateup<T, BPL, WT, false, STAMP>, jf(kKernGateup), n2, 64 * GW, lds2, stream,
                        evk(kKernGateup), a2));
     else
-        MOE_TRY(launch(k2_gateup<T, BPL, 1, STAMP>, jf(kKernGateup), n_sh_wg + n_gu_wg, 64 * GW, lds2, stream,
+        MOE_TRY(launch(k2_gateup<T, BPL, 1, false, STAMP>, jf(kKernGateup), n2, 64 * GW, lds2, stream,
                        evk(kKernGateup), a2));
 
     if (CENTRAL) {

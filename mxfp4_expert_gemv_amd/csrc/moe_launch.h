@@ -12,6 +12,7 @@ namespace moe {
 
 struct LayerPtrs {
     const void *router, *w13, *w13s, *w2, *w2s;  // repacked tensors of one layer
+    bool w13_mfma;                               // w13 / w13s in the scaled-MFMA operand layout
 };
 
 struct RunPtrs {
@@ -51,7 +52,7 @@ struct JitKernels {
 
 hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, const void* w13s, const void* w2,
                          const void* w2s, void* d_router, void* d_w13, void* d_w13s, void* d_w2, void* d_w2s,
-                         hipStream_t stream);
+                         bool mfma, hipStream_t stream);
 // ev (nullable) = 4 events recorded before the router and after each of the three kernels.
 // jit: run-time compiled kernels to launch instead of the ahead-of-time ones, or null.
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
@@ -61,7 +62,7 @@ int layer_grid(const Shape& sh, int T, int kind);
 hipError_t launch_clear_u64(unsigned long long* p, uint64_t n, hipStream_t stream);
 // Name expressions of the kernel instances a layer of this shape launches at T tokens ("" for kinds
 // it does not launch); false for an unsupported shape or token count.
-bool jit_kernel_names(const Shape& sh, int T, std::string (&names)[kLayerKernels]);
+bool jit_kernel_names(const Shape& sh, int T, bool mfma, std::string (&names)[kLayerKernels]);
 bool shape_supported(const Shape& sh);
 
 }  // namespace moe

@@ -159,6 +159,24 @@ def tokens_correlated(hidden: int, seed: int, T: int, rho: float, attempt: int =
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+def tokens_wide_range(hidden: int, seed: int, T: int, attempt: int = 0) -> np.ndarray:
+    """bf16 bits [T][H] with a wide dynamic range inside every block of 32: one element of magnitude
+    4 (random position and sign) and 31 of magnitude in [0.12, 0.24] / 112 (random sign), so that
+    after per-token E4M3 quantisation (amax 4 -> 448, scale 1/112) every block holds one code of 448
+    and 31 codes between 2^-3 and 2^-2.  Random bytes come from the E2M1-code stream with the expert
+    coordinate 64 + t; magnitudes are rounded once to bf16 (nearest, ties to even)."""
+    out = np.empty((T, hidden), dtype=np.float32)
+    for t in range(T):
+        r = codes(2 * hidden, key(seed, 0, TENSOR_X, 64 + t, attempt)).astype(np.int64)
+        mag = (0.12 + 0.12 * r[:hidden] / 255.0) / 112.0
+        for b in range(hidden // 32):
+            mag[32 * b + (r[hidden + 32 * b] & 31)] = 4.0
+        sign = np.where(r[hidden:] & 1, -1.0, 1.0)
+        out[t] = (sign * mag).astype(np.float32)
+    u = out.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def expert(shape: Shape, seed: int, layer: int, e: int) -> dict:
     """Canonical MXFP4 tensors of expert e (index num_experts is the shared expert).
 

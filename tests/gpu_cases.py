@@ -64,9 +64,10 @@ class DeviceLayer:
         return {e: synth.expert(self.shape, self.seed, self.layer, e) for e in used}
 
 
-# the two kernel builds behind the same calls: compiled ahead of time (default) and compiled at run
-# time for the handle's shape (MOE_F_JIT); the MoE parity tests run on both
-VARIANTS = {"aot": 0, "jit": moe.F_JIT}
+# the kernel builds behind the same calls: compiled ahead of time (default), compiled at run time for
+# the handle's shape (MOE_F_JIT), and the gate/up dot products on the scaled matrix cores
+# (MOE_F_MFMA); the MoE parity tests run on each
+VARIANTS = {"aot": 0, "jit": moe.F_JIT, "mfma": moe.F_MFMA}
 _variant = {"flags": 0}
 
 

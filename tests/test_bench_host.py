@@ -25,10 +25,14 @@ def test_kernel_bytes_of_the_four_token_verify_layer():
 
 
 def test_kernel_names_follow_the_variant_string():
+    """Names as the demangler prints them: every template argument, defaults included."""
     n = bench.kernel_names("gfx950-3k-gu5x8-dn8x3-graph", 1)
-    assert n == {"router": "void moe::k1_router<1, 8>(moe::K1Args)",
-                 "gateup": "void moe::k2_gateup<1, 8, 4>(moe::K2Args)",
-                 "down": "void moe::k3_down<8, 3, 1, 1>(moe::K3Args)"}
+    assert n == {"router": "void moe::k1_router<1, 8, false, false>(moe::K1Args)",
+                 "gateup": "void moe::k2_gateup<1, 8, 4, false, false>(moe::K2Args)",
+                 "down": "void moe::k3_down<8, 3, 1, 1, false>(moe::K3Args)"}
+    n = bench.kernel_names("gfx950-3k-gu5x8-dn8x3-graph-jit-mfma", 2)
+    assert n["router"] == "void moe::k1_router<2, 8, true, false>(moe::K1Args)"
+    assert n["gateup"] == "void moe::k2_gateup<2, 8, 2, true, false>(moe::K2Args)"
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):

@@ -59,14 +59,15 @@ def test_compile_then_cache_hit(cache_dir):
     assert len({i1["jit_code_object"], i3["jit_code_object"], i4["jit_code_object"]}) == 3
 
 
+@pytest.mark.parametrize("base", [0, moe.F_MFMA], ids=["valu", "mfma"])
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
-def test_jit_kernels_match_the_ahead_of_time_kernels_bit_for_bit(cache_dir, T):
+def test_jit_kernels_match_the_ahead_of_time_kernels_bit_for_bit(cache_dir, T, base):
     m = MANIFEST["layer_t4"]
     shape = synth.FLASH
     lay = DeviceLayer(shape, m["seed"])
     x = synth.tokens(shape.hidden, m["seed"], 4, m["x_attempt"])[:T]
     out = {}
-    for name, flags in (("aot", 0), ("jit", moe.F_JIT)):
+    for name, flags in (("aot", base), ("jit", base | moe.F_JIT)):
         h = _create(shape, flags)
         lay.set_into(h, 0)
         out[name] = run_layer(h, shape, x)
