@@ -47,16 +47,22 @@ def main():
     ap.add_argument("--no-single", action="store_true", help="skip the single-layer measurements")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 LM-head measurement")
     ap.add_argument("--no-jit", action="store_true", help="skip the run-time compiled (hipRTC) kernels' measurement")
+    ap.add_argument("--no-mfma", action="store_true", help="skip the matrix-core gate/up (MOE_F_MFMA) stack measurement")
     ap.add_argument("--graph-only", action="store_true",
                     help="time only graph replays of the stack (no direct-launch kernel timing, no single layers, "
                          "head or probe): the command to run under a kernel-trace profiler")
+    ap.add_argument("--head-only", action="store_true",
+                    help="time only the LM heads (and the copy probe with --copy-probe): the command to run under a "
+                         "counter profiler for the head kernels")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel for HBM counters)")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
                     help="print a summary of the rocprofv3 CSV output in the DIRs (no GPU) and exit")
+    ap.add_argument("--last", type=int, default=0,
+                    help="with --summarize: also the mean duration of each kernel's last N dispatches")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize)
+        summarize(args.summarize, args.last)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode",
@@ -68,6 +74,15 @@ def main():
 
     import mxfp4_expert_gemv_amd as moe
     import synth
+
+    if args.head_only:
+        dev = torch.device("cuda:0")
+        torch.cuda.init()
+        stream = torch.cuda.current_stream()
+        if args.copy_probe:
+            copy_probe(torch, dev)
+        print(json.dumps({"metric": "LM head", "lm_head": time_head(moe, dev, stream)}), flush=True)
+        return
 
     man = json.load(open(os.path.join(ROOT, "tests", "golden", "manifest.json")))
     st = man["stack"]
@@ -167,13 +182,7 @@ def main():
         return out
 
     if args.copy_probe:
-        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"copy probe: 4 copies of {COPY_PROBE_BYTES} bytes")
+        copy_probe(torch, dev)
 
     results = {}
     flush_buf = None if args.graph_only else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -239,6 +248,26 @@ def main():
             jit[f"t{T}_us_per_layer"] = round(ms * 1e3 / L, 3)
             jit[f"t{T}_vs_ahead_of_time"] = round(results[T]["ms_per_pass"] / ms, 4)
         log(f"run-time compiled kernels: {jit}")
+    # the same stack with the gate/up dot products on the matrix cores (MOE_F_MFMA, a per-handle choice)
+    mfma = None
+    if not args.no_mfma:
+        moe.moe_decode_destroy(h)
+        torch.cuda.synchronize()
+        h = moe.moe_decode_create(H, shape.num_experts, shape.top_k, shape.num_shared, I, 4, L,
+                                  moe.F_RMSNORM_INPUT | moe.F_MFMA)
+        for l in range(L):
+            layer_tensors(st["seed"], l, st["router_attempts"][l], bufs)
+            moe.moe_decode_set_layer(h, l, bufs["router"], bufs["w13"], bufs["w13_s"], bufs["w2"], bufs["w2_s"])
+        torch.cuda.synchronize()
+        mfma = {"variant": moe.moe_decode_query(h)["variant"]}
+        for T in (1, 4):
+            nbytes, _ = pass_bytes(T)
+            ms = time_stack(T, args.steps, args.warmup)
+            moe.moe_decode_check(h)
+            mfma[f"t{T}_us_per_layer"] = round(ms * 1e3 / L, 3)
+            mfma[f"t{T}_gb_s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            mfma[f"t{T}_vs_valu"] = round(results[T]["ms_per_pass"] / ms, 4)
+        log(f"matrix-core gate/up stack: {mfma}")
     probe = hbm_probe(moe, torch, dev, stream)
 
     # single layers (1 and 4 tokens), last-level cache flushed between passes
@@ -318,7 +347,8 @@ def main():
            "pct_of_practical_read_ceiling": round(100 * r1["gb_s"] / probe["best_gb_s"], 2),
            "stack_t1": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r1.items()},
            "stack_t4": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[4].items()},
-           "single_layer": single, "lm_head": head, "hbm_read_probe": probe, "jit": jit, "variant": info["variant"],
+           "single_layer": single, "lm_head": head, "hbm_read_probe": probe, "jit": jit, "mfma_gateup": mfma,
+           "variant": info["variant"],
            "roofline": roofline, "cpu_baseline": cpu, "env": env}
     moe.moe_decode_destroy(h)
     print(json.dumps(out), flush=True)
@@ -328,6 +358,18 @@ COPY_PROBE_BYTES = 256 << 20
 KERNEL_SOURCES = [os.path.join(ROOT, "mxfp4_expert_gemv_amd", "csrc", f)
                   for f in ("moe_kernels.hip", "moe_kernels.h", "moe_device.h", "moe_layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_stack_t1.md")
+
+
+def copy_probe(torch, dev):
+    """Four plain device-to-device copies of COPY_PROBE_BYTES: the reference dispatches that scale
+    the HBM byte counters (each reads and writes COPY_PROBE_BYTES)."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"copy probe: 4 copies of {COPY_PROBE_BYTES} bytes")
 
 
 def source_digest():
@@ -356,10 +398,17 @@ def measured_traffic(kernel):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
-def summarize(dirs):
+def ours(name):
+    """A kernel of this library (not torch's or the runtime's, nor the input generator's)."""
+    return any(k in name for k in ("moe::", "head::", "probe::"))
+
+
+def summarize(dirs, last=0):
     """Markdown summary of rocprofv3 output in the given directories: the kernel statistics (--stats)
-    and, when counter files are present, FETCH_SIZE / WRITE_SIZE per dispatch, each scaled by what
-    the same counter reads for the 256 MiB copy probe (known to read and write 256 MiB)."""
+    of this library's kernels (with last: also the mean of each kernel's last `last` dispatches, from
+    the kernel trace) and, when counter files are present, FETCH_SIZE / WRITE_SIZE per dispatch, each
+    scaled by what the same counter reads for the 256 MiB copy probe (known to read and write 256 MiB),
+    and the other counters per dispatch."""
     import csv
     import glob
 
@@ -371,13 +420,23 @@ def summarize(dirs):
                     out += list(csv.DictReader(fh))
         return out
 
-    stats = rows("*kernel_stats.csv")
+    stats = [r for r in rows("*kernel_stats.csv") if ours(r["Name"])]
     if stats:
-        print("| kernel | calls | average us | min us | max us | share % |")
-        print("|---|---:|---:|---:|---:|---:|")
+        tail = {}
+        if last:
+            per = {}
+            for r in rows("*kernel_trace.csv"):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            for n, v in per.items():
+                v.sort()
+                tail[n] = sum(d for _, d in v[-last:]) / len(v[-last:]) / 1e3
+        print("| kernel | calls | average us | min us | max us | share % |" + (f" last {last}: average us |" if last else ""))
+        print("|---|---:|---:|---:|---:|---:|" + ("---:|" if last else ""))
         for r in stats:
+            t = f" {tail[r['Name']]:.2f} |" if last and r["Name"] in tail else (" |" if last else "")
             print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |" + t)
     counters = rows("*counter_collection.csv")
     if counters:
         # the probe copies are the copy-kernel dispatches of the largest size; other copies (router
@@ -398,13 +457,24 @@ def summarize(dirs):
             a[0] += float(r["Counter_Value"])
             a[1] += 1
         kib = {k: v[0] / v[1] for k, v in acc.items()}
+        sizes = {(n, c): v for (n, c), v in kib.items() if c in ("FETCH_SIZE", "WRITE_SIZE")}
+        other = sorted({c for (_, c) in kib if c not in ("FETCH_SIZE", "WRITE_SIZE")})
+        if other:  # one row per kernel, one column per counter (means per dispatch)
+            print()
+            print("| kernel | dispatches | " + " | ".join(other) + " |")
+            print("|---|---:|" + "---:|" * len(other))
+            for n in sorted({n for (n, c) in kib if c in other}):
+                d = max(acc[(n, c)][1] for c in other if (n, c) in acc)
+                print(f"| `{n}` | {d} | " + " | ".join(f"{kib[(n, c)]:.2f}" if (n, c) in kib else "" for c in other)
+                      + " |")
+        if not sizes:
+            return
         print()
-        print("| kernel | counter | mean per dispatch (KiB for FETCH_SIZE / WRITE_SIZE) | dispatches | "
-              "scale (copy probe) | bytes per dispatch |")
+        print("| kernel | counter | mean per dispatch (KiB) | dispatches | scale (copy probe) | bytes per dispatch |")
         print("|---|---|---:|---:|---:|---:|")
         rec = {"kernel_source_sha256_16": source_digest(), "copy_probe_bytes": COPY_PROBE_BYTES, "scale": scale,
                "kernels": {}}
-        for (n, c), v in sorted(kib.items()):
+        for (n, c), v in sorted(sizes.items()):
             sc = scale.get(c)
             b = v * 1024 * sc if sc else None
             print(f"| `{n}` | {c} | {v:.2f} | {acc[(n, c)][1]} | {'' if sc is None else round(sc, 4)} | "
