@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_HERE, "libmoe_decode.so")
+# MOE_SANITIZED_LIBS: a directory holding an AddressSanitizer / UndefinedBehaviorSanitizer build of
+# the library (host code instrumented; built by tests/sanitized.py) to load instead
+LIB = os.path.join(os.environ.get("MOE_SANITIZED_LIBS") or _HERE, "libmoe_decode.so")
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_DTYPE",

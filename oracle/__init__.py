@@ -16,7 +16,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "moe_oracle.c")
-LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_SANITIZED_LIBS: a directory holding an AddressSanitizer / UndefinedBehaviorSanitizer build of
+# the oracle (tests/sanitized.py) to load instead
+LIB = os.path.join(os.environ.get("MOE_SANITIZED_LIBS") or _HERE, "libmoe_oracle.so")
 GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-shared", "-fPIC", "-fopenmp"]
 
 # Which independent check pins each oracle function (tests/test_oracle_*.py).
@@ -60,6 +62,8 @@ _lib = None
 
 
 def build(force: bool = False) -> str:
+    if os.environ.get("MOE_SANITIZED_LIBS"):
+        return LIB  # built by tests/sanitized.py
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         subprocess.check_call(["gcc", *GCC_FLAGS, SRC, "-o", LIB, "-lm"])
     return LIB

@@ -18,7 +18,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
+# MOE_SANITIZED_LIBS: a directory holding an AddressSanitizer / UndefinedBehaviorSanitizer build of
+# the host generator (tests/sanitized.py) to load instead
+HOST_LIB = os.path.join(os.environ.get("MOE_SANITIZED_LIBS") or _HERE, "libsynth_host.so")
 DEVICE_LIB = os.path.join(_HERE, "libsynth_device.so")
 
 TENSOR_ROUTER, TENSOR_W13, TENSOR_W13S, TENSOR_W2, TENSOR_W2S, TENSOR_X, TENSOR_HEAD = range(7)
