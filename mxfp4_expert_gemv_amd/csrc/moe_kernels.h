@@ -1060,7 +1060,7 @@ template <int KSUB, int ITERS, int T, int UPW, bool STAMP = false>
 __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     stamp_start<STAMP>(a.stamp);
     constexpr int R = kWave / KSUB;  // units per wave and group; rows per repacked tile
-    constexpr bool CODES = T >= 3;   // FP8 h codes from the requantisation kernel
+    constexpr bool CODES = T >= kKqMinT;  // FP8 h codes from the requantisation kernel
     constexpr int MAXP = CODES ? 1 : T == 1 ? 5 : 9;  // h columns (rows of h) per thread, loaded up front
     extern __shared__ uint4 smem3[];
     const int H = MOE_SHAPE(H, a.H), I = MOE_SHAPE(I, a.I), k = MOE_SHAPE(K, a.k), Ih = I / 2, tiles = I / kGuOut, rtiles = H / R;

@@ -229,7 +229,7 @@ int layer_grid(const Shape& sh, int T, int kind) {
         case kKernInput: return central ? T : 0;
         case kKernRouter: return n_router_wg + (central ? sh.S * tiles : 0);
         case kKernGateup: return (central ? 0 : sh.S * tiles) + routed_slots_max(sh, T) * tiles;
-        case kKernRequant: return central ? sh.pairs(T) : 0;
+        case kKernRequant: return T >= kKqMinT ? sh.pairs(T) : 0;
         case kKernDown: return down_two_per_cu(sh, T) ? 2 * kDownGrid : kDownGrid;
         default: return 0;
     }
@@ -242,7 +242,7 @@ bool jit_kernel_names(const Shape& sh, int T, bool mfma, std::string (&names)[kL
     names[kKernRouter] = "moe::k1_router<" + t + ", " + bpl + ", " + mf + ">";
     names[kKernGateup] =
         "moe::k2_gateup<" + t + ", " + bpl + ", " + std::to_string(gateup_wt(sh, T)) + ", " + mf + ">";
-    names[kKernRequant] = T >= 3 ? "moe::kq_requant<false>" : "";
+    names[kKernRequant] = T >= kKqMinT ? "moe::kq_requant<false>" : "";
     names[kKernDown] = "moe::k3_down<" + std::to_string(sh.ksub()) + ", " + std::to_string(sh.iters()) + ", " + t +
                        ", " + std::to_string(down_two_per_cu(sh, T) ? 2 : T) + ">";
     return true;
@@ -322,7 +322,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
         MOE_TRY(launch(k2_gateup<T, BPL, 1, false, STAMP>, jf(kKernGateup), n2, 64 * GW, lds2, stream,
                        evk(kKernGateup), a2));
 
-    if (CENTRAL) {
+    if (T >= kKqMinT) {
         KQArgs aq{P.h, P.hamax, P.hq, P.hs, sh.I};
         aq.stamp = P.stamp[kKernRequant];
         MOE_TRY(launch(kq_requant<STAMP>, jf(kKernRequant), sh.pairs(T), 256, 0, stream, evk(kKernRequant), aq));
