@@ -213,7 +213,7 @@ moe_status fp8_head_verify(fp8_head_handle* h, const void* x, int32_t num_tokens
  * harnesses that forbid allocation): the computation of fp8_head_run on the caller's own row-major
  * weights, with no handle.  w: E4M3 [vocab][hidden] row-major (16-byte aligned); row_scale: FP32
  * [vocab]; x, logits (nullable), argmax and num_tokens as in fp8_head_run.  Allocates nothing: the
- * argmax reduction's scratch (an arrival counter and per-tile maxima, 131,328 bytes) is one fixed
+ * argmax reduction's scratch (an arrival counter and per-workgroup maxima, 131,328 bytes) is one fixed
  * device array per GPU, held until the process ends; every call on a GPU uses that GPU's copy, so
  * calls that overlap on one GPU (other streams, other threads) race and must be serialised by the
  * caller.  The last workgroup of each call resets the counter to zero.  vocab above

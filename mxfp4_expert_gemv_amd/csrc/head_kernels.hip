@@ -8,8 +8,12 @@
 //
 // The same kernel also runs the unquantised BF16 head (bf16_head_create), for comparison.
 //
-// Each workgroup owns one 64-row tile and has H / 256 waves; wave w takes K [256 w, 256 w + 256) of
-// the tile's rows on the matrix cores: v_mfma_f32_16x16x32_bf16 on four 16-row groups, A = the
+// As many workgroups as the device holds at once each walk 64-row tiles (blockIdx.x, + grid, ...),
+// the next tile's first weight loads issued while the current tile finishes, and keep each token's
+// best (value, lowest index) in registers; one partial per workgroup goes to the final argmax (one
+// tile per workgroup, with a write-through partial and an arrival per tile, measured 81 against 67
+// us for the E4M3 head).  A workgroup has H / 256 waves; wave w takes K [256 w, 256 w + 256) of the
+// tile's rows on the matrix cores: v_mfma_f32_16x16x32_bf16 on four 16-row groups, A = the
 // weights (E4M3 codes converted exactly to bf16 in VGPRs, or the bf16 weights themselves), B = x
 // (bf16, from LDS; column n = token n, zero columns past T), fp32 accumulators.  Measured on gfx950,
 // one such instruction is within 2.7 * 2^-24 * sum |terms| of the exact sum (C + 32 products), so
@@ -31,6 +35,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace head {
@@ -81,12 +86,13 @@ struct HeadArgs {
     const uint16_t* x;    // [T][H] bf16
     float* logits;        // [T][V] or null
     int32_t* argmax;      // [T]
-    float* pval;          // [VT][T] per-tile maxima
-    int32_t* pidx;        // [VT][T]
+    float* pval;          // [grid][T] per-workgroup maxima (room for [VT][T])
+    int32_t* pidx;        // [grid][T]
     unsigned* ticket;
     const int32_t* draft;  // [T-1] drafted tokens of positions 1 .. T-1, or null
     int32_t* accept;       // [1] accepted drafts (with draft)
     int V, H;
+    int VT;                // 64-row tiles (the grid is smaller: each workgroup walks several)
 };
 
 __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
@@ -96,14 +102,15 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
     }
 }
 
-// The end of every head kernel: red[w][t][r] holds wave w's partial sum of row r of the tile for
-// token t.  Sums the waves, scales, writes the logits, takes the tile's (max, lowest index) per
-// token, and the last workgroup to arrive reduces the tiles' maxima (and the verify acceptance).
+// One tile's end: red[w][t][r] holds wave w's partial sum of row r of tile vt for token t.  Wave
+// t % NW sums the waves, scales, writes the logits and folds the tile's (max, lowest index) into
+// token t's running best (bv[t], bi[t]), the same in every lane of the wave.
 template <int T>
-__device__ void head_finish(const HeadArgs& a, const float (*red)[T][kWave], int* is_last) {
-    const int vt = blockIdx.x, VT = gridDim.x;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    for (int t = wv; t < T; t += NW) {
+__device__ void tile_best(const HeadArgs& a, const float (*red)[T][kWave], int vt, float (&bv)[T], int (&bi)[T]) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t % NW != wv) continue;  // uniform per wave
         float s = 0.0f;
         for (int w = 0; w < NW; ++w) s += red[w][t][lane];
         const int row = vt * kWave + lane;
@@ -115,33 +122,45 @@ __device__ void head_finish(const HeadArgs& a, const float (*red)[T][kWave], int
             if (a.logits) a.logits[(size_t)t * a.V + row] = v;
         }
         for (int off = 32; off > 0; off >>= 1) better(v, idx, __shfl_xor(v, off, 64), __shfl_xor(idx, off, 64));
-        if (lane == 0) {  // write-through: the last workgroup reads them without any cache flush
-            __hip_atomic_store(a.pval + (size_t)vt * T + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.pidx + (size_t)vt * T + t, idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        better(bv[t], bi[t], v, idx);
+    }
+}
+
+// The end of the head kernel: each token's best over this workgroup's tiles is its partial; the
+// last workgroup to arrive reduces the partials of all workgroups (and the verify acceptance).
+template <int T>
+__device__ void head_finish(const HeadArgs& a, const float (&bv)[T], const int (&bi)[T], int* is_last) {
+    const int G = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t % NW == wv && lane == 0) {  // write-through: the last workgroup reads them without any cache flush
+            __hip_atomic_store(a.pval + (size_t)blockIdx.x * T + t, bv[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.pidx + (size_t)blockIdx.x * T + t, bi[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // the last workgroup to arrive reduces the per-tile maxima.  Ordering rests on the ISA, not on
-    // release/acquire (an L2 write-back in each of the 2,456 workgroups made the head ten times
-    // slower): the partials are agent-scope atomic stores, written through to the device-coherent
-    // level, vmcnt(0) waits for the memory's acknowledgement before the arrival, and the last
-    // workgroup reads them with agent-scope atomic loads, which do not hit in the non-coherent L2.
+    // the last workgroup to arrive reduces the partials.  Ordering rests on the ISA, not on
+    // release/acquire (an L2 write-back in every workgroup made the head ten times slower): the
+    // partials are agent-scope atomic stores, written through to the device-coherent level,
+    // vmcnt(0) waits for the memory's acknowledgement before the arrival, and the last workgroup
+    // reads them with agent-scope atomic loads, which do not hit in the non-coherent L2.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tid == 0)
-        *is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(VT - 1);
+        *is_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(G - 1);
     __syncthreads();
     if (!*is_last) return;
     __shared__ int32_t am_s[T];
     for (int t = wv; t < T; t += NW) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int i = lane; i < VT; i += kWave)
-            better(bv, bi, __hip_atomic_load(a.pval + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+        float v = -INFINITY;
+        int idx = 0x7fffffff;
+        for (int i = lane; i < G; i += kWave)
+            better(v, idx, __hip_atomic_load(a.pval + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                    __hip_atomic_load(a.pidx + (size_t)i * T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        for (int off = 32; off > 0; off >>= 1) better(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
+        for (int off = 32; off > 0; off >>= 1) better(v, idx, __shfl_xor(v, off, 64), __shfl_xor(idx, off, 64));
         if (lane == 0) {
-            a.argmax[t] = bi;
-            am_s[t] = bi;
+            a.argmax[t] = idx;
+            am_s[t] = idx;
         }
     }
     if (a.draft) {
@@ -180,81 +199,92 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t d0, uint32_t d1) {
 template <bool FP8, bool RM>
 constexpr int head_ring_steps() { return FP8 && !RM ? 2 : 1; }
 template <int T, bool FP8, bool RM = false>
-__global__ __launch_bounds__(640) __attribute__((amdgpu_waves_per_eu(FP8 ? 6 : 8))) void head_mfma(HeadArgs a) {
+__global__ __launch_bounds__(640) __attribute__((amdgpu_waves_per_eu(6))) void head_mfma(HeadArgs a) {
     constexpr int U = FP8 ? 16 : 32;  // units per lane
     constexpr int S = U / 4;          // steps
     constexpr int RS = head_ring_steps<FP8, RM>();
+    static_assert(S % RS == 0, "a step keeps its ring slot from tile to tile");
     extern __shared__ uint32_t xs[];  // [T][H/2] bf16 pairs
     __shared__ float red[10][T][kWave];
     __shared__ int is_last;
-    const int vt = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, NW = blockDim.x >> 6;
-    const int H = a.H, Hh = H / 2;
+    const int H = a.H, Hh = H / 2, VT = a.VT, G = gridDim.x;
 
     uint4 wr[4 * RS];
-    const uint4* p = RM ? a.w : a.w + ((size_t)vt * NW + wv) * U * kWave + lane;
-    // row-major: the lane's first unit in each 16-row group (a 32-bit unit index: the caller's
-    // matrix is at most MOE_NOALLOC_MAX_VOCAB x 2560 bytes)
-    uint32_t ru[4];
-    if constexpr (RM) {
-        static_assert(FP8, "row-major weights are E4M3");
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ru[r] = (uint32_t)min(vt * kWave + 16 * r + (lane & 15), a.V - 1) * (uint32_t)(H / 16) + wv * U + (lane >> 4);
-    }
-    // step st: unit 4 st + r of the lane (16-row group r) into ring slot st % RS
-    auto issue = [&](int st) {
+    // step st of tile vt: unit 4 st + r of the lane (16-row group r) into ring slot st % RS.  Row-
+    // major: a 32-bit unit index (the caller's matrix is at most MOE_NOALLOC_MAX_VOCAB x 2560 bytes).
+    auto issue = [&](int vt, int st) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (RM)
-                wr[(st % RS) * 4 + r] = ld_nt(p + (ru[r] + 4 * st));
-            else
-                wr[(st % RS) * 4 + r] = ld_nt(p + (4 * st + r) * kWave);
+            if constexpr (RM) {
+                static_assert(FP8, "row-major weights are E4M3");
+                const uint32_t row = (uint32_t)min(vt * kWave + 16 * r + (lane & 15), a.V - 1);
+                wr[(st % RS) * 4 + r] = ld_nt(a.w + (row * (uint32_t)(H / 16) + wv * U + (lane >> 4) + 4 * st));
+            } else {
+                wr[(st % RS) * 4 + r] = ld_nt(a.w + ((((size_t)vt * NW + wv) * U + 4 * st + r) * kWave + lane));
+            }
         }
     };
+    int vt = blockIdx.x;  // this workgroup's tiles: blockIdx.x, + G, + 2 G, ... (G <= VT)
 #pragma unroll
-    for (int st = 0; st < RS; ++st) issue(st);
+    for (int st = 0; st < RS; ++st) issue(vt, st);
     for (int i = tid; i < T * Hh; i += blockDim.x) xs[i] = ((const uint32_t*)a.x)[i];
     __syncthreads();
 
     const int n = lane & 15, g = lane >> 4;
     const bool on = n < T;
     const uint16_t* xrow = (const uint16_t*)xs + (on ? n : 0) * H + wv * 256;
-    f32x4_t acc[4];
+    float bv[T];  // token t's best over the workgroup's tiles (held by wave t % NW)
+    int bi[T];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < T; ++t) {
+        bv[t] = -INFINITY;
+        bi[t] = 0x7fffffff;
+    }
+    for (; vt < VT; vt += G) {
+        const int nvt = vt + G;
+        f32x4_t acc[4];
 #pragma unroll
-    for (int st = 0; st < S; ++st) {
-        // E4M3: the step's units hold blocks 2 st and 2 st + 1 (their low and high halves); bf16:
-        // block st
+        for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
-            const int kofs = FP8 ? 64 * st + 16 * g + 8 * h : 32 * st + 8 * g;
-            uint4 xb = make_uint4(0, 0, 0, 0);
-            if (on) xb = *(const uint4*)(xrow + kofs);
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb);
+        for (int st = 0; st < S; ++st) {
+            // E4M3: the step's units hold blocks 2 st and 2 st + 1 (their low and high halves); bf16:
+            // block st
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint4& q = wr[(st % RS) * 4 + r];
-                bf16x8_t w;
-                if constexpr (FP8)
-                    w = h ? e4m3x8_to_bf16x8(q.z, q.w) : e4m3x8_to_bf16x8(q.x, q.y);
-                else
-                    w = __builtin_bit_cast(bf16x8_t, q);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, b, acc[r], 0, 0, 0);
+            for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
+                const int kofs = FP8 ? 64 * st + 16 * g + 8 * h : 32 * st + 8 * g;
+                uint4 xb = make_uint4(0, 0, 0, 0);
+                if (on) xb = *(const uint4*)(xrow + kofs);
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint4& q = wr[(st % RS) * 4 + r];
+                    bf16x8_t w;
+                    if constexpr (FP8)
+                        w = h ? e4m3x8_to_bf16x8(q.z, q.w) : e4m3x8_to_bf16x8(q.x, q.y);
+                    else
+                        w = __builtin_bit_cast(bf16x8_t, q);
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, b, acc[r], 0, 0, 0);
+                }
             }
+            // refill the slot: a later step of this tile, or the first steps of the next one
+            if (st + RS < S)
+                issue(vt, st + RS);
+            else if (nvt < VT)
+                issue(nvt, st + RS - S);
         }
-        if (st + RS < S) issue(st + RS);
-    }
-    // lane l holds rows 16 r + 4 (l / 16) + i of the tile for token l % 16
-    if (on) {
+        // lane l holds rows 16 r + 4 (l / 16) + i of the tile for token l % 16
+        if (on) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wv][n][16 * r + 4 * g + i] = acc[r][i];
+                for (int i = 0; i < 4; ++i) red[wv][n][16 * r + 4 * g + i] = acc[r][i];
+        }
+        __syncthreads();
+        tile_best<T>(a, red, vt, bv, bi);
+        __syncthreads();  // red is rewritten by the next tile
     }
-    __syncthreads();
-    head_finish<T>(a, red, &is_last);
+    head_finish<T>(a, bv, bi, &is_last);
 }
 
 // Per-row FP8 quantisation of the head at load time (the step the pages put before the FP8 head):
@@ -334,31 +364,44 @@ hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, 
     return hipGetLastError();
 }
 
-template <bool FP8, bool RM = false>
-static hipError_t launch_head_t(const HeadArgs& a, int T, int VT, hipStream_t stream) {
+// The grid: as many workgroups as the device holds at once (each walks tiles blockIdx.x, + grid,
+// ...), at most one per tile.
+template <int T, bool FP8, bool RM>
+static hipError_t launch_head_tt(const HeadArgs& a, hipStream_t stream) {
     const unsigned block = kWave * (a.H / kSlice);
     const size_t lds = (size_t)T * a.H * 2;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, head_mfma<T, FP8, RM>, block, lds);
+    if (e != hipSuccess) return e;
+    const int grid = std::min(a.VT, std::max(per_cu, 1) * std::max(cus, 1));
+    head_mfma<T, FP8, RM><<<grid, block, lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <bool FP8, bool RM = false>
+static hipError_t launch_head_t(const HeadArgs& a, int T, hipStream_t stream) {
     switch (T) {
-        case 1: head_mfma<1, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 2: head_mfma<2, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 3: head_mfma<3, FP8, RM><<<VT, block, lds, stream>>>(a); break;
-        case 4: head_mfma<4, FP8, RM><<<VT, block, lds, stream>>>(a); break;
+        case 1: return launch_head_tt<1, FP8, RM>(a, stream);
+        case 2: return launch_head_tt<2, FP8, RM>(a, stream);
+        case 3: return launch_head_tt<3, FP8, RM>(a, stream);
+        case 4: return launch_head_tt<4, FP8, RM>(a, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_head(const void* w, const float* scale, const uint16_t* x, int T, float* logits, int32_t* argmax,
                        float* pval, int32_t* pidx, unsigned* ticket, const int32_t* draft, int32_t* accept, int V,
                        int H, bool fp8, hipStream_t stream) {
     const int VT = (V + kWave - 1) / kWave;
-    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, draft, accept, V, H};
-    return fp8 ? launch_head_t<true>(a, T, VT, stream) : launch_head_t<false>(a, T, VT, stream);
+    HeadArgs a{(const uint4*)w, scale, x, logits, argmax, pval, pidx, ticket, draft, accept, V, H, VT};
+    return fp8 ? launch_head_t<true>(a, T, stream) : launch_head_t<false>(a, T, stream);
 }
 
 // ------------------------------------------------------------------------------------------------
 // The head without a handle, for callers that cannot allocate: its scratch (the arrival counter and
-// the per-tile maxima of the argmax reduction) is this fixed device array, one copy per GPU that
+// the per-workgroup maxima of the argmax reduction) is this fixed device array, one copy per GPU that
 // the library runs on, held until the process ends.  Host code never passes the array's name to a
 // kernel (in host code it is a stand-in, not a device address); it passes the address that
 // hipGetSymbolAddress returns for the current device.
@@ -400,8 +443,8 @@ hipError_t launch_head_rowmajor(const void* w, const float* scale, const uint16_
     const int VT = (V + kWave - 1) / kWave;
     uint8_t* sp = (uint8_t*)scratch_dev;
     HeadArgs a{(const uint4*)w, scale, x, logits, argmax, (float*)(sp + kScratchVal), (int32_t*)(sp + kScratchIdx),
-               (unsigned*)(sp + kScratchTicket), nullptr, nullptr, V, H};
-    return launch_head_t<true, true>(a, T, VT, stream);
+               (unsigned*)(sp + kScratchTicket), nullptr, nullptr, V, H, VT};
+    return launch_head_t<true, true>(a, T, stream);
 }
 
 }  // namespace head
