@@ -776,12 +776,12 @@ struct K1Args {
     float* x_scale;          // 1-2 tokens: [T] or null
     uint8_t* x_codes;        // 1-2 tokens: [T][H] or null
     float* logits;           // [T][E]
-    // 3-4 tokens: the last router workgroup to finish takes the top-k once for the layer
+    // above gu_route_max_t tokens: the last router workgroup to finish takes the top-k once for the layer
     unsigned* ticket;        // arrivals of router workgroups; zero between layers
     SlotTable* slots_out;    // routed experts of this layer
     int32_t* ids_out;        // [T][k] or null
     float* w_out;            // [T][k] or null
-    // 3-4 tokens: workgroups from n_router_wg on compute the shared expert's gate/up tiles (CUs the
+    // 3-4 tokens: workgroups from n_router_wg on compute the shared expert's gate/up items (CUs the
     // router leaves idle), which keeps the gate/up kernel within one workgroup round
     const uint4* w13;
     const uint8_t* w13s;
@@ -811,11 +811,18 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
     // 3-4 tokens: the MoE input comes from the input kernel (once per layer) instead of being
     // recomputed by every workgroup (its fp64 work grows with the token count)
     constexpr bool CENTRAL = T >= 3;
+    constexpr bool TICKET = T > gu_route_max_t(MF);  // the last router workgroup takes the top-k
     if constexpr (CENTRAL) {
-        if ((int)blockIdx.x >= a.n_router_wg) {  // the shared expert's gate/up tile, every token
+        if ((int)blockIdx.x >= a.n_router_wg) {  // the shared expert's gate/up items
             __shared__ float red[kMaxWaves * T * kGuRows];
             __shared__ float sx[T];
-            const int tiles = MOE_SHAPE(I, a.I) / kGuOut, tile = blockIdx.x - a.n_router_wg, NC = H / 8;
+            const int tiles = MOE_SHAPE(I, a.I) / kGuOut, NC = H / 8, b = blockIdx.x - a.n_router_wg;
+            // VALU form: one item per tile and token (a one-token dot reads a quarter of the LDS
+            // activations of a 4-token one); the T items of a tile sit 8 apart in blockIdx, on one XCD
+            // (whose L2 then serves the tile's weights to all of them) when tiles % 8 == 0
+            constexpr bool SPLIT = !MF;
+            const int g = tiles % 8 == 0 ? 8 : 1, grp = b / (g * T), r = b - grp * g * T;
+            const int tile = SPLIT ? grp * g + r % g : b, t0 = SPLIT ? r / g : 0, ntk = SPLIT ? 1 : a.ntok;
             uint2 xc[T];
             const int xi = min(tid, NC - 1) * 8;
 #pragma unroll
@@ -831,11 +838,10 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
             int tok[T], pair[T];
 #pragma unroll
             for (int j = 0; j < T; ++j) {
-                tok[j] = j;
-                pair[j] = j * (MOE_SHAPE(K, a.k) + MOE_SHAPE(S, a.S)) + MOE_SHAPE(K, a.k);
+                tok[j] = min(t0 + j, T - 1);
+                pair[j] = tok[j] * (MOE_SHAPE(K, a.k) + MOE_SHAPE(S, a.S)) + MOE_SHAPE(K, a.k);
             }
-            gateup_tile<T, BPL, MF>(L, smem1, H, sx, a.ntok, tok, pair, tile, MOE_SHAPE(I, a.I), a.h, a.hamax,
-                                    red);
+            gateup_tile<T, BPL, MF>(L, smem1, H, sx, ntk, tok, pair, tile, MOE_SHAPE(I, a.I), a.h, a.hamax, red);
             stamp_end<STAMP>(a.stamp);
             return;
         }
@@ -886,16 +892,16 @@ __global__ __launch_bounds__(320) void k1_router(K1Args a) {
         for (int t = 0; t < T; ++t) {
             const float v = sum64(acc[t]);
             if (lane == 0) {
-                if constexpr (CENTRAL)  // write-through: the last workgroup reads it without a cache flush
+                if constexpr (TICKET)  // write-through: the last workgroup reads it without a cache flush
                     __hip_atomic_store(a.logits + t * MOE_SHAPE(E, a.E) + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else
                     a.logits[t * MOE_SHAPE(E, a.E) + e] = v;
             }
         }
     }
-    if constexpr (CENTRAL) {
-        // 3-4 tokens: the last router workgroup to arrive takes the top-k of every token (the gate/up
-        // workgroups would otherwise each redo it for all tokens).  Ordering rests on the ISA, not on
+    if constexpr (TICKET) {
+        // Above gu_route_max_t tokens: the last router workgroup to arrive takes the top-k of every token
+        // (the gate/up workgroups would otherwise each redo it for all tokens).  Ordering rests on the ISA, not on
         // release/acquire (whose L2 write-back in every workgroup costs microseconds): the logits are
         // agent-scope atomic stores, written through to the device-coherent level; vmcnt(0) waits
         // until the memory has acknowledged them, before the barrier and the arrival; the last
@@ -934,8 +940,8 @@ struct K2Args {
     const uint8_t* w13s;
     float* h;                // [pairs][I]
     float* hamax;            // [pairs][I/16]
-    SlotTable* slots;        // routed experts of this layer: stored here for the down kernel (1-2
-                             // tokens) or read (3-4 tokens, from the router kernel)
+    SlotTable* slots;        // routed experts of this layer: stored here for the down kernel (up to
+                             // gu_route_max_t tokens) or read (above, from the router kernel)
     int32_t* ids_out;        // [T][k] or null
     float* w_out;            // [T][k] or null
     int H, E, k, S, I, n_sh_wg;
@@ -948,8 +954,11 @@ struct K2Args {
 // token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
 // tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
 // the weights.
+// VALU form with the router kernel's top-k (4 tokens): at most 64 VGPRs: six workgroups per CU, so that the
+// 4-token grid of 32 slots x 48 tiles runs in one round (44.1 against 44.7 us/layer).
 template <int T, int BPL, int W, bool MF = false, bool STAMP = false>
-__global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
+__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(T > gu_route_max_t(MF) && !MF ? 8 : 1)))
+void k2_gateup(K2Args a) {
     stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem2[];
     // smem2: the input's FP8 codes as f16 pairs [T][H/2], or as bf16 [T][H] (MF)
@@ -968,8 +977,8 @@ __global__ __launch_bounds__(320) void k2_gateup(K2Args a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) xc[t] = *(const uint2*)(a.xq + (size_t)t * H + xi);
     const float sxv = a.xs[tid < T ? tid : 0];
-    // 1-2 tokens: every routed workgroup takes the top-k itself; 3-4 tokens: the router kernel did
-    constexpr bool ROUTE = T <= 2;
+    // up to gu_route_max_t tokens every routed workgroup takes the top-k itself; above, the router kernel did
+    constexpr bool ROUTE = T <= gu_route_max_t(MF);
     // W waves per token take the top-k together (W = 1: one wave per token)
     float lgv[8 / W];
     if constexpr (ROUTE) route_issue<T, W>(a.logits, MOE_SHAPE(E, a.E), lgv);  // shared workgroups load them too: exact waits below

@@ -6,11 +6,12 @@
 //                     quantisation of the MoE input, once per layer.
 //   k1_router         router GEMV, one wave per expert row (bf16 x bf16 products, fp32 FMA).  At
 //                     1-2 tokens every workgroup also normalises the input itself and stores the
-//                     FP8 codes of its share of it; at 3-4 tokens the last router workgroup to
-//                     finish takes the top-k once (arrival ticket), and extra workgroups compute
-//                     the shared expert's gate/up tiles.
-//   k2_gateup         the routed gate/up tiles (and at 1-2 tokens the shared expert's): at 1-2
-//                     tokens every routed workgroup redoes the top-k from the logits (one wave per
+//                     FP8 codes of its share of it; at 3-4 tokens extra workgroups compute the
+//                     shared expert's gate/up tiles (VALU form: one workgroup per tile and token),
+//                     and above 3 tokens (2 in the matrix-core form) the last router workgroup
+//                     to finish takes the top-k once (arrival ticket).
+//   k2_gateup         the routed gate/up tiles (and at 1-2 tokens the shared expert's): at 1-3
+//                     tokens (1-2 in the matrix-core form) every routed workgroup redoes the top-k from the logits (1-4 waves per
 //                     token, lower index first on ties) and builds the list of distinct routed
 //                     experts; each workgroup streams its 32-row MXFP4 gate/up tile: E2M1 pairs are
 //                     converted to f16 in VGPRs and dot2-multiplied with the FP8 activation codes
@@ -227,7 +228,7 @@ int layer_grid(const Shape& sh, int T, int kind) {
     const int tiles = sh.gu_tiles(), n_router_wg = (sh.E + sh.gw() - 1) / sh.gw();
     switch (kind) {
         case kKernInput: return central ? T : 0;
-        case kKernRouter: return n_router_wg + (central ? sh.S * tiles : 0);
+        case kKernRouter: return n_router_wg + (central ? sh.S * tiles * T : 0);  // at most (MFMA form: S tiles)
         case kKernGateup: return (central ? 0 : sh.S * tiles) + routed_slots_max(sh, T) * tiles;
         case kKernRequant: return T >= kKqMinT ? sh.pairs(T) : 0;
         case kKernDown: return down_two_per_cu(sh, T) ? 2 * kDownGrid : kDownGrid;
@@ -286,10 +287,12 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
         MOE_TRY(launch(k0_input<STAMP>, jf(kKernInput), T, 1024, (size_t)sh.H * 2, stream, evk(kKernInput), a0));
     }
     const int n_router_wg = (sh.E + GW - 1) / GW;
-    const int n_sh1 = CENTRAL ? sh.S * tiles : 0;  // shared gate/up tiles in the router kernel
+    // shared gate/up items in the router kernel: per tile, or per tile and token
+    const int n_sh1 = CENTRAL ? sh.S * tiles * (L.w13_mfma ? 1 : T) : 0;
+    const bool ticket = T > gu_route_max_t(L.w13_mfma);  // the router kernel takes the top-k
     K1Args a1{(const uint16_t*)L.router, P.x, P.xn, P.xq, P.xs, CENTRAL ? nullptr : P.trace,
               CENTRAL ? nullptr : P.x_scale, CENTRAL ? nullptr : P.x_codes, P.logits, P.ticket, P.slots,
-              CENTRAL ? P.ids : nullptr, CENTRAL ? P.w : nullptr, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h,
+              ticket ? P.ids : nullptr, ticket ? P.w : nullptr, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h,
               P.hamax, sh.H, sh.E, sh.k, sh.S, sh.I, normalize ? 1 : 0, n_router_wg, T};
     a1.stamp = P.stamp[kKernRouter];
     const size_t lds1 = (size_t)T * sh.H * 2;
@@ -303,7 +306,7 @@ static hipError_t launch_layer_t(const Shape& sh, const LayerPtrs& L, const RunP
     const int n_sh_wg = CENTRAL ? 0 : sh.S * tiles;  // 1-2 tokens: shared gate/up tiles here
     const int n_gu_wg = routed_slots_max(sh, T) * tiles;
     K2Args a2{P.logits, P.xq, P.xs, (const uint4*)L.w13, (const uint8_t*)L.w13s, P.h, P.hamax, P.slots,
-              CENTRAL ? nullptr : P.ids, CENTRAL ? nullptr : P.w, sh.H, sh.E, sh.k, sh.S, sh.I, n_sh_wg, T};
+              ticket ? nullptr : P.ids, ticket ? nullptr : P.w, sh.H, sh.E, sh.k, sh.S, sh.I, n_sh_wg, T};
     a2.stamp = P.stamp[kKernGateup];
     const size_t lds2 = (size_t)T * sh.H * 2;
     constexpr int WT = T == 1 ? 4 : T == 2 ? 2 : 1;

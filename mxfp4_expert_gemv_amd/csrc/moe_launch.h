@@ -28,7 +28,7 @@ struct RunPtrs {
     uint8_t* xq;        // 3-4 tokens: [T][H] FP8 codes of the MoE input
     float* xs;          // 3-4 tokens: [T] their scales
     float* logits;      // [T][E]
-    unsigned* ticket;   // 3-4 tokens: router arrivals (zero between layers)
+    unsigned* ticket;   // router arrivals when it takes the top-k (zero between layers)
     SlotTable* slots;
     float* h;           // [T*(k+S)][I]
     float* hamax;       // [T*(k+S)][I/16]

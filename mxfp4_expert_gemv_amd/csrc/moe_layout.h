@@ -39,6 +39,13 @@ constexpr int kMaxWaves = 5;        // waves per workgroup of the router / gate/
 // workgroup requantises all h rows itself: at 4 tokens, 36 rows per workgroup, that measured
 // 28.7 us for the down kernel against 11.2 us plus 1.4 us for the requantisation kernel).
 constexpr int kKqMinT = 3;
+// Token counts up to which every routed gate/up workgroup takes the top-k itself (VALU form: 3,
+// matrix-core form: 2); above, the last router workgroup takes it once, behind an arrival ticket.
+// Measured on the 42-layer stack, us/layer: VALU form, top-k in gate/up at 3 tokens 37.8 against
+// 38.9 with the ticket, at 4 tokens 47.5 against 44.7 (1,536 workgroups each redoing four top-k's
+// cost more than the ticket's tail); matrix-core form at 3 tokens 41.6 against 39.0 (its 76-VGPR
+// workgroups, four per CU, run the 3-token grid in two rounds, each paying the top-k).
+constexpr int gu_route_max_t(bool mfma) { return mfma ? 2 : 3; }
 constexpr int kDownGrid = 256;      // workgroups of the down kernel: one per compute unit (H % 256 == 0)
 
 // Work list of the routed experts of one call, built identically by every workgroup of the
