@@ -954,10 +954,13 @@ struct K2Args {
 // token), builds the distinct-expert list, and computes tile `tile` of routed expert `slot` for the
 // tokens routed to it (slots beyond the list exit).  The first of them stores the list, the ids and
 // the weights.
-// VALU form with the router kernel's top-k (4 tokens): at most 64 VGPRs: six workgroups per CU, so that the
-// 4-token grid of 32 slots x 48 tiles runs in one round (44.1 against 44.7 us/layer).
+// VALU form with the router kernel's top-k (4 tokens): at most 64 VGPRs, six workgroups per CU, so
+// that the 4-token grid of 32 slots x 48 tiles runs in one round (44.1 against 44.7 us/layer).  The
+// stamping instance is left uncapped (under the cap its stamps cost it six VGPR spills): it runs
+// five workgroups per CU, so the timing record overstates this kernel slightly at 4 tokens.
 template <int T, int BPL, int W, bool MF = false, bool STAMP = false>
-__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(T > gu_route_max_t(MF) && !MF ? 8 : 1)))
+__global__ __launch_bounds__(320)
+__attribute__((amdgpu_waves_per_eu(T > gu_route_max_t(MF) && !MF && !STAMP ? 8 : 1)))
 void k2_gateup(K2Args a) {
     stamp_start<STAMP>(a.stamp);
     extern __shared__ uint4 smem2[];
