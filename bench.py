@@ -356,7 +356,7 @@ def main():
 
 COPY_PROBE_BYTES = 256 << 20
 KERNEL_SOURCES = [os.path.join(ROOT, "mxfp4_expert_gemv_amd", "csrc", f)
-                  for f in ("moe_kernels.hip", "moe_kernels.h", "moe_device.h", "moe_layout.h")]
+                  for f in ("moe_kernels.hip", "moe_kernels_flash.hip", "moe_kernels.h", "moe_device.h", "moe_layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_stack_t1.md")
 
 
@@ -504,15 +504,17 @@ def kernel_bytes(shape, T, distinct):
 
 def kernel_names(variant, T):
     """Full names of the kernels of a 1-2 token layer as the profiler lists them, from the library's
-    variant string (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-<launch>[-jit][-mfma])."""
+    variant string (gfx950-3k-gu<waves>x<blocks per lane>-dn<ksub>x<iters>-<launch>[-jit][-mfma][-flash]).
+    "-flash": the ahead-of-time build with the layer shape folded in, in namespace moe::flash."""
     parts = variant.split("-")
     gu, dn = parts[2:4]
     bpl = int(gu[2:].split("x")[1])
     ksub, iters = (int(v) for v in dn[2:].split("x"))
     mf = "true" if "mfma" in parts[4:] else "false"
-    return {"router": f"void moe::k1_router<{T}, {bpl}, {mf}, false>(moe::K1Args)",
-            "gateup": f"void moe::k2_gateup<{T}, {bpl}, {4 if T == 1 else 2}, {mf}, false>(moe::K2Args)",
-            "down": f"void moe::k3_down<{ksub}, {iters}, {T}, {T}, false>(moe::K3Args)"}
+    ns = "moe::flash::" if "flash" in parts[4:] else "moe::"
+    return {"router": f"void {ns}k1_router<{T}, {bpl}, {mf}, false>({ns}K1Args)",
+            "gateup": f"void {ns}k2_gateup<{T}, {bpl}, {4 if T == 1 else 2}, {mf}, false>({ns}K2Args)",
+            "down": f"void {ns}k3_down<{ksub}, {iters}, {T}, {T}, false>({ns}K3Args)"}
 
 
 def time_head(moe, dev, stream, steps=50, warmup=5):

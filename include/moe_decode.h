@@ -101,6 +101,13 @@ typedef enum {
                                     的"; devotd.net, section 2) is the same in both; measured on the
                                     42-layer stack it is faster at 4 tokens (the verify step) and slower at
                                     1, so it is a choice per handle, not the default. */
+#define MOE_F_GENERIC 0x20u      /* use the shape-generic ahead-of-time kernels, which read the layer shape
+                                    from their arguments.  Without it, a handle whose shape is the MoE
+                                    layer of the pages' model (hidden 2560, 512 routed experts, top-8, 1
+                                    shared, width 768: tanhow.com, section "Ling 3.0 是什么") runs a build
+                                    of the same kernels with that shape folded in at compile time (as
+                                    MOE_F_JIT does at run time), which computes the same results.  No
+                                    effect with MOE_F_JIT. */
 
 typedef struct moe_decode_handle moe_decode_handle;
 typedef struct fp8_head_handle fp8_head_handle;

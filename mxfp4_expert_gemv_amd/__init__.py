@@ -24,6 +24,7 @@ F_RMSNORM_INPUT = 0x1
 F_DIRECT_LAUNCH = 0x2
 F_JIT = 0x8
 F_MFMA = 0x10
+F_GENERIC = 0x20  # shape-generic kernels even for the flash layer shape
 
 # every symbol the header declares
 EXPORTS = ("moe_decode_create", "moe_decode_set_layer", "moe_decode_run", "moe_decode_query",

@@ -80,6 +80,8 @@ struct moe_decode_handle {
     uint64_t span_n[MOE_TIMING_CLASSES] = {}, gap_n[MOE_TIMING_CLASSES] = {};
     // kernels compiled at run time for this shape (MOE_F_JIT)
     bool jit_on = false;
+    // the ahead-of-time build with this shape folded in (moe::flash), unless MOE_F_GENERIC
+    bool flash = false;
     moe::JitResult jit{};
 };
 
@@ -132,7 +134,7 @@ static moe_status check_config(const moe_decode_config* c) {
     if (c->inter % moe::kBlock || !moe::shape_supported(sh))
         return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d: no kernel for this shape (inter 64, 128, 256 or 768)",
                     c->hidden, c->inter);
-    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_JIT | MOE_F_MFMA))
+    if (c->flags & ~(uint32_t)(MOE_F_RMSNORM_INPUT | MOE_F_DIRECT_LAUNCH | MOE_F_JIT | MOE_F_MFMA | MOE_F_GENERIC))
         return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return MOE_OK;
 }
@@ -242,6 +244,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config* cfg, void* stre
         }
         h->jit_on = true;
     }
+    h->flash = !h->jit_on && !(cfg->flags & MOE_F_GENERIC) && moe::flash::shape_matches(sh);
     *out = h;
     g_err[0] = 0;
     return MOE_OK;
@@ -318,7 +321,8 @@ static moe_status enqueue_run(moe_decode_handle* h, const void* x, int32_t T, co
             for (int k = 0; k < MOE_TIMING_CLASSES; ++k)
                 p.stamp[k] = moe::layer_grid(sh, T, k) ? h->stamps + h->stamp_off[(size_t)l * MOE_TIMING_CLASSES + k]
                                                        : nullptr;
-        hipError_t e = moe::launch_layer(sh, T, lp, p, norm, stream, ev, h->jit_on ? &h->jit.kernels : nullptr);
+        hipError_t e = h->flash ? moe::flash::launch_layer(sh, T, lp, p, norm, stream, ev, nullptr)
+                                : moe::launch_layer(sh, T, lp, p, norm, stream, ev, h->jit_on ? &h->jit.kernels : nullptr);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "layer %d launch failed: %s", l, hipGetErrorString(e));
     }
     return MOE_OK;
@@ -509,9 +513,9 @@ extern "C" moe_status moe_decode_query(const moe_decode_handle* h, moe_decode_in
         return fail(MOE_ERR_INVALID_ARG, "info struct_size %u != %zu", info->struct_size, sizeof(moe_decode_info));
     const Shape& sh = h->sh;
     memset(info->variant, 0, sizeof info->variant);
-    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s%s%s", sh.gw(), sh.bpl(), sh.ksub(),
-             sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph", h->jit_on ? "-jit" : "",
-             (h->cfg.flags & MOE_F_MFMA) ? "-mfma" : "");
+    snprintf(info->variant, sizeof info->variant, "gfx950-3k-gu%dx%d-dn%dx%d-%s%s%s%s", sh.gw(), sh.bpl(),
+             sh.ksub(), sh.iters(), (h->cfg.flags & MOE_F_DIRECT_LAUNCH) ? "direct" : "graph", h->jit_on ? "-jit" : "",
+             (h->cfg.flags & MOE_F_MFMA) ? "-mfma" : "", h->flash ? "-flash" : "");
     info->weight_bytes = h->layer_bytes * (uint64_t)h->cfg.num_layers;
     info->workspace_bytes = h->ws_bytes;
     const uint64_t expert = sh.w13_bytes_per_expert() + sh.w13s_bytes_per_expert() + sh.w2_bytes_per_expert() +

@@ -14,7 +14,14 @@
 #define MOE_SHAPE(name, runtime) (runtime)
 #endif
 
-namespace moe {
+// Namespace of the kernels and their argument structs: moe, or a nested one in a build with the
+// shape folded in ahead of time (moe_kernels_flash.hip), so that both builds link into one library.
+#ifndef MOE_KERNELS_NS_BEGIN
+#define MOE_KERNELS_NS_BEGIN namespace moe {
+#define MOE_KERNELS_NS_END }
+#endif
+
+MOE_KERNELS_NS_BEGIN
 
 // Timing record of a graph-replayed pass (moe_decode_timing_enable, mode 1): the kernels' STAMP
 // instances write, from thread 0 of every workgroup, the device's constant-rate wall clock at the
@@ -1278,4 +1285,4 @@ __global__ __launch_bounds__(768) void k3_down(K3Args a) {
     stamp_end<STAMP>(a.stamp);
 }
 
-}  // namespace moe
+MOE_KERNELS_NS_END

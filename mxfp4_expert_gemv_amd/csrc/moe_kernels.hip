@@ -38,7 +38,12 @@
 #include "moe_kernels.h"
 #include "moe_launch.h"
 
-namespace moe {
+MOE_KERNELS_NS_BEGIN
+
+// The repack kernels, the grid sizes of the timing record and the run-time compiled kernel names
+// belong to the shape-generic build only; a build with the shape folded in (MOE_SHAPE_H defined)
+// contributes its layer launcher.
+#ifndef MOE_SHAPE_H
 
 // ------------------------------------------------------------------------------------------------
 // repack kernels (canonical row-major -> lane tiles; pure permutations of 16-byte units / bytes)
@@ -201,8 +206,11 @@ hipError_t launch_repack(const Shape& sh, const void* router, const void* w13, c
     return hipGetLastError();
 }
 
-int routed_slots_max(const Shape& sh, int T) { return T * sh.k < sh.E ? T * sh.k : sh.E; }
+#endif  // MOE_SHAPE_H
 
+static int routed_slots_max(const Shape& sh, int T) { return T * sh.k < sh.E ? T * sh.k : sh.E; }
+
+#ifndef MOE_SHAPE_H
 __global__ void clear_u64(unsigned long long* p, uint64_t n) {
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
         p[i] = 0ull;
@@ -212,6 +220,7 @@ hipError_t launch_clear_u64(unsigned long long* p, uint64_t n, hipStream_t strea
     clear_u64<<<grid_for(n, 256), 256, 0, stream>>>(p, n);
     return hipGetLastError();
 }
+#endif  // MOE_SHAPE_H
 
 // Launch decisions shared by the ahead-of-time launcher and the list of kernels compiled at run time.
 // Top-k waves per token in the 1-2 token gate/up workgroups (workgroups of at least T W waves).
@@ -223,6 +232,7 @@ static int gateup_wt(const Shape& sh, int T) {
 // hide the LDS latency of its dot phase), with two unit groups per wave.
 static bool down_two_per_cu(const Shape& sh, int T) { return T >= 3 && sh.H % (2 * kDownGrid) == 0; }
 
+#ifndef MOE_SHAPE_H
 int layer_grid(const Shape& sh, int T, int kind) {
     const bool central = T >= 3;
     const int tiles = sh.gu_tiles(), n_router_wg = (sh.E + sh.gw() - 1) / sh.gw();
@@ -248,6 +258,7 @@ bool jit_kernel_names(const Shape& sh, int T, bool mfma, std::string (&names)[kL
                        ", " + std::to_string(down_two_per_cu(sh, T) ? 2 : T) + ">";
     return true;
 }
+#endif  // MOE_SHAPE_H
 
 // One kernel launch: the ahead-of-time instance kern, or the run-time compiled function jf when there
 // is one; in timing mode (ev) a launch whose start/stop events carry the kernel's own begin and end.
@@ -355,10 +366,15 @@ template <int T, int BPL, bool STAMP>
 static hipError_t launch_layer_s(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                  hipStream_t stream, hipEvent_t* ev, const JitKernels* jit) {
     const int ks = sh.ksub(), it = sh.iters();
+#ifdef MOE_FIXED_KSUB  // a build for one shape: only its down-kernel geometry
+    if (ks == MOE_FIXED_KSUB && it == MOE_FIXED_ITERS)
+        return launch_layer_t<T, BPL, MOE_FIXED_KSUB, MOE_FIXED_ITERS, STAMP>(sh, L, P, normalize, stream, ev, jit);
+#else
     if (ks == 8 && it == 3) return launch_layer_t<T, BPL, 8, 3, STAMP>(sh, L, P, normalize, stream, ev, jit);
     if (ks == 8 && it == 1) return launch_layer_t<T, BPL, 8, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
     if (ks == 4 && it == 1) return launch_layer_t<T, BPL, 4, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
     if (ks == 2 && it == 1) return launch_layer_t<T, BPL, 2, 1, STAMP>(sh, L, P, normalize, stream, ev, jit);
+#endif
     return hipErrorInvalidValue;
 }
 
@@ -374,8 +390,13 @@ static hipError_t launch_layer_b(const Shape& sh, const LayerPtrs& L, const RunP
 template <int T>
 static hipError_t launch_layer_tt(const Shape& sh, const LayerPtrs& L, const RunPtrs& P, bool normalize,
                                   hipStream_t stream, hipEvent_t* ev, const JitKernels* jit) {
+#ifdef MOE_FIXED_BPL  // a build for one shape: only its gate/up geometry
+    return sh.bpl() == MOE_FIXED_BPL ? launch_layer_b<T, MOE_FIXED_BPL>(sh, L, P, normalize, stream, ev, jit)
+                                     : hipErrorInvalidValue;
+#else
     return sh.bpl() == 8 ? launch_layer_b<T, 8>(sh, L, P, normalize, stream, ev, jit)
                          : launch_layer_b<T, 4>(sh, L, P, normalize, stream, ev, jit);
+#endif
 }
 
 hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
@@ -389,6 +410,7 @@ hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtr
     }
 }
 
+#ifndef MOE_SHAPE_H
 bool shape_supported(const Shape& sh) {
     if (sh.H % 256 || sh.H > 2560 || sh.I % kBlock) return false;
     if (sh.gw() < 1 || sh.gw() > kMaxWaves) return false;
@@ -397,4 +419,6 @@ bool shape_supported(const Shape& sh) {
     return (ks == 8 && (it == 1 || it == 3)) || (ks == 4 && it == 1) || (ks == 2 && it == 1);
 }
 
-}  // namespace moe
+#endif  // MOE_SHAPE_H
+
+MOE_KERNELS_NS_END

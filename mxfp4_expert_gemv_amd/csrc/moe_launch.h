@@ -65,6 +65,14 @@ hipError_t launch_clear_u64(unsigned long long* p, uint64_t n, hipStream_t strea
 bool jit_kernel_names(const Shape& sh, int T, bool mfma, std::string (&names)[kLayerKernels]);
 bool shape_supported(const Shape& sh);
 
+// The same layer launcher built with one layer shape folded in at compile time
+// (moe_kernels_flash.hip): for shapes where shape_matches holds.
+namespace flash {
+bool shape_matches(const Shape& sh);
+hipError_t launch_layer(const Shape& sh, int T, const LayerPtrs& L, const RunPtrs& P, bool normalize,
+                        hipStream_t stream, hipEvent_t* ev, const JitKernels* jit);
+}  // namespace flash
+
 }  // namespace moe
 
 // Records a message for moe_last_error() and returns s (defined in moe_api.cpp).

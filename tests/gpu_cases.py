@@ -67,7 +67,9 @@ class DeviceLayer:
 # the kernel builds behind the same calls: compiled ahead of time (default), compiled at run time for
 # the handle's shape (MOE_F_JIT), and the gate/up dot products on the scaled matrix cores
 # (MOE_F_MFMA); the MoE parity tests run on each
-VARIANTS = {"aot": 0, "jit": moe.F_JIT, "mfma": moe.F_MFMA}
+# aot: the ahead-of-time kernels (for the flash layer shape, the build with that shape folded in);
+# generic: the shape-generic ahead-of-time kernels on every shape
+VARIANTS = {"aot": 0, "generic": moe.F_GENERIC, "jit": moe.F_JIT, "mfma": moe.F_MFMA}
 _variant = {"flags": 0}
 
 

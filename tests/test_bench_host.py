@@ -33,6 +33,9 @@ def test_kernel_names_follow_the_variant_string():
     n = bench.kernel_names("gfx950-3k-gu5x8-dn8x3-graph-jit-mfma", 2)
     assert n["router"] == "void moe::k1_router<2, 8, true, false>(moe::K1Args)"
     assert n["gateup"] == "void moe::k2_gateup<2, 8, 2, true, false>(moe::K2Args)"
+    n = bench.kernel_names("gfx950-3k-gu5x8-dn8x3-graph-flash", 1)
+    assert n["gateup"] == "void moe::flash::k2_gateup<1, 8, 4, false, false>(moe::flash::K2Args)"
+    assert n["down"] == "void moe::flash::k3_down<8, 3, 1, 1, false>(moe::flash::K3Args)"
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):

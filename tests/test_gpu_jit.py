@@ -59,22 +59,28 @@ def test_compile_then_cache_hit(cache_dir):
     assert len({i1["jit_code_object"], i3["jit_code_object"], i4["jit_code_object"]}) == 3
 
 
+@pytest.mark.parametrize("norm", [0, moe.F_RMSNORM_INPUT], ids=["raw", "rmsnorm"])
 @pytest.mark.parametrize("base", [0, moe.F_MFMA], ids=["valu", "mfma"])
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
-def test_jit_kernels_match_the_ahead_of_time_kernels_bit_for_bit(cache_dir, T, base):
+def test_jit_kernels_match_the_ahead_of_time_kernels_bit_for_bit(cache_dir, T, base, norm):
+    """The run-time compiled kernels, the ahead-of-time build with the flash shape folded in and the
+    shape-generic ahead-of-time build compute the same bytes."""
     m = MANIFEST["layer_t4"]
     shape = synth.FLASH
     lay = DeviceLayer(shape, m["seed"])
     x = synth.tokens(shape.hidden, m["seed"], 4, m["x_attempt"])[:T]
     out = {}
-    for name, flags in (("aot", base), ("jit", base | moe.F_JIT)):
-        h = _create(shape, flags)
+    for name, flags in (("aot", base), ("generic", base | moe.F_GENERIC), ("jit", base | moe.F_JIT)):
+        h = _create(shape, flags | norm)
+        tags = moe.moe_decode_query(h)["variant"].split("-")[5:]
+        assert ("flash" in tags) == (name == "aot"), (name, tags)
         lay.set_into(h, 0)
         out[name] = run_layer(h, shape, x)
         moe.moe_decode_destroy(h)
-    for k in ("y", "topk_ids", "topk_w", "x_scale", "x_codes"):
-        a, b = out["aot"][k], out["jit"][k]
-        assert (a.view(np.uint8) == b.view(np.uint8)).all(), k
+    for other in ("generic", "jit"):
+        for k in ("y", "topk_ids", "topk_w", "x_scale", "x_codes"):
+            a, b = out["aot"][k], out[other][k]
+            assert (a.view(np.uint8) == b.view(np.uint8)).all(), (other, k)
 
 
 def test_unwritable_cache_still_compiles(cache_dir, monkeypatch):

@@ -214,6 +214,7 @@ def test_query_reports_variant_and_bytes(flash_t1, variant):
     tags = info["variant"].split("-")[5:]
     assert info["variant"].startswith("gfx950-3k")
     assert ("jit" in tags) == (variant == "jit") and ("mfma" in tags) == (variant == "mfma")
+    assert ("flash" in tags) == (variant in ("aot", "mfma"))  # the build with the flash shape folded in
     assert info["bytes_per_layer_t1"] == 30_822_400
 
 
