@@ -3,15 +3,45 @@
 // moe_kernels.hip) and, for one layer shape at a time, at run time by hipRTC (moe_jit.cpp): there
 // the macros MOE_SHAPE_H, _E, _K, _S, _I and _NORM fix the layer's shape and input normalisation at
 // compile time (MOE_SHAPE below), so that the compiler folds the divisions and loop bounds that the
-// ahead-of-time build takes from the kernel arguments.  Private to the library.
+// shape-generic ahead-of-time build takes from the kernel arguments; moe_kernels_flash.hip does the
+// same ahead of time for one shape (each macro left undefined stays a run-time value).  Private to
+// the library.
 #pragma once
 #include "moe_device.h"
 #include "moe_layout.h"
 
+// MOE_SHAPE(name, runtime): the compile-time constant MOE_SHAPE_<name> where the build defines it,
+// else the run-time expression.
+#define MOE_SHAPE(name, runtime) MOE_SHAPE_SEL_##name(runtime)
 #ifdef MOE_SHAPE_H
-#define MOE_SHAPE(name, runtime) (MOE_SHAPE_##name)
+#define MOE_SHAPE_SEL_H(r) (MOE_SHAPE_H)
 #else
-#define MOE_SHAPE(name, runtime) (runtime)
+#define MOE_SHAPE_SEL_H(r) (r)
+#endif
+#ifdef MOE_SHAPE_E
+#define MOE_SHAPE_SEL_E(r) (MOE_SHAPE_E)
+#else
+#define MOE_SHAPE_SEL_E(r) (r)
+#endif
+#ifdef MOE_SHAPE_K
+#define MOE_SHAPE_SEL_K(r) (MOE_SHAPE_K)
+#else
+#define MOE_SHAPE_SEL_K(r) (r)
+#endif
+#ifdef MOE_SHAPE_S
+#define MOE_SHAPE_SEL_S(r) (MOE_SHAPE_S)
+#else
+#define MOE_SHAPE_SEL_S(r) (r)
+#endif
+#ifdef MOE_SHAPE_I
+#define MOE_SHAPE_SEL_I(r) (MOE_SHAPE_I)
+#else
+#define MOE_SHAPE_SEL_I(r) (r)
+#endif
+#ifdef MOE_SHAPE_NORM
+#define MOE_SHAPE_SEL_NORM(r) (MOE_SHAPE_NORM)
+#else
+#define MOE_SHAPE_SEL_NORM(r) (r)
 #endif
 
 // Namespace of the kernels and their argument structs: moe, or a nested one in a build with the

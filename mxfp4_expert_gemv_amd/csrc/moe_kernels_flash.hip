@@ -3,14 +3,14 @@
 // of the pages' model: tanhow.com, "NVIDIA 在单台 DGX Spark 上叠加三项优化...", section "Ling 3.0 是什么").
 // The shape is folded in at compile time, as in the run-time compiled kernels (MOE_F_JIT), so that the
 // compiler resolves the divisions, loop bounds and tile counts that the shape-generic build takes
-// from the kernel arguments.  The input normalisation stays a run-time argument.  Everything lands in
-// namespace moe::flash; handles of this shape use it unless created with MOE_F_GENERIC.
+// from the kernel arguments.  The input normalisation (MOE_SHAPE_NORM, left undefined) stays a
+// run-time argument.  Everything lands in namespace moe::flash; handles of this shape use it unless
+// created with MOE_F_GENERIC.
 #define MOE_SHAPE_H 2560
 #define MOE_SHAPE_E 512
 #define MOE_SHAPE_K 8
 #define MOE_SHAPE_S 1
 #define MOE_SHAPE_I 768
-#define MOE_SHAPE_NORM (a.normalize)
 // the gate/up and down geometry that shape implies (Shape::bpl, ksub, iters): the only instances built
 #define MOE_FIXED_BPL 8
 #define MOE_FIXED_KSUB 8
