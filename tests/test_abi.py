@@ -58,6 +58,32 @@ def test_valid_config_without_device_is_no_device():
     assert _status({"hidden": 256, "num_experts": 16, "top_k": 2, "inter": 64}) == -6
 
 
+def _header_flags():
+    text = open(os.path.join(ROOT, "include", "moe_decode.h")).read()
+    return {m.group(1): int(m.group(2), 16) for m in re.finditer(r"#define MOE_F_(\w+) (0x[0-9a-fA-F]+)u", text)}
+
+
+def test_binding_flags_match_the_header():
+    flags = _header_flags()
+    assert set(flags) == {"RMSNORM_INPUT", "DIRECT_LAUNCH", "JIT", "MFMA", "GENERIC"}
+    for name, value in flags.items():
+        assert getattr(moe, "F_" + name) == value, name
+
+
+def test_every_documented_flag_passes_validation_and_other_bits_are_refused():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    known = 0
+    for value in _header_flags().values():
+        known |= value
+        assert _status({"flags": value}) == -6  # valid: only the missing device stops create
+    assert _status({"flags": known}) == -6
+    for bit in range(32):
+        if not (known >> bit) & 1:
+            assert _status({"flags": 1 << bit}) == -1, bit
+
+
 def test_null_arguments():
     L = moe.lib()
     assert L.moe_decode_create(None, None, None) == -1
