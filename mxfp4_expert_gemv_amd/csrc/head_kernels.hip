@@ -364,8 +364,10 @@ hipError_t launch_repack_head(const void* w, const void* s, void* dw, void* ds, 
     return hipGetLastError();
 }
 
-// The grid: as many workgroups as the device holds at once (each walks tiles blockIdx.x, + grid,
-// ...), at most one per tile.
+// The grid: at most as many workgroups as the device holds at once (each walks tiles blockIdx.x,
+// + grid, ...), and no more than the number of rounds those need: with the tiles spread evenly, the
+// last round keeps nearly every workgroup busy (157,184 rows: 492 workgroups of 5 tiles, not 512 of
+// which 104 idle through the fifth round).
 template <int T, bool FP8, bool RM>
 static hipError_t launch_head_tt(const HeadArgs& a, hipStream_t stream) {
     const unsigned block = kWave * (a.H / kSlice);
@@ -375,7 +377,8 @@ static hipError_t launch_head_tt(const HeadArgs& a, hipStream_t stream) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, head_mfma<T, FP8, RM>, block, lds);
     if (e != hipSuccess) return e;
-    const int grid = std::min(a.VT, std::max(per_cu, 1) * std::max(cus, 1));
+    const int cap = std::max(per_cu, 1) * std::max(cus, 1), rounds = (a.VT + cap - 1) / cap;
+    const int grid = (a.VT + rounds - 1) / rounds;
     head_mfma<T, FP8, RM><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
