@@ -140,7 +140,7 @@ __device__ void head_finish(const HeadArgs& a, const float (&bv)[T], const int (
         }
     }
     // the last workgroup to arrive reduces the partials.  Ordering rests on the ISA, not on
-    // release/acquire (an L2 write-back in every workgroup made the head ten times slower): the
+    // release/acquire (its L2 write-back in every workgroup costs the head about 15 us): the
     // partials are agent-scope atomic stores, written through to the device-coherent level,
     // vmcnt(0) waits for the memory's acknowledgement before the arrival, and the last workgroup
     // reads them with agent-scope atomic loads, which do not hit in the non-coherent L2.
