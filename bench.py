@@ -616,7 +616,9 @@ def hbm_probe(moe, torch, dev, stream, nbytes=4 << 30, reps=10):
 
 
 def environment(torch):
-    """GPU, ROCm version and clocks of the box the numbers were taken on."""
+    """GPU, ROCm version and clocks of the box the numbers were taken on.  rocm-smi is sampled after
+    the runs, with the GPU at rest, so its clock levels are the idle ones, not those of the timed
+    kernels."""
     import subprocess
     env = {"gpu": torch.cuda.get_device_name(0),
            "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
@@ -628,9 +630,9 @@ def environment(torch):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
             lines = [l.strip() for l in r.stdout.splitlines() if "GPU[" in l]
-            env[" ".join(cmd[1:])] = lines[:12]
+            env[" ".join(cmd[1:]) + " (GPU at rest)"] = lines[:12]
         except (OSError, subprocess.SubprocessError):
-            env[" ".join(cmd[1:])] = None
+            env[" ".join(cmd[1:]) + " (GPU at rest)"] = None
     return env
 
 
