@@ -54,6 +54,61 @@ def test_small_head_matches_oracle(V, T, H):
             assert am[t] == am_o[t]
 
 
+# 1,030 tiles of 64 rows, the last of 37: more tiles than the device's resident workgroups hold, so
+# each workgroup walks several tiles (rounds), and the grid sized to those rounds leaves a few
+# workgroups one tile fewer.
+MULTI_V = 64 * 1029 + 37
+
+
+@pytest.fixture(scope="module")
+def multi_round_head():
+    return _quantised(MULTI_V, 2560, seed=13)
+
+
+def test_multi_round_ragged_head_matches_oracle(multi_round_head):
+    """Every logit of a head whose tiles take several rounds, with a ragged last tile, within the
+    oracle's fp32 evaluation bound; the argmax exact where it is well posed (1 and 4 tokens)."""
+    Wq, s = multi_round_head
+    for T in (1, 4):
+        x = synth.tokens(2560, 13 + T, T)
+        lg_o, bd_o, am_o = oracle.head_logits(Wq, s, x)
+        am, lg = _run(Wq, s, x)
+        bad = np.argwhere(np.abs(lg - lg_o) > bd_o)
+        assert bad.size == 0, f"T={T}: {len(bad)} logits outside the bound, first (token, row) {bad[:3].tolist()}"
+        for t in range(T):
+            if oracle.argmax_margin_ok(lg_o[t], bd_o[t]):
+                assert am[t] == am_o[t], f"T={T} token {t}: {am[t]} against {am_o[t]}"
+
+
+def test_multi_round_duplicates_lowest_index_wins(multi_round_head):
+    """Copies of the winning row spread over rounds and workgroups.  Copies at higher indices (later
+    rounds, the ragged last tile) must lose to the original; copies then added at lower indices (the
+    same workgroup's earlier rounds, the first tile) must win, the lowest index each time.  Equal rows
+    give bit-equal logits (same products in the same order), so only the cross-tile and
+    cross-workgroup reductions decide the index."""
+    Wq0, s0 = multi_round_head
+    x = synth.tokens(2560, 9, 1)
+    lg_o, bd_o, am_o = oracle.head_logits(Wq0, s0, x)
+    assert oracle.argmax_margin_ok(lg_o[0], bd_o[0]), "fixture: the winner must be well separated"
+    r = int(am_o[0])
+    tiles, tr = (MULTI_V + 63) // 64, r // 64
+    stride = -(-tiles // 3)  # a workgroup's step between tiles when they take three rounds (512 resident)
+    higher = sorted(i for i in {MULTI_V - 1, 64 * (tiles - 2) + 63, *(64 * t + 7 for t in (tr + stride, tr + 2 * stride)
+                                                                        if t < tiles)} if i > r)
+    lower = sorted((i for i in {*(64 * t + 5 for t in (tr - stride, tr - 2 * stride) if t >= 0), 3} if i < r),
+                   reverse=True)
+    assert len(higher) >= 2 and len(lower) >= 2, (r, higher, lower)
+    Wq, s = Wq0.copy(), s0.copy()
+    for i in higher:
+        Wq[i], s[i] = Wq0[r], s0[r]
+    am, _ = _run(Wq, s, x, want_logits=False)
+    assert am[0] == r, f"copies at {higher} of row {r}: got {am[0]}"
+    for i in lower:
+        Wq[i], s[i] = Wq0[r], s0[r]
+        am, _ = _run(Wq, s, x, want_logits=False)
+        assert am[0] == i, f"copies of row {r} down to {i}: got {am[0]}"
+
+
 def test_duplicate_rows_lowest_index_wins():
     V, H = 500, 2560
     Wq, s = _quantised(V, H, seed=9)
@@ -162,7 +217,7 @@ def _run_bf16(Wb, x):
     return am.cpu().numpy(), lg.cpu().numpy()
 
 
-@pytest.mark.parametrize("V,T,H", [(3000, 4, 2560), (64 * 5 + 3, 1, 2560), (200, 3, 512)])
+@pytest.mark.parametrize("V,T,H", [(3000, 4, 2560), (64 * 5 + 3, 1, 2560), (200, 3, 512), (MULTI_V, 4, 2560)])
 def test_bf16_head_matches_oracle(V, T, H):
     """The unquantised BF16 head (the comparison point of the FP8 head): logits within the fp32
     evaluation bound of the oracle's fp64 logits, argmax exact where it is well posed."""
