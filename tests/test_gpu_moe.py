@@ -80,6 +80,30 @@ def test_tiny_shapes_without_shared_and_k1():
         check_layer(shape, gpu, ref_y, ref_tr)
 
 
+# One shape per kernel geometry accepted besides the tiny and flash ones: router and gate/up
+# workgroups of 2, 3, 4 and 5 waves with 8 or 4 MX blocks per lane; down splits of 8 x 1, 4 x 1,
+# 2 x 1 and 8 x 3 lanes x blocks, one or two down workgroups per CU at 3-4 tokens; router grids
+# whose last workgroup holds fewer experts than waves; no shared expert.
+MID_SHAPES = [synth.Shape(1024, 128, 4, 1, 256), synth.Shape(1536, 200, 6, 1, 128), synth.Shape(2048, 256, 8, 1, 768),
+              synth.Shape(1280, 128, 8, 0, 64), synth.Shape(768, 40, 3, 1, 256)]
+
+
+@pytest.mark.parametrize("shape", MID_SHAPES,
+                         ids=lambda s: f"H{s.hidden}-E{s.num_experts}-k{s.top_k}-S{s.num_shared}-I{s.inter}")
+def test_mid_shapes_every_geometry(shape):
+    """Each geometry at 1, 2, 3 and 4 tokens through one handle: ids exact, weights, activation
+    scale and codes, and y against the oracle."""
+    lay = DeviceLayer(shape, 41)
+    h = create(shape)
+    lay.set_into(h, 0)
+    for T in (1, 2, 3, 4):
+        _, x = margin_attempt(shape, lay.router_host, 41, T)
+        print(f"shape {shape} T={T}", flush=True)
+        gpu, ref_y, ref_tr = _layer_case(shape, 41, x, lay, h)
+        check_layer(shape, gpu, ref_y, ref_tr)
+    moe.moe_decode_destroy(h)
+
+
 def _wide_range_attempt(shape, router_host, seed, T):
     for a in range(1000):
         x = synth.tokens_wide_range(shape.hidden, seed, T, a)
