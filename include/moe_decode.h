@@ -177,7 +177,9 @@ moe_status moe_decode_set_layer(moe_decode_handle* h, int32_t layer, const moe_l
  * MOE_F_DIRECT_LAUNCH is set, the first call with a given (x, T, outputs) captures the kernel
  * sequence (three kernels per layer, plus two small ones per layer at 3-4 tokens) into a HIP graph
  * owned by the handle and every later call with the same arguments replays it (up to 16 graphs;
- * they hold pointers, not data, so new contents of x and new weights are picked up). */
+ * they hold pointers, not data, so new contents of x and new weights are picked up).  A call with a
+ * 17th set of arguments waits for the device to finish its queued work (hipDeviceSynchronize),
+ * then drops the 16 graphs and captures anew; so does moe_decode_timing_enable. */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t num_tokens, const moe_outputs* out,
                           void* stream);
 

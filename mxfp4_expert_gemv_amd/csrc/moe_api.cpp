@@ -85,7 +85,10 @@ struct moe_decode_handle {
     moe::JitResult jit{};
 };
 
+// Frees the timing record; queued runs may still record its events or write its stamps, so the
+// device is drained first.
 static void free_events(moe_decode_handle* h) {
+    if (!h->events.empty() || h->stamps) (void)hipDeviceSynchronize();
     for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
     h->events.clear();
     h->timing_T.clear();
@@ -148,7 +151,12 @@ static moe_status device_present() {
     return MOE_OK;
 }
 
+// Destroys the captured graphs.  run only enqueues, so launches of them may still be executing on
+// the callers' streams: the device is drained first (this happens when the 16 entries are full, on
+// timing changes and at destroy, not on the replay path).
 static void free_graphs(moe_decode_handle* h) {
+    if (h->graphs.empty()) return;
+    (void)hipDeviceSynchronize();
     for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
     h->graphs.clear();
 }

@@ -11,8 +11,8 @@ import torch
 import mxfp4_expert_gemv_amd as moe
 import oracle
 import synth
-from gpu_cases import (MANIFEST, VARIANTS, DeviceLayer, check_layer, create, margin_attempt, normwise_err, run_layer,
-                       set_variant, to_dev_u16)
+from gpu_cases import (MANIFEST, VARIANTS, DeviceLayer, bf16_bits, check_layer, create, dev, margin_attempt,
+                       normwise_err, run_layer, set_variant, to_dev_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -344,3 +344,106 @@ def test_graph_replay_timing_record(flash_t1):
     recorded = sum(t[c]["total_ms"] + t[c]["gap_ms"] for c in moe.TIMING_CLASSES)
     assert 0 < recorded <= e0.elapsed_time(e1)
     assert (got["y"] == ref["y"]).all()
+
+
+def _fixed_outputs(shape, T):
+    """One set of output buffers; runs that pass the same set (and x, T) replay one captured graph."""
+    H, k = shape.hidden, shape.top_k
+    f32 = dict(dtype=torch.float32, device=dev())
+    return {"y": torch.full((T, H), float("nan"), **f32),
+            "x_out": torch.empty((T, H), dtype=torch.bfloat16, device=dev()),
+            "topk_ids": torch.full((1, T, k), -1, dtype=torch.int32, device=dev()),
+            "topk_w": torch.full((1, T, k), float("nan"), **f32),
+            "x_trace": torch.empty((1, T, H), dtype=torch.bfloat16, device=dev()),
+            "x_scale": torch.full((1, T), float("nan"), **f32),
+            "x_codes": torch.empty((1, T, H), dtype=torch.uint8, device=dev())}
+
+
+def _read(out):
+    res = {n: t.cpu().numpy() for n, t in out.items() if t.dtype != torch.bfloat16}
+    res["x_out"] = bf16_bits(out["x_out"])
+    res["x_trace"] = bf16_bits(out["x_trace"])
+    return res
+
+
+def _assert_same(a, b, what):
+    for n in a:
+        assert np.array_equal(a[n], b[n], equal_nan=True), f"{what}: {n} differs"
+
+
+def test_direct_launch_equals_graph_replay():
+    """MOE_F_DIRECT_LAUNCH (the kernels enqueued at every run) and the default captured-graph replay
+    give bit-identical outputs, tiny and flash layers at 1-4 tokens."""
+    for shape, seed in ((synth.TINY, 7), (synth.FLASH, 7)):
+        lay = DeviceLayer(shape, seed)
+        hg, hd = create(shape), create(shape, flags=moe.F_DIRECT_LAUNCH)
+        lay.set_into(hg, 0)
+        lay.set_into(hd, 0)
+        for T in (1, 2, 3, 4):
+            _, x = margin_attempt(shape, lay.router_host, seed, T)
+            print(f"shape {shape} T={T}", flush=True)
+            _assert_same(run_layer(hg, shape, x), run_layer(hd, shape, x), f"{shape} T={T}")
+        moe.moe_decode_destroy(hg)
+        moe.moe_decode_destroy(hd)
+
+
+def test_graph_replay_picks_up_new_inputs_and_weights():
+    """A graph is captured per (x, T, outputs) and holds pointers: replays with new contents of x, and
+    after set_layer has replaced the layer's weights, compute the new results (checked against the
+    oracle each time)."""
+    shape, T = synth.TINY, 2
+    la, lb = DeviceLayer(shape, 50), DeviceLayer(shape, 51)
+    h = create(shape)
+    la.set_into(h, 0)
+    a1, x1 = margin_attempt(shape, la.router_host, 50, T)
+    _, x2 = margin_attempt(shape, la.router_host, 50, T, start=a1 + 1)
+    _, x3 = margin_attempt(shape, lb.router_host, 51, T)
+    xd = to_dev_u16(x1)
+    out = _fixed_outputs(shape, T)
+
+    def run_and_check(lay, x):
+        moe.moe_decode_run(h, xd, T, **out)
+        torch.cuda.synchronize()
+        moe.moe_decode_check(h)
+        ro = oracle.route(shape, lay.router_host, x)
+        ref_y, ref_tr = oracle.moe_layer(shape, lay.router_host, lay.oracle_experts(ro["ids"]), x)
+        check_layer(shape, _read(out), ref_y, ref_tr)
+
+    run_and_check(la, x1)  # captured
+    run_and_check(la, x1)  # replayed
+    xd.copy_(to_dev_u16(x2))
+    run_and_check(la, x2)  # same graph, new x
+    lb.set_into(h, 0)
+    xd.copy_(to_dev_u16(x3))
+    run_and_check(lb, x3)  # same graph, new weights
+    moe.moe_decode_destroy(h)
+
+
+def test_graph_cache_overflow_with_runs_in_flight():
+    """Twenty distinct output sets enqueued back to back with no host wait: the 17th call frees the
+    16 captured graphs while their launches may still be queued.  Every output equals the
+    direct-launch result, and so do re-captured runs of the first sets."""
+    shape = synth.TINY
+    lay = DeviceLayer(shape, 52)
+    h, hd = create(shape), create(shape, flags=moe.F_DIRECT_LAUNCH)
+    lay.set_into(h, 0)
+    lay.set_into(hd, 0)
+    _, x = margin_attempt(shape, lay.router_host, 52, 1)
+    ref = run_layer(hd, shape, x)
+    xd = to_dev_u16(x)
+    outs = [_fixed_outputs(shape, 1) for _ in range(20)]
+    for o in outs:
+        moe.moe_decode_run(h, xd, 1, **o)
+    torch.cuda.synchronize()
+    moe.moe_decode_check(h)
+    for i, o in enumerate(outs):
+        _assert_same(_read(o), ref, f"output set {i}")
+    for o in outs[:3]:
+        for t in o.values():
+            t.zero_()
+        moe.moe_decode_run(h, xd, 1, **o)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs[:3]):
+        _assert_same(_read(o), ref, f"re-captured output set {i}")
+    moe.moe_decode_destroy(h)
+    moe.moe_decode_destroy(hd)
