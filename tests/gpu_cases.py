@@ -113,6 +113,19 @@ def normwise_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
     return np.where(den > 0, num / np.where(den > 0, den, 1), num)
 
 
+def elementwise_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray, floor: float = 1e-3) -> dict:
+    """For information: |y_gpu - y_ref| / |y_ref| element by element, over the elements with
+    |y_ref| >= floor * max |y_ref| of their token (the elementwise form is ill-posed near zero):
+    median, p99 and maximum, and the fraction of elements covered."""
+    y_gpu = y_gpu.astype(np.float64)
+    y_ref = y_ref.astype(np.float64)
+    den = np.abs(y_ref)
+    keep = den >= floor * den.max(axis=-1, keepdims=True)
+    r = np.abs(y_gpu - y_ref)[keep] / den[keep]
+    return {"median": float(np.median(r)), "p99": float(np.percentile(r, 99)), "max": float(r.max()),
+            "covered": float(keep.mean())}
+
+
 def check_layer(shape, gpu: dict, ref_y: np.ndarray, ref_tr: dict, layer: int = 0, check_codes: bool = True):
     """GPU outputs of one layer against the oracle: ids bit-exact, weights within W_TOL, activation
     scale and codes bit-exact, y within Y_TOL normwise."""
