@@ -517,6 +517,22 @@ def kernel_names(variant, T):
             "down": f"void {ns}k3_down<{ksub}, {iters}, {T}, {T}, false>({ns}K3Args)"}
 
 
+def _event_time_us(fn, stream, steps, warmup):
+    """Mean µs per call of fn over `steps` back-to-back calls, event-timed on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def time_head(moe, dev, stream, steps=50, warmup=5):
     """The FP8 LM head (vocab 157,184 x hidden 2,560, E4M3 rows with fp32 row scales, argmax only)
     at 1 and 4 tokens, back to back (its 403 MB exceed the 256 MB last-level cache).  Random codes
@@ -535,19 +551,19 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
     nbytes = V * H + V * 4
     out = {"vocab": V, "hidden": H, "bytes_per_call": nbytes}
     for T in (1, 4):
-        for _ in range(warmup):
-            moe.fp8_head_run(hd, x[:T], am[:T])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            moe.fp8_head_run(hd, x[:T], am[:T])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = _event_time_us(lambda: moe.fp8_head_run(hd, x[:T], am[:T]), stream, steps, warmup)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[f"t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
         log(f"LM head T={T}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    # the head of a 4-token verify step: the same pass with the greedy acceptance of the 3 drafts
+    # fused into its final reduction
+    draft = torch.zeros((3,), dtype=torch.int32, device=dev)
+    accept = torch.empty((1,), dtype=torch.int32, device=dev)
+    us = _event_time_us(lambda: moe.fp8_head_verify(hd, x, draft, am, accept), stream, steps, warmup)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out["verify_t4"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                        "vs_plain_t4": round(us / out["t4"]["us"], 3)}
+    log(f"LM head verify step T=4 (argmax + acceptance): {us:.1f} us, {us / out['t4']['us']:.3f}x the plain T=4 head")
     moe.fp8_head_destroy(hd)
     # the unquantised BF16 head it replaces (twice the bytes), for the comparison
     wb = (torch.randn((V, H), device=dev) * 0.02).to(torch.bfloat16)
@@ -556,16 +572,7 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
     del wb
     bbytes = V * H * 2
     for T in (1, 4):
-        for _ in range(warmup):
-            moe.fp8_head_run(hb, x[:T], am[:T])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            moe.fp8_head_run(hb, x[:T], am[:T])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = _event_time_us(lambda: moe.fp8_head_run(hb, x[:T], am[:T]), stream, steps, warmup)
         gbs = bbytes / (us * 1e-6) / 1e9
         out[f"bf16_t{T}"] = {"us": round(us, 2), "gb_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                              "fp8_speedup": round(us / out[f"t{T}"]["us"], 3)}
@@ -575,15 +582,7 @@ def time_head(moe, dev, stream, steps=50, warmup=5):
     wf = torch.randn((V, H), device=dev) * 0.02
     codes = torch.empty((V, H), dtype=torch.uint8, device=dev)
     sc = torch.empty((V,), dtype=torch.float32, device=dev)
-    moe.fp8_head_quantize(wf, codes, sc)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(10):
-        moe.fp8_head_quantize(wf, codes, sc)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / 10
+    us = _event_time_us(lambda: moe.fp8_head_quantize(wf, codes, sc), stream, 10, 1)
     qbytes = V * H * 4 + V * H + V * 4
     out["quantize_fp32"] = {"us": round(us, 1), "bytes": qbytes, "gb_s": round(qbytes / (us * 1e-6) / 1e9, 1)}
     log(f"LM head quantisation (fp32 in): {us:.1f} us, {qbytes / (us * 1e-6) / 1e9:.0f} GB/s")
