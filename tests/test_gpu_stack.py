@@ -1,5 +1,5 @@
 """GPU parity of the full-size 42-layer MoE decode stack (hidden 2560, 512 experts, top-8 + 1
-shared, width 768, ~67.6 GB of resident MXFP4 experts), at 1 and 4 tokens, teacher-forced on every
+shared, width 768, ~67.6 GB of resident MXFP4 experts), at 1 to 4 tokens, teacher-forced on every
 layer: the oracle recomputes each layer from the GPU's own input residual x_l (traced by the
 library) and checks the ids (exact wherever the routing is well posed), the FP8 activation scale
 and codes (exact), and the layer's effect on the residual (x_(l+1) within half a bf16 ulp of
@@ -47,7 +47,7 @@ def _ulp_bf16(v):
     return 2.0 ** (e - 7)
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_stack_teacher_forced_every_layer(stack, T):
     shape, h, layers, st = stack
     L = len(layers)
