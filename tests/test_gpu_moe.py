@@ -447,3 +447,33 @@ def test_graph_cache_overflow_with_runs_in_flight():
         _assert_same(_read(o), ref, f"re-captured output set {i}")
     moe.moe_decode_destroy(h)
     moe.moe_decode_destroy(hd)
+
+
+def test_two_handles_on_two_streams_do_not_interfere():
+    """Handles share no device state (workspace, routing list, arrival ticket, graphs): two handles
+    with different weights, run three times each on two streams with no host wait between the
+    calls, give bit for bit the outputs each gives alone (4 tokens: the ticket form)."""
+    shape, T = synth.FLASH, 4
+    la, lb = DeviceLayer(shape, 60), DeviceLayer(shape, 61)
+    ha, hb = create(shape), create(shape)
+    la.set_into(ha, 0)
+    lb.set_into(hb, 0)
+    _, xa = margin_attempt(shape, la.router_host, 60, T)
+    _, xb = margin_attempt(shape, lb.router_host, 61, T)
+    ref_a, ref_b = run_layer(ha, shape, xa), run_layer(hb, shape, xb)
+    xda, xdb = to_dev_u16(xa), to_dev_u16(xb)
+    outs_a = [_fixed_outputs(shape, T) for _ in range(3)]
+    outs_b = [_fixed_outputs(shape, T) for _ in range(3)]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for oa, ob in zip(outs_a, outs_b):
+        moe.moe_decode_run(ha, xda, T, stream=sa, **oa)
+        moe.moe_decode_run(hb, xdb, T, stream=sb, **ob)
+    torch.cuda.synchronize()
+    moe.moe_decode_check(ha)
+    moe.moe_decode_check(hb)
+    for i in range(3):
+        _assert_same(_read(outs_a[i]), ref_a, f"handle a, run {i}")
+        _assert_same(_read(outs_b[i]), ref_b, f"handle b, run {i}")
+    moe.moe_decode_destroy(ha)
+    moe.moe_decode_destroy(hb)
