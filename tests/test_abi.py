@@ -129,6 +129,15 @@ def test_head_quantize_arguments_checked_before_device():
 def test_head_verify_arguments():
     L = moe.lib()
     assert L.fp8_head_verify(None, None, 4, None, None, None, None) == -1
+    # every check below fails before the handle would be read, so a stand-in address serves as one
+    buf = (ctypes.c_uint8 * 64)()
+    addr = (ctypes.addressof(buf) + 15) & ~15
+    fake = ctypes.c_void_p(addr)
+    for T in (0, 1, 5):  # a verify step scores the current token and 1-3 drafts: 2 <= T <= 4
+        assert L.fp8_head_verify(fake, addr, T, addr, addr, addr, None) == -1, T
+    assert L.fp8_head_verify(fake, addr, 4, None, addr, addr, None) == -1  # draft is required
+    assert L.fp8_head_verify(fake, addr, 4, addr, addr, None, None) == -1  # accept is required
+    assert L.fp8_head_verify(fake, addr + 8, 4, addr, addr, addr, None) == -1  # x not 16-byte aligned
 
 
 def test_binding_tags_tensors_from_their_own_dtype():
